@@ -1,0 +1,87 @@
+"""The oracle's pins are strong enough to catch plausible mistakes.
+
+Each mutant below is a copy of oracle/nsa_oracle.c with one planted bug (a
+dropped term, a wrong sign, an off-by-one, a transposed operand, a wrong head
+map).  It is compiled on the CPU, swapped in for the real oracle, and the pin
+checks of test_oracle_pins.py are run against it: at least one must fail.
+"""
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "nsa_oracle.c")
+
+MUTANTS = {
+    "dq drops scale": ("dq_out[d] += sh->scale * dS * kj[d];", "dq_out[d] += dS * kj[d];"),
+    "dS sign": ("double dS = P[a] * (dP[a] - delta);", "double dS = P[a] * (dP[a] + delta);"),
+    "causal strict": ("j < sh->T && j <= t;", "j < sh->T && j < t;"),
+    "block start off by one": ("for (int j = u * sh->bs; j <", "for (int j = u * sh->bs + 1; j <"),
+    "dk uses dO": ("dk_out[d] += sh->scale * dS * q_r[d];", "dk_out[d] += sh->scale * dS * do_r[d];"),
+    "dv uses dS": ("dv_out[d] += Pj * do_r[d];", "dv_out[d] += dS * do_r[d];"),
+    "dkdv skips diagonal": ("for (int t = j; t < sh->T; ++t)", "for (int t = j + 1; t < sh->T; ++t)"),
+    "delta drops P": ("delta += P[a] * dP[a];", "delta += dP[a];"),
+    "head map transposed": ("int G = sh->Hq / sh->Hkv, hkv = h / G, D = sh->D;\n    const double* K",
+                            "int G = sh->Hq / sh->Hkv, hkv = h % sh->Hkv, D = sh->D;\n    const double* K"),
+    "lse drops log": ("double lse = m + log(sum);", "double lse = m + sum;"),
+    "no scale in scores": ("P[a] = sh->scale * dot(q_r,", "P[a] = dot(q_r,"),
+    "o uses k": ("const double* V = krow(sh, v, b, hkv, 0);\n    int n = selected_keys",
+                 "const double* V = krow(sh, k, b, hkv, 0);\n    int n = selected_keys"),
+}
+
+
+@contextlib.contextmanager
+def _swapped(lib_path):
+    saved = oracle._lib
+    oracle._lib = None
+    real = oracle._LIB_PATH
+    real_src = oracle._SRC
+    try:
+        oracle._LIB_PATH = lib_path
+        oracle._SRC = lib_path  # mtime check passes: the library is its own source
+        yield
+    finally:
+        oracle._LIB_PATH = real
+        oracle._SRC = real_src
+        oracle._lib = saved
+
+
+CHECKS = [
+    lambda: pins.test_finite_differences(pins.TINY[0]),
+    lambda: pins.test_finite_differences(pins.TINY[1]),
+    lambda: pins.test_dense_masked_autograd(11, 2, 4, 2, 40, 8, 4, 5),
+    lambda: pins.test_full_selection_is_causal_sdpa(2, 4, 1, 48, 16, 8),
+    lambda: pins.test_gqa_equals_sum_over_heads(),
+    lambda: pins.test_closed_forms(),
+    lambda: pins.test_rows_sum_to_one_and_invariants(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site not found: {name}"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", lib,
+                    str(path), "-lm"], check=True)
+    caught = []
+    with _swapped(lib):
+        for i, check in enumerate(CHECKS):
+            try:
+                check()
+            except AssertionError:
+                caught.append(i)
+    assert caught, f"no pin caught mutant {name!r}"
+
+
+def test_unmutated_oracle_passes_all_checks():
+    for check in CHECKS:
+        check()
