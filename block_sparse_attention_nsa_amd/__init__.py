@@ -1,0 +1,195 @@
+"""NSA selection attention on MI355X (gfx950): a thin binding over the C ABI
+of libnsa_sel.so (include/nsa_sel.h).
+
+The binding only marshals arguments: it reads shapes from torch tensors,
+allocates outputs and the backward workspace with torch (device memory), and
+passes raw pointers and the current HIP stream to the library.  Every step of
+the computation runs in the library's HIP kernels; there is no other path.
+
+Layouts (page 1 of the reference text, run_one): dense q/dO [B, Hq, T, D],
+k/v [B, Hkv, T, D], block_idx [B, Hkv, T, S] int32.  Packed sequences
+(page 3, cumulative sequence lengths): q [T, Hq, D], k/v [T, Hkv, D],
+block_idx [Hkv, T, S] with sequence-local block numbers, cu_seqlens int32
+[n_seqs + 1] on the device.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "nsa_sel_fwd",
+    "nsa_sel_bwd",
+    "nsa_sel_delta",
+    "nsa_sel_invert",
+    "bwd_workspace_bytes",
+    "make_problem",
+    "selection_attn",
+    "SelectionAttn",
+]
+
+_DTYPES = {torch.float32: _lib.NSA_F32, torch.bfloat16: _lib.NSA_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, block_idx: torch.Tensor, block_size: int,
+                 scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                 max_seqlen: Optional[int] = None) -> _lib.Problem:
+    """The nsa_sel_problem describing these tensors."""
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    p = _lib.Problem()
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4 or block_idx.dim() != 4:
+            raise ValueError("dense layout needs q/k [B, H, T, D] and block_idx [B, Hkv, T, S]")
+        p.layout = _lib.NSA_DENSE
+        p.B, p.Hq, p.T, p.D = q.shape
+        p.Hkv = k.shape[1]
+        p.S = block_idx.shape[-1]
+        p.n_seqs, p.max_seqlen = 0, 0
+    else:
+        if q.dim() != 3 or k.dim() != 3 or block_idx.dim() != 3:
+            raise ValueError("packed layout needs q/k [T, H, D] and block_idx [Hkv, T, S]")
+        p.layout = _lib.NSA_PACKED
+        p.B = 1
+        p.T, p.Hq, p.D = q.shape
+        p.Hkv = k.shape[1]
+        p.S = block_idx.shape[-1]
+        p.n_seqs = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if p.n_seqs else 0
+        p.max_seqlen = int(max_seqlen)
+    p.block_size = int(block_size)
+    p.dtype = _DTYPES[q.dtype]
+    p.scale = float(q.shape[-1] ** -0.5 if scale is None else scale)
+    return p
+
+
+def _check_tensors(q, k, v, block_idx, cu_seqlens, p: _lib.Problem):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    if block_idx.dtype != torch.int32 or not block_idx.is_contiguous():
+        raise TypeError("block_idx must be a contiguous int32 tensor")
+    dense = cu_seqlens is None
+    want_k = (p.B, p.Hkv, p.T, p.D) if dense else (p.T, p.Hkv, p.D)
+    want_i = (p.B, p.Hkv, p.T, p.S) if dense else (p.Hkv, p.T, p.S)
+    if tuple(k.shape) != want_k or tuple(block_idx.shape) != want_i:
+        raise ValueError(f"shape mismatch: k {tuple(k.shape)} (want {want_k}), "
+                         f"block_idx {tuple(block_idx.shape)} (want {want_i})")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous()):
+        raise TypeError("cu_seqlens must be a contiguous int32 tensor")
+
+
+def _lse_shape(q, cu_seqlens):
+    return tuple(q.shape[:3]) if cu_seqlens is None else (q.shape[1], q.shape[0])
+
+
+def nsa_sel_fwd(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None,
+                out=None, lse=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """o, lse = forward (nsa_sel_fwd)."""
+    p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+    _check_tensors(q, k, v, block_idx, cu_seqlens, p)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty(_lse_shape(q, cu_seqlens), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = _lib.load().nsa_sel_fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(cu_seqlens),
+                                 _ptr(o), _ptr(lse_t), _stream())
+    _lib.check("nsa_sel_fwd", st)
+    return o, lse_t
+
+
+def bwd_workspace_bytes(p: _lib.Problem) -> int:
+    n = _lib.load().nsa_sel_bwd_workspace_bytes(p)
+    err = _lib.last_error()
+    if err:
+        raise _lib.NsaError("nsa_sel_bwd_workspace_bytes", _lib.NSA_ERR_INVALID_ARG, err)
+    return int(n)
+
+
+def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqlens=None,
+                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None):
+    """dq, dk, dv = backward (nsa_sel_bwd)."""
+    p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+    _check_tensors(q, k, v, block_idx, cu_seqlens, p)
+    for name, t in (("o", o), ("dO", dO)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q in shape, dtype and contiguity")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor")
+    nbytes = bwd_workspace_bytes(p)
+    ws = workspace
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = _lib.load().nsa_sel_bwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
+                                 _ptr(block_idx), _ptr(cu_seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(ws), ws.numel(), _stream())
+    _lib.check("nsa_sel_bwd", st)
+    return dq, dk, dv
+
+
+def nsa_sel_delta(o, dO, block_size, block_idx, k, scale=None, cu_seqlens=None, max_seqlen=None):
+    """Delta = rowsum(dO * o) (nsa_sel_delta), laid out like lse."""
+    p = make_problem(o, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+    delta = torch.empty(_lse_shape(o, cu_seqlens), dtype=torch.float32, device=o.device)
+    st = _lib.load().nsa_sel_delta(p, _ptr(o), _ptr(dO), _ptr(cu_seqlens), _ptr(delta), _stream())
+    _lib.check("nsa_sel_delta", st)
+    return delta
+
+
+def nsa_sel_invert(q, k, block_idx, block_size, cu_seqlens=None, max_seqlen=None):
+    """Block -> query lists (nsa_sel_invert): (offsets [Z, Hkv, NBmax+1], tokens)."""
+    p = make_problem(q, k, block_idx, block_size, None, cu_seqlens, max_seqlen)
+    lib = _lib.load()
+    cap = int(lib.nsa_sel_invert_tokens_capacity(p))
+    Z = p.B if cu_seqlens is None else p.n_seqs
+    tmax = p.T if cu_seqlens is None else p.max_seqlen
+    nb = -(-tmax // p.block_size)
+    offsets = torch.empty((Z, p.Hkv, nb + 1), dtype=torch.int32, device=block_idx.device)
+    tokens = torch.empty(max(cap, 1), dtype=torch.int32, device=block_idx.device)
+    nbytes = bwd_workspace_bytes(p)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=block_idx.device)
+    st = lib.nsa_sel_invert(p, _ptr(block_idx), _ptr(cu_seqlens), _ptr(offsets), _ptr(tokens),
+                            _ptr(ws), ws.numel(), _stream())
+    _lib.check("nsa_sel_invert", st)
+    return offsets, tokens
+
+
+class SelectionAttn(torch.autograd.Function):
+    """o = selection attention; backward through nsa_sel_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen):
+        o, lse = nsa_sel_fwd(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+        ctx.save_for_backward(q, k, v, o, lse, block_idx, cu_seqlens)
+        ctx.cfg = (block_size, scale, max_seqlen)
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, o, lse, block_idx, cu_seqlens = ctx.saved_tensors
+        block_size, scale, max_seqlen = ctx.cfg
+        dq, dk, dv = nsa_sel_bwd(q, k, v, o, lse, dO.contiguous(), block_idx, block_size, scale,
+                                 cu_seqlens, max_seqlen)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def selection_attn(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None):
+    """Differentiable NSA selection attention (page 1's selection_attn call)."""
+    return SelectionAttn.apply(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen)

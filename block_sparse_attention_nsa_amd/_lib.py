@@ -1,0 +1,96 @@
+"""ctypes view of libnsa_sel.so (include/nsa_sel.h).  No computation here."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnsa_sel.so")
+
+NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP = range(5)
+NSA_F32, NSA_BF16 = 0, 1
+NSA_DENSE, NSA_PACKED = 0, 1
+
+# Every symbol include/nsa_sel.h declares.
+EXPORTS = (
+    "nsa_sel_fwd",
+    "nsa_sel_bwd",
+    "nsa_sel_bwd_workspace_bytes",
+    "nsa_sel_delta",
+    "nsa_sel_invert",
+    "nsa_sel_invert_tokens_capacity",
+    "nsa_status_string",
+    "nsa_last_error",
+)
+
+
+class Problem(ctypes.Structure):
+    """Mirror of struct nsa_sel_problem."""
+    _fields_ = [
+        ("layout", ctypes.c_int32),
+        ("B", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("Hq", ctypes.c_int32),
+        ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("S", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_seqs", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class NsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load():
+    """Load the library; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m block_sparse_attention_nsa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, ip, fp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    st, sz = ctypes.c_int, ctypes.c_size_t
+    lib.nsa_sel_fwd.argtypes = [P, vp, vp, vp, ip, ip, vp, fp, vp]
+    lib.nsa_sel_fwd.restype = st
+    lib.nsa_sel_bwd.argtypes = [P, vp, vp, vp, vp, fp, vp, ip, ip, vp, vp, vp, vp, sz, vp]
+    lib.nsa_sel_bwd.restype = st
+    lib.nsa_sel_bwd_workspace_bytes.argtypes = [P]
+    lib.nsa_sel_bwd_workspace_bytes.restype = sz
+    lib.nsa_sel_delta.argtypes = [P, vp, vp, ip, fp, vp]
+    lib.nsa_sel_delta.restype = st
+    lib.nsa_sel_invert.argtypes = [P, ip, ip, ip, ip, vp, sz, vp]
+    lib.nsa_sel_invert.restype = st
+    lib.nsa_sel_invert_tokens_capacity.argtypes = [P]
+    lib.nsa_sel_invert_tokens_capacity.restype = sz
+    lib.nsa_status_string.argtypes = [ctypes.c_int]
+    lib.nsa_status_string.restype = ctypes.c_char_p
+    lib.nsa_last_error.argtypes = []
+    lib.nsa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().nsa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().nsa_last_error().decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != NSA_OK:
+        raise NsaError(fn, status, last_error())

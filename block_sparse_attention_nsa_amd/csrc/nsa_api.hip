@@ -1,0 +1,325 @@
+// nsa_api.hip -- the C ABI declared in include/nsa_sel.h: argument checks
+// (all on the host, before any HIP call), workspace carving and the ordered
+// launch of the kernels on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "nsa_internal.h"
+#include "nsa_sel.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nsa_status fail(nsa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+nsa_status hip_fail(hipError_t e, const char* what) {
+    return fail(NSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool misaligned(const void* ptr, size_t a) { return ((uintptr_t)ptr) % a != 0; }
+
+// Validates the problem and fills the host/device descriptions.
+nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
+    if (!p) return fail(NSA_ERR_INVALID_ARG, "problem pointer is NULL");
+    if (p->layout != NSA_DENSE && p->layout != NSA_PACKED)
+        return fail(NSA_ERR_INVALID_ARG, "layout %d is not NSA_DENSE or NSA_PACKED", p->layout);
+    const bool packed = p->layout == NSA_PACKED;
+    if (p->dtype != NSA_F32 && p->dtype != NSA_BF16)
+        return fail(NSA_ERR_INVALID_ARG, "dtype %d is not NSA_F32 or NSA_BF16", p->dtype);
+    if (p->B < 0 || p->T < 0) return fail(NSA_ERR_INVALID_ARG, "B=%d and T=%d must be >= 0", p->B, p->T);
+    if (p->Hq < 1 || p->Hkv < 1) return fail(NSA_ERR_INVALID_ARG, "Hq=%d and Hkv=%d must be >= 1", p->Hq, p->Hkv);
+    if (p->Hq % p->Hkv) return fail(NSA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+    if (p->D < 1) return fail(NSA_ERR_INVALID_ARG, "D=%d must be >= 1", p->D);
+    if (p->S < 1) return fail(NSA_ERR_INVALID_ARG, "S=%d must be >= 1", p->S);
+    if (p->block_size < 1) return fail(NSA_ERR_INVALID_ARG, "block_size=%d must be >= 1", p->block_size);
+    if (!isfinite(p->scale)) return fail(NSA_ERR_INVALID_ARG, "scale is not finite");
+    int Tmax = p->T, Z = p->B;
+    if (packed) {
+        if (p->B != 1) return fail(NSA_ERR_INVALID_ARG, "packed inputs need B == 1 (got %d)", p->B);
+        if (p->n_seqs < 0) return fail(NSA_ERR_INVALID_ARG, "n_seqs=%d must be >= 0", p->n_seqs);
+        if (p->T > 0 && p->n_seqs < 1) return fail(NSA_ERR_INVALID_ARG, "T=%d tokens but n_seqs=%d", p->T, p->n_seqs);
+        if (p->max_seqlen < 0 || p->max_seqlen > p->T)
+            return fail(NSA_ERR_INVALID_ARG, "max_seqlen=%d must lie in [0, T=%d]", p->max_seqlen, p->T);
+        if (p->T > 0 && p->max_seqlen < 1) return fail(NSA_ERR_INVALID_ARG, "max_seqlen must be >= 1 when T > 0");
+        Tmax = p->max_seqlen;
+        Z = p->n_seqs;
+    }
+    if (p->S > 4096) return fail(NSA_ERR_UNSUPPORTED, "S=%d exceeds 4096 slots", p->S);
+    if (p->dtype == NSA_BF16) {
+        if (p->D != 32 && p->D != 64 && p->D != 128)
+            return fail(NSA_ERR_UNSUPPORTED, "bf16 needs D in {32, 64, 128} (got %d)", p->D);
+        if (p->block_size != 32 && p->block_size != 64 && p->block_size != 128)
+            return fail(NSA_ERR_UNSUPPORTED, "bf16 needs block_size in {32, 64, 128} (got %d)", p->block_size);
+    } else {
+        if (p->D != 16 && p->D != 32 && p->D != 64 && p->D != 128)
+            return fail(NSA_ERR_UNSUPPORTED, "f32 needs D in {16, 32, 64, 128} (got %d)", p->D);
+    }
+    const int64_t NBmax = ((int64_t)Tmax + p->block_size - 1) / p->block_size;
+    if (NBmax > 8192) return fail(NSA_ERR_UNSUPPORTED, "ceil(max length / block_size) = %lld exceeds 8192", (long long)NBmax);
+    const int G = p->Hq / p->Hkv;
+    if ((int64_t)Tmax * G > (1ll << 30)) return fail(NSA_ERR_UNSUPPORTED, "max length * G exceeds 2^30 rows");
+    const int64_t ZH = (int64_t)Z * p->Hkv;
+    if (ZH > 8192) return fail(NSA_ERR_UNSUPPORTED, "(batch or sequences) * Hkv = %lld exceeds 8192", (long long)ZH);
+    const int64_t idx_rows = (int64_t)p->B * p->Hkv * p->T;
+    const int64_t Smin = std::min<int64_t>(p->S, std::max<int64_t>(NBmax, 1));
+
+    nsa::Problem& d = hp.dev;
+    d.B = p->B; d.T = p->T; d.Hq = p->Hq; d.Hkv = p->Hkv; d.G = G; d.D = p->D; d.S = p->S;
+    d.bs = p->block_size; d.Z = Z; d.packed = packed ? 1 : 0; d.Tmax = Tmax; d.NBmax = (int)NBmax;
+    d.Smin = (int)Smin; d.scale = p->scale; d.scale_log2 = p->scale * nsa::kLog2e; d.cu = nullptr;
+    hp.dtype = p->dtype;
+    hp.ZH = (int)ZH;
+    hp.CT = 64 * std::max(1, (Tmax + 64 * 64 - 1) / (64 * 64));
+    hp.C = (Tmax + hp.CT - 1) / hp.CT;
+    hp.rows = (int64_t)p->B * p->Hq * p->T;
+    hp.cap = Smin * idx_rows;
+    const int64_t rows_ub = hp.cap * G;
+    int64_t cr = (rows_ub / 1024 + 31) / 32 * 32;
+    hp.CR = (int)std::min<int64_t>(16384, std::max<int64_t>(1024, cr));
+    hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
+    if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");
+    hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
+    if (p->dtype == NSA_BF16 && nsa::fwd_bf16_lds_bytes(hp) > 65536)
+        return fail(NSA_ERR_UNSUPPORTED, "bf16 forward/dQ need %zu bytes of LDS for %lld blocks (max 65536)",
+                    nsa::fwd_bf16_lds_bytes(hp), (long long)NBmax);
+    return NSA_OK;
+}
+
+nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
+    nsa::BwdWorkspace w{};
+    size_t off = 0;
+    char* b = static_cast<char*>(base);
+    auto take = [&](size_t bytes) -> char* {
+        char* ptr = b ? b + off : nullptr;
+        off += align256(bytes);
+        return ptr;
+    };
+    const int64_t ZH = hp.ZH, NB = hp.dev.NBmax;
+    w.delta = (float*)take(sizeof(float) * hp.rows);
+    w.chunk_pos = (int*)take(sizeof(int) * ZH * hp.C * NB);
+    w.offsets = (int*)take(sizeof(int) * ZH * (NB + 1));
+    w.tokens = (int*)take(sizeof(int) * hp.cap);
+    w.item_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
+    w.pslot_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
+    w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 2 * ZH));
+    w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * hp.dev.bs * hp.dev.D);
+    w.bytes = off;
+    return w;
+}
+
+// cu_seqlens must be given exactly for packed problems that hold tokens.
+nsa_status check_cu(const nsa::HostProblem& hp, const int32_t* cu) {
+    if (!hp.dev.packed && cu) return fail(NSA_ERR_INVALID_ARG, "cu_seqlens given for a dense problem");
+    if (hp.dev.packed && hp.dev.T > 0 && !cu) return fail(NSA_ERR_INVALID_ARG, "cu_seqlens is NULL for a packed problem");
+    if (cu && misaligned(cu, 4)) return fail(NSA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+    return NSA_OK;
+}
+
+nsa_status check_tensor(const void* ptr, int64_t elems, size_t align, const char* name) {
+    if (elems > 0 && !ptr) return fail(NSA_ERR_INVALID_ARG, "%s is NULL", name);
+    if (ptr && misaligned(ptr, align))
+        return fail(NSA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+    return NSA_OK;
+}
+
+struct Sizes {
+    int64_t q, kv, idx, lse;
+};
+Sizes sizes_of(const nsa::HostProblem& hp) {
+    const nsa::Problem& d = hp.dev;
+    return {(int64_t)d.B * d.Hq * d.T * d.D, (int64_t)d.B * d.Hkv * d.T * d.D,
+            (int64_t)d.B * d.Hkv * d.T * d.S, (int64_t)d.B * d.Hq * d.T};
+}
+
+size_t elem_align(const nsa::HostProblem& hp) { return hp.dtype == NSA_BF16 ? 16 : 4; }
+
+#define NSA_TRY(x)                       \
+    do {                                 \
+        nsa_status st_ = (x);            \
+        if (st_ != NSA_OK) return st_;   \
+    } while (0)
+
+#define NSA_HIP(x, what)                           \
+    do {                                           \
+        hipError_t e_ = (x);                       \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+}  // namespace
+
+namespace nsa {
+BwdWorkspace carve_bwd_workspace(const HostProblem& hp, void* base) { return carve(hp, base); }
+}  // namespace nsa
+
+extern "C" {
+
+const char* nsa_status_string(nsa_status s) {
+    switch (s) {
+        case NSA_OK: return "ok";
+        case NSA_ERR_INVALID_ARG: return "invalid argument";
+        case NSA_ERR_UNSUPPORTED: return "unsupported problem";
+        case NSA_ERR_WORKSPACE: return "workspace missing or too small";
+        case NSA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* nsa_last_error(void) { return g_last_error.c_str(); }
+
+nsa_status nsa_sel_fwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* block_idx, const int32_t* cu_seqlens, void* o, float* lse,
+                       nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, cu_seqlens));
+    const Sizes sz = sizes_of(hp);
+    const size_t a = elem_align(hp);
+    NSA_TRY(check_tensor(q, sz.q, a, "q"));
+    NSA_TRY(check_tensor(k, sz.kv, a, "k"));
+    NSA_TRY(check_tensor(v, sz.kv, a, "v"));
+    NSA_TRY(check_tensor(o, sz.q, a, "o"));
+    NSA_TRY(check_tensor(block_idx, sz.idx, 4, "block_idx"));
+    NSA_TRY(check_tensor(lse, sz.lse, 4, "lse"));
+    if (sz.q == 0) return NSA_OK;
+    hp.dev.cu = cu_seqlens;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (hp.dtype == NSA_BF16) {
+        NSA_HIP(nsa::launch_fwd_bf16(hp, q, k, v, block_idx, o, lse, st), "forward launch");
+    } else {
+        NSA_HIP(nsa::launch_fwd_f32(hp, (const float*)q, (const float*)k, (const float*)v,
+                                    block_idx, (float*)o, lse, st),
+                "forward launch");
+    }
+    return NSA_OK;
+}
+
+size_t nsa_sel_bwd_workspace_bytes(const nsa_sel_problem* p) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    if (!p) {
+        fail(NSA_ERR_INVALID_ARG, "problem pointer is NULL");
+        return 0;
+    }
+    if (make_problem(p, hp) != NSA_OK) return 0;
+    return carve(hp, nullptr).bytes;
+}
+
+size_t nsa_sel_invert_tokens_capacity(const nsa_sel_problem* p) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    if (!p) {
+        fail(NSA_ERR_INVALID_ARG, "problem pointer is NULL");
+        return 0;
+    }
+    if (make_problem(p, hp) != NSA_OK) return 0;
+    return (size_t)hp.cap;
+}
+
+nsa_status nsa_sel_delta(const nsa_sel_problem* p, const void* o, const void* dO,
+                         const int32_t* cu_seqlens, float* delta, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, cu_seqlens));
+    const Sizes sz = sizes_of(hp);
+    const size_t a = elem_align(hp);
+    NSA_TRY(check_tensor(o, sz.q, a, "o"));
+    NSA_TRY(check_tensor(dO, sz.q, a, "dO"));
+    NSA_TRY(check_tensor(delta, sz.lse, 4, "delta"));
+    if (sz.q == 0) return NSA_OK;
+    hp.dev.cu = cu_seqlens;
+    NSA_HIP(nsa::launch_delta(hp, o, dO, delta, reinterpret_cast<hipStream_t>(stream)), "delta launch");
+    return NSA_OK;
+}
+
+nsa_status nsa_sel_invert(const nsa_sel_problem* p, const int32_t* block_idx,
+                          const int32_t* cu_seqlens, int32_t* offsets, int32_t* tokens,
+                          void* workspace, size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, cu_seqlens));
+    const Sizes sz = sizes_of(hp);
+    NSA_TRY(check_tensor(block_idx, sz.idx, 4, "block_idx"));
+    const int64_t n_off = (int64_t)hp.ZH * (hp.dev.NBmax + 1);
+    NSA_TRY(check_tensor(offsets, n_off, 4, "offsets"));
+    NSA_TRY(check_tensor(tokens, hp.cap, 4, "tokens"));
+    const nsa::BwdWorkspace need = carve(hp, nullptr);
+    if (need.bytes && (!workspace || workspace_bytes < need.bytes))
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need.bytes);
+    if (workspace && misaligned(workspace, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (hp.ZH == 0 || hp.dev.NBmax == 0) {
+        if (n_off) NSA_HIP(hipMemsetAsync(offsets, 0, sizeof(int) * n_off, reinterpret_cast<hipStream_t>(stream)), "offsets clear");
+        return NSA_OK;
+    }
+    hp.dev.cu = cu_seqlens;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const nsa::BwdWorkspace ws = carve(hp, workspace);
+    NSA_HIP(nsa::launch_invert(hp, block_idx, ws, st), "inversion launch");
+    NSA_HIP(hipMemcpyAsync(offsets, ws.offsets, sizeof(int) * n_off, hipMemcpyDeviceToDevice, st), "offsets copy");
+    if (hp.cap)
+        NSA_HIP(hipMemcpyAsync(tokens, ws.tokens, sizeof(int) * hp.cap, hipMemcpyDeviceToDevice, st), "tokens copy");
+    return NSA_OK;
+}
+
+nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dO,
+                       const int32_t* block_idx, const int32_t* cu_seqlens, void* dq, void* dk,
+                       void* dv, void* workspace, size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, cu_seqlens));
+    const Sizes sz = sizes_of(hp);
+    const size_t a = elem_align(hp);
+    NSA_TRY(check_tensor(q, sz.q, a, "q"));
+    NSA_TRY(check_tensor(k, sz.kv, a, "k"));
+    NSA_TRY(check_tensor(v, sz.kv, a, "v"));
+    NSA_TRY(check_tensor(o, sz.q, a, "o"));
+    NSA_TRY(check_tensor(dO, sz.q, a, "dO"));
+    NSA_TRY(check_tensor(dq, sz.q, a, "dq"));
+    NSA_TRY(check_tensor(dk, sz.kv, a, "dk"));
+    NSA_TRY(check_tensor(dv, sz.kv, a, "dv"));
+    NSA_TRY(check_tensor(lse, sz.lse, 4, "lse"));
+    NSA_TRY(check_tensor(block_idx, sz.idx, 4, "block_idx"));
+    const nsa::BwdWorkspace need = carve(hp, nullptr);
+    if (need.bytes && (!workspace || workspace_bytes < need.bytes))
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need.bytes);
+    if (workspace && misaligned(workspace, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (sz.q == 0) return NSA_OK;
+    hp.dev.cu = cu_seqlens;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const nsa::BwdWorkspace ws = carve(hp, workspace);
+    NSA_HIP(nsa::launch_delta(hp, o, dO, ws.delta, st), "delta launch");
+    NSA_HIP(nsa::launch_invert(hp, block_idx, ws, st), "inversion launch");
+    if (hp.dtype == NSA_BF16) {
+        NSA_HIP(nsa::launch_plan(hp, ws, st), "planner launch");
+        NSA_HIP(nsa::launch_dq_bf16(hp, q, k, v, dO, lse, ws.delta, block_idx, dq, st), "dQ launch");
+        NSA_HIP(nsa::launch_dkdv_bf16(hp, q, k, v, dO, lse, ws.delta, ws, dk, dv, st), "dK/dV launch");
+    } else {
+        NSA_HIP(nsa::launch_dq_f32(hp, (const float*)q, (const float*)k, (const float*)v,
+                                   (const float*)dO, lse, ws.delta, block_idx, (float*)dq, st),
+                "dQ launch");
+        NSA_HIP(nsa::launch_dkdv_f32(hp, (const float*)q, (const float*)k, (const float*)v,
+                                     (const float*)dO, lse, ws.delta, ws, (float*)dk, (float*)dv, st),
+                "dK/dV launch");
+    }
+    return NSA_OK;
+}
+
+}  // extern "C"

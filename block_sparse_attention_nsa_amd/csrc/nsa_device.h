@@ -1,0 +1,187 @@
+// nsa_device.h -- device-side building blocks shared by the gfx950 kernels of
+// libnsa_sel: problem geometry, bf16 conversions, the 16x16x32 bf16 matrix-core
+// (MFMA) step, wavefront shuffles and wave-local LDS ordering.
+//
+// MFMA lane layouts used throughout (v_mfma_f32_16x16x32_bf16, one wave):
+//   A (16 x 32):  lane l holds A[l % 16][8 * (l / 16) + e],  e = 0..7
+//   B (32 x 16):  lane l holds B[8 * (l / 16) + e][l % 16],  e = 0..7
+//   C (16 x 16):  lane l holds C[4 * (l / 16) + i][l % 16],  i = 0..3
+// The contraction index k only has to be laid out the same way in A and B, so
+// every kernel is free to pick which 8 k-values lane group g = l / 16 carries.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Everything a kernel needs to know about the problem (passed by value).
+struct Problem {
+    int B, T, Hq, Hkv, G, D, S, bs;
+    int Z;        // batch entries (dense) or sequences (packed)
+    int packed;   // 1 when cu is a cumulative-length array
+    int Tmax;     // longest sequence (T for dense)
+    int NBmax;    // ceil(Tmax / bs)
+    int Smin;     // min(S, NBmax): distinct usable entries per row, at most
+    float scale;  // softmax scale
+    float scale_log2;  // scale * log2(e): scores in the base-2 domain
+    const int* cu;
+};
+
+// Where sequence z lives.  Offsets are in elements; "rows" of block_idx and
+// lse/delta are counted in their own arrays.  Packed lengths are clamped so
+// every access stays inside the T-token arrays whatever cu holds.
+struct Seq {
+    int start, len;
+    int64_t q_base, q_sh, q_st;    // q/o/dO/dq: element offset of (h, t)
+    int64_t k_base, k_sh, k_st;    // k/v/dk/dv
+    int64_t i_base;                // block_idx row of (hkv, t) = i_base + hkv*T + t
+    int64_t l_base;                // lse/delta index of (h, t)  = l_base + h*T + t
+};
+
+__device__ __forceinline__ Seq seq_of(const Problem& p, int z) {
+    Seq s;
+    if (p.packed) {
+        int a = p.cu[z], b = p.cu[z + 1];
+        a = min(max(a, 0), p.T);
+        b = min(max(b, a), p.T);
+        s.start = a;
+        s.len = min(b - a, p.Tmax);
+        s.q_base = (int64_t)a * p.Hq * p.D;
+        s.q_sh = p.D;
+        s.q_st = (int64_t)p.Hq * p.D;
+        s.k_base = (int64_t)a * p.Hkv * p.D;
+        s.k_sh = p.D;
+        s.k_st = (int64_t)p.Hkv * p.D;
+        s.i_base = a;
+        s.l_base = a;
+    } else {
+        s.start = 0;
+        s.len = p.T;
+        s.q_base = (int64_t)z * p.Hq * p.T * p.D;
+        s.q_sh = (int64_t)p.T * p.D;
+        s.q_st = p.D;
+        s.k_base = (int64_t)z * p.Hkv * p.T * p.D;
+        s.k_sh = (int64_t)p.T * p.D;
+        s.k_st = p.D;
+        s.i_base = (int64_t)z * p.Hkv * p.T;
+        s.l_base = (int64_t)z * p.Hq * p.T;
+    }
+    return s;
+}
+
+__device__ __forceinline__ int64_t q_off(const Seq& s, int h, int t) {
+    return s.q_base + h * s.q_sh + (int64_t)t * s.q_st;
+}
+__device__ __forceinline__ int64_t k_off(const Seq& s, int h, int t) {
+    return s.k_base + h * s.k_sh + (int64_t)t * s.k_st;
+}
+__device__ __forceinline__ int64_t l_off(const Problem& p, const Seq& s, int h, int t) {
+    return s.l_base + (int64_t)h * p.T + t;
+}
+__device__ __forceinline__ const int* idx_row(const Problem& p, const Seq& s, const int* idx,
+                                              int hkv, int t) {
+    return idx + (s.i_base + (int64_t)hkv * p.T + t) * p.S;
+}
+// First entry of the (z, hkv) region of the inverted token lists.
+__device__ __forceinline__ int64_t region_base(const Problem& p, const Seq& s, int hkv) {
+    return (s.i_base + (int64_t)hkv * p.T) * p.Smin;
+}
+
+// ---- bf16 ---------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round to nearest even (inputs here are finite or +-inf; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transposing read (ds_read_b64_tr_b16).  Inside each 16-lane group,
+// lane 4r + c passes the address of 4 consecutive bf16 of "row" r
+// (Tile[row_r][n0 + 4c .. 4c + 3]); lane i of the group then receives the
+// column {Tile[row_r][n0 + i] : r = 0..3}.  Two such reads give one MFMA
+// operand whose contraction index runs over 8 rows of a row-major tile.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* lds_ptr) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_ptr));
+    return __builtin_bit_cast(uint2, r);
+}
+
+// Operand A[m][k] = Tile[rows(k)][col0 + m] (or B[k][n] = Tile[rows(k)][col0 + n])
+// for the 8 rows rows(8g + e) = row_lo + 4g + e (e < 4), row_hi + 4g + e - 4
+// (e >= 4) of a row-major bf16 tile with `stride` elements per row.
+__device__ __forceinline__ bf16x8 lds_col_operand(const uint16_t* tile, int stride, int row_lo,
+                                                  int row_hi, int col0, int lane) {
+    int g = lane >> 4, j = lane & 15, r = j >> 2, c = j & 3;
+    uint2 lo = lds_read_tr(tile + (row_lo + 4 * g + r) * stride + col0 + 4 * c);
+    uint2 hi = lds_read_tr(tile + (row_hi + 4 * g + r) * stride + col0 + 4 * c);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---- wavefront helpers ----------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+    int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one C-layout column).
+__device__ __forceinline__ float col_max4(float v) {
+    v = fmaxf(v, shfl_xor(v, 16));
+    return fmaxf(v, shfl_xor(v, 32));
+}
+__device__ __forceinline__ float col_sum4(float v) {
+    v += shfl_xor(v, 16);
+    return v + shfl_xor(v, 32);
+}
+
+// Order this wave's LDS accesses: everything issued before is complete and
+// visible to the wave before anything after it runs.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Workgroup index remapped so that consecutive logical indices stay on one
+// XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each
+// with its own L2): logical ranges then share K/V in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    const int X = 8;
+    int xcd = bid % X, k = bid / X;
+    int q = n / X, r = n % X;
+    return xcd * q + min(xcd, r) + k;
+}
+
+}  // namespace nsa

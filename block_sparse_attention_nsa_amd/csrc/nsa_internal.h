@@ -1,0 +1,70 @@
+// nsa_internal.h -- host-side glue between the C ABI (nsa_api.hip) and the
+// kernel files: the backward workspace layout and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nsa_device.h"
+
+namespace nsa {
+
+// Host description of a validated problem (plus the device Problem).
+struct HostProblem {
+    Problem dev;
+    int dtype;      // 0 f32, 1 bf16
+    int ZH;         // Z * Hkv
+    int CT;         // tokens per inversion chunk
+    int C;          // inversion chunks per (z, hkv): ceil(Tmax / CT)
+    int CR;         // query rows per dK/dV work item
+    int64_t rows;   // query rows in lse/delta: B*Hq*T (dense) or Hq*T (packed)
+    int64_t cap;    // token-list capacity: Smin * rows of block_idx
+    int64_t items_ub;  // upper bound on dK/dV work items
+    int64_t pslots;    // fp32 partial slots reserved for split lists
+};
+
+// Backward workspace carve (all offsets 256-byte aligned).
+struct BwdWorkspace {
+    float* delta;        // [rows]
+    int* chunk_pos;      // [ZH][C][NBmax]: per-chunk counts, then list cursors
+    int* offsets;        // [ZH][NBmax + 1]: CSR offsets inside each region
+    int* tokens;         // [cap]: inverted lists
+    int* item_pre;       // [ZH][NBmax + 1]: exclusive prefix of work items per list
+    int* pslot_pre;      // [ZH][NBmax + 1]: exclusive prefix of partial slots per list
+    int* zh_base;        // [2][ZH + 1]: global prefixes of items and partial slots
+    float* partials;     // [pslots][bs][D][2]
+    size_t bytes;
+};
+
+BwdWorkspace carve_bwd_workspace(const HostProblem& hp, void* base);
+
+// ---- launchers (return the launch status) ---------------------------------
+hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, float* delta,
+                        hipStream_t st);
+hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
+                         hipStream_t st);
+hipError_t launch_plan(const HostProblem& hp, const BwdWorkspace& ws, hipStream_t st);
+
+hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
+                           const int* block_idx, void* o, float* lse, hipStream_t st);
+hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
+                          const void* dO, const float* lse, const float* delta,
+                          const int* block_idx, void* dq, hipStream_t st);
+hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
+                            const void* dO, const float* lse, const float* delta,
+                            const BwdWorkspace& ws, void* dk, void* dv, hipStream_t st);
+
+hipError_t launch_fwd_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
+                          const int* block_idx, float* o, float* lse, hipStream_t st);
+hipError_t launch_dq_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
+                         const float* dO, const float* lse, const float* delta,
+                         const int* block_idx, float* dq, hipStream_t st);
+hipError_t launch_dkdv_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
+                           const float* dO, const float* lse, const float* delta,
+                           const BwdWorkspace& ws, float* dk, float* dv, hipStream_t st);
+
+// Dynamic LDS the bf16 forward / dQ kernels need (0 if unsupported).
+size_t fwd_bf16_lds_bytes(const HostProblem& hp);
+
+}  // namespace nsa

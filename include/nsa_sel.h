@@ -1,0 +1,155 @@
+/*
+ * nsa_sel.h -- C ABI of the MI355X (gfx950) NSA selection-attention library
+ * (libnsa_sel.so).
+ *
+ * What it computes.  Page 1 of the reference text, "test_kernel_backward.py
+ * -- GRADCHECK GATE for the NSA selection BACKWARD kernel" (docstring and
+ * run_one), defines the call: q, k, v and a per-token list of selected key
+ * blocks (block_idx, block_size) give o; o.backward(dO) gives dQ, dK, dV; G =
+ * Hq/Hkv query heads share one KV head and its block list.  Page 3, the
+ * cudnn-frontend SM80 backward pull request (walkthrough and review of
+ * sdpa_bwd_wrapper_sm80), shows the backward consuming o, dO and the forward's
+ * lse, and packed (THD) batches described by cumulative sequence lengths.
+ *
+ * For query row (z, h, t) -- z a batch entry or packed sequence, h a query
+ * head, t a sequence-local token -- with hkv = h / G and NB = ceil(len/bs):
+ *   Sel = { u : u listed in block_idx[z, hkv, t, :], 0 <= u < NB }   (a set)
+ *   A   = { j : j / bs in Sel, j < len, j <= t }
+ *   lse = log sum_{j in A} exp(scale <q, k_j>),  o = sum_{j in A} P_j v_j
+ * and the backward is the exact gradient of o.  An empty A gives o = 0,
+ * lse = -inf, dq = 0.  Negative or >= NB entries are padding.  Repeated
+ * entries count once.  Keys listed by no row get dk = dv = 0.
+ *
+ * Layouts (all contiguous, row-major, last dimension D):
+ *   dense  (layout NSA_DENSE, cu_seqlens == NULL): q, o, dO, dq [B][Hq][T][D];
+ *          k, v, dk, dv [B][Hkv][T][D]; block_idx [B][Hkv][T][S] int32;
+ *          lse, delta [B][Hq][T] float.
+ *   packed (layout NSA_PACKED, cu_seqlens != NULL, B == 1, T = total tokens):
+ *          q, o, dO, dq [T][Hq][D]; k, v, dk, dv [T][Hkv][D];
+ *          block_idx [Hkv][T][S] with sequence-local block numbers;
+ *          lse, delta [Hq][T]; cu_seqlens [n_seqs + 1] int32 on the device,
+ *          cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] = T, and
+ *          max_seqlen >= every sequence length (host value).
+ * Element type: dtype NSA_F32 (float) or NSA_BF16 (bfloat16) for q, k, v, o,
+ * dO, dq, dk, dv; lse/delta are float; block_idx/cu_seqlens are int32.
+ *
+ * Ownership and errors.  Every pointer is device memory owned by the caller;
+ * the library allocates nothing.  Inputs are read-only; outputs are fully
+ * overwritten and must not alias inputs.  All work is queued on `stream` only
+ * and is asynchronous: device faults surface at the caller's next
+ * synchronisation.  Each call checks its arguments on the host before any
+ * HIP call and returns a non-zero nsa_status without touching any buffer when
+ * a check fails; nsa_last_error() then names the failed check (thread-local
+ * text).  There is no fallback path: an unsupported shape is an error.
+ * The library keeps no state besides that text and is reentrant.
+ *
+ * Supported (else NSA_ERR_UNSUPPORTED): dtype f32 with D in {16, 32, 64,
+ * 128} and any block_size >= 1 (vector-ALU kernels); dtype bf16 with D in
+ * {32, 64, 128} and block_size in {32, 64, 128} (matrix-core kernels), and
+ * 4 * (64 * (D + 8) + 6 * NBmax) <= 65536 bytes of forward/dQ LDS (NBmax =
+ * ceil(max length / block_size); e.g. NBmax <= 1280 at D = 128).  For both:
+ * S <= 4096, NBmax <= 8192, (B or n_seqs) * Hkv <= 8192, max length * G
+ * <= 2^30.
+ */
+#ifndef NSA_SEL_H
+#define NSA_SEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nsa_status {
+    NSA_OK = 0,
+    NSA_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, inconsistent sizes */
+    NSA_ERR_UNSUPPORTED = 2,   /* valid but outside the supported set above */
+    NSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    NSA_ERR_HIP = 4            /* a HIP runtime call failed (launch error) */
+} nsa_status;
+
+typedef enum nsa_dtype { NSA_F32 = 0, NSA_BF16 = 1 } nsa_dtype;
+
+typedef enum nsa_layout {
+    NSA_DENSE = 0,   /* [B][H][T][D], cu_seqlens must be NULL */
+    NSA_PACKED = 1   /* [T][H][D] sequences back to back, cu_seqlens required */
+} nsa_layout;
+
+/* Problem description (host memory, read only during the call). */
+typedef struct nsa_sel_problem {
+    int32_t layout;      /* nsa_layout */
+    int32_t B;           /* batch entries (dense); 1 for packed */
+    int32_t T;           /* tokens per entry (dense) or total tokens (packed) */
+    int32_t Hq;          /* query heads */
+    int32_t Hkv;         /* key/value heads; G = Hq / Hkv */
+    int32_t D;           /* head dimension */
+    int32_t S;           /* slots per block_idx row */
+    int32_t block_size;  /* keys per block */
+    int32_t n_seqs;      /* packed: number of sequences; dense: ignored */
+    int32_t max_seqlen;  /* packed: bound on every sequence length; dense: ignored */
+    int32_t dtype;       /* nsa_dtype */
+    float scale;         /* softmax scale applied to <q, k> (e.g. 1/sqrt(D)) */
+} nsa_sel_problem;
+
+typedef struct hipStream_t_opaque* nsa_stream_t; /* a hipStream_t; NULL = null stream */
+
+/* Forward: o and lse from q, k, v and block_idx (the online softmax over the
+ * gathered blocks).  cu_seqlens is NULL for dense inputs.  Needs no
+ * workspace. */
+nsa_status nsa_sel_fwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                       const int32_t* block_idx, const int32_t* cu_seqlens, void* o,
+                       float* lse, nsa_stream_t stream);
+
+/* Bytes of device workspace nsa_sel_bwd needs for this problem (0 when the
+ * problem is invalid; check nsa_last_error()).  The workspace must be
+ * 256-byte aligned; its contents need not be initialised. */
+size_t nsa_sel_bwd_workspace_bytes(const nsa_sel_problem* p);
+
+/* Backward: dq, dk, dv from q, k, v, the forward's o and lse, dO and
+ * block_idx.  Runs, in order on `stream`: Delta = rowsum(dO * o); the
+ * block -> query inversion; the dQ kernel (per query tile, no atomics); the
+ * dK/dV kernel (per key block and row chunk, no atomics) and its
+ * fixed-order reduction.  Results are deterministic (bitwise repeatable). */
+nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dO,
+                       const int32_t* block_idx, const int32_t* cu_seqlens, void* dq, void* dk,
+                       void* dv, void* workspace, size_t workspace_bytes,
+                       nsa_stream_t stream);
+
+/* Delta preprocess alone: delta[row] = sum_d dO[row, d] * o[row, d] (float
+ * accumulation), layout of lse.  The backward's first stage (page 3 names it
+ * the do_dot step of its kernel chain). */
+nsa_status nsa_sel_delta(const nsa_sel_problem* p, const void* o, const void* dO,
+                         const int32_t* cu_seqlens, float* delta, nsa_stream_t stream);
+
+/* Block -> query inversion alone.  For every (z, hkv, u) it lists, in
+ * ascending order, the tokens t >= u * block_size whose row lists block u
+ * (once each).  Z = B (dense) or n_seqs (packed); NBmax = ceil(T /
+ * block_size) (dense) or ceil(max_seqlen / block_size) (packed); Smin =
+ * min(S, NBmax).  Outputs: offsets [Z][Hkv][NBmax + 1] int32, offsets of
+ * each list inside the (z, hkv) region of `tokens` (offsets[..][0] = 0, the
+ * last one is the region's entry count; blocks past a packed sequence's end
+ * have empty lists); tokens: the region of (z, hkv) starts at entry
+ * Smin * r0, where r0 is the block_idx row of token 0 of (z, hkv):
+ * (z * Hkv + hkv) * T dense, hkv * T + cu_seqlens[z] packed.  Capacity of
+ * tokens: nsa_sel_invert_tokens_capacity() entries.  Uses the backward's
+ * workspace (its size from nsa_sel_bwd_workspace_bytes()). */
+nsa_status nsa_sel_invert(const nsa_sel_problem* p, const int32_t* block_idx,
+                          const int32_t* cu_seqlens, int32_t* offsets, int32_t* tokens,
+                          void* workspace, size_t workspace_bytes, nsa_stream_t stream);
+
+/* Entries the tokens array of nsa_sel_invert must hold: Smin * B * Hkv * T
+ * (dense) or Smin * Hkv * T (packed). */
+size_t nsa_sel_invert_tokens_capacity(const nsa_sel_problem* p);
+
+/* Text of a status code, and the detail of the calling thread's last
+ * error (empty string if none). */
+const char* nsa_status_string(nsa_status s);
+const char* nsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_SEL_H */

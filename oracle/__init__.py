@@ -170,8 +170,9 @@ def bwd(q, k, v, dO, block_idx, block_size, scale=None):
 
 
 def invert(block_idx, block_size) -> Tuple[np.ndarray, np.ndarray]:
-    """Brute-force block -> token lists.  Returns (counts [B,Hkv,NB], tokens)
-    with the lists concatenated in (b, hkv, u) order, each ascending."""
+    """Brute-force block -> token lists: for block u the ascending tokens
+    t >= u*bs that list u.  Returns (counts [B,Hkv,NB], tokens) with the lists
+    concatenated in (b, hkv, u) order."""
     idx = _i32(block_idx)
     B, Hkv, T, S = idx.shape
     NB = -(-T // block_size)

@@ -286,7 +286,9 @@ int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v
 }
 
 /* Block -> query inversion, brute force.  For every (b, hkv, u) in order, the
- * ascending tokens t whose row lists u (once per token).  counts is
+ * ascending tokens t whose key set A meets block u: t lists u and t >= u*bs
+ * (a listed block that starts after t adds no key, so it is not an entry);
+ * each token appears once however often it lists u.  counts is
  * [B][Hkv][NB]; tokens receives the lists back to back in that order (its
  * capacity is cap entries).  Returns the total entry count, or -1 if cap is
  * too small. */
@@ -299,7 +301,7 @@ int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* i
         for (int hkv = 0; hkv < Hkv; ++hkv)
             for (int u = 0; u < NB; ++u) {
                 int32_t c = 0;
-                for (int t = 0; t < T; ++t) {
+                for (int t = u * bs; t < T; ++t) {
                     if (!row_lists_block(idx_row(&sh, idx, b, hkv, t), S, u)) continue;
                     if (n >= cap) return -1;
                     tokens[n++] = t;

@@ -330,8 +330,8 @@ def test_selection_sentinels():
 
 
 def test_inversion_brute_force():
-    """O9: per (b, hkv, block) the ascending tokens listing that block, once
-    each, against plain Python dict-of-lists."""
+    """O9: per (b, hkv, block u) the ascending tokens t >= u*bs listing u,
+    once each, against plain Python dict-of-lists."""
     rng = np.random.default_rng(71)
     B, Hkv, T, bs, S = 2, 3, 50, 4, 5
     idx = _weird_idx(rng, B, Hkv, T, bs, S)
@@ -342,7 +342,7 @@ def test_inversion_brute_force():
         for h in range(Hkv):
             for t in range(T):
                 for u in set(int(x) for x in idx[b, h, t]):
-                    if 0 <= u < NB:
+                    if 0 <= u < NB and u * bs <= t:
                         expect.setdefault((b, h, u), []).append(t)
     pos = 0
     for b in range(B):
