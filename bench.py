@@ -1,0 +1,276 @@
+"""Benchmark: NSA selection attention fwd + bwd on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload cfg2|cfg3|cfg4|cfg1]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+nsa_sel_fwd, then the backward's three stages (Delta + block->query
+inversion + plan, dQ, dK/dV).  Inputs are resident in HBM before timing.
+The metric is useful TFLOP/s: F_fwd = 4*D*N and F_bwd = 10*D*N with N the
+exact number of (query-head row, key) pairs the block lists select (counted
+here from block_idx), per step, over the wall time of K steps bracketed by
+device synchronisation.  Per-stage times come from events on the stream the
+kernels run on.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {"cfg1": 1, "cfg2": 2, "cfg3": 3, "cfg4": 4}
+# Algorithmic flops per (row, key) pair of each timed stage, in units of D:
+# fwd S and PV; dq recomputes S and dP and forms dS K; dkdv recomputes S and
+# dP and forms dV and dK.
+STAGE_FLOPS_PER_PAIR_D = {"fwd": 4, "dq": 6, "dkdv": 8}
+STAGE_KERNEL = {"fwd": "fwd_bf16_kernel", "dq": "dq_bf16_kernel", "dkdv": "dkdv_bf16_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def useful_pairs(block_idx: np.ndarray, G: int, bs: int, lengths) -> int:
+    """N = sum over query-head rows of |A|: a row (z, hkv, t) counts each
+    distinct listed block u with 0 <= u < ceil(len/bs) and u*bs <= t, for
+    min((u+1)*bs, t+1) - u*bs keys; times G heads."""
+    total = 0
+    for rows, L in lengths:  # rows: [n, S] int array for tokens 0..L-1 of one (z, hkv)
+        if L == 0:
+            continue
+        t = np.arange(L)[:, None]
+        u = rows.astype(np.int64)
+        nb = -(-L // bs)
+        ok = (u >= 0) & (u < nb) & (u * bs <= t)
+        u = np.where(ok, u, -1)
+        u.sort(axis=1)
+        dup = np.zeros_like(ok)
+        dup[:, 1:] = (u[:, 1:] == u[:, :-1])
+        keep = (u >= 0) & ~dup
+        keys = np.minimum((u + 1) * bs, t + 1) - u * bs
+        total += int(np.where(keep, keys, 0).sum())
+    return total * G
+
+
+def row_groups(w):
+    """(rows [L, S], L) per (z, hkv) of a workload."""
+    if w.packed:
+        for z in range(w.n_seqs):
+            a, b = int(w.cu_seqlens[z]), int(w.cu_seqlens[z + 1])
+            for h in range(w.Hkv):
+                yield w.block_idx[h, a:b], b - a
+    else:
+        for z in range(w.B):
+            for h in range(w.Hkv):
+                yield w.block_idx[z, h], w.T
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for d in ("block_sparse_attention_nsa_amd/csrc", "include"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            if f.endswith((".hip", ".h")):
+                h.update(open(os.path.join(ROOT, d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def git_sha() -> str:
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                              text=True).stdout.strip() or "unknown"
+    except OSError:
+        return "unknown"
+
+
+def stored_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_tokens: int):
+    """The float64 oracle on the first n_tokens of every (entry, head) of the
+    same draw (a closed causal sub-problem), full forward + backward."""
+    import oracle
+
+    if w.packed:
+        z = int(np.argmax(np.diff(w.cu_seqlens)))
+        a = int(w.cu_seqlens[z])
+        L = min(n_tokens, int(w.cu_seqlens[z + 1]) - a)
+        tr = lambda x: np.ascontiguousarray(x[a:a + L].transpose(1, 0, 2))[None]
+        q, k, v, dO = tr(w.q), tr(w.k), tr(w.v), tr(w.dO)
+        idx = np.ascontiguousarray(w.block_idx[:, a:a + L])[None]
+        what = f"first {L} tokens of packed sequence {z}, all heads"
+    else:
+        L = min(n_tokens, w.T)
+        sl = (slice(None), slice(None), slice(0, L))
+        q, k, v, dO, idx = (np.ascontiguousarray(x[sl]) for x in (w.q, w.k, w.v, w.dO, w.block_idx))
+        what = f"first {L} of {w.T} tokens of every batch entry and head"
+    n = oracle.count_pairs(idx, w.Hq, w.block_size)
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, idx, w.block_size, w.scale)
+    oracle.bwd(q, k, v, dO, idx, w.block_size, w.scale)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * w.D * n
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{what} (N={n} pairs), float64 fwd+bwd"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens per (entry, head) of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU: the path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_nsa_amd as nsa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = WORKLOADS[args.workload]
+    w = workloads.make_config(cfg, seed=args.seed)
+    G = w.Hq // w.Hkv
+    N = useful_pairs(w.block_idx, G, w.block_size, row_groups(w))
+    f_fwd, f_bwd = 4.0 * w.D * N, 10.0 * w.D * N
+    log(f"[bench] {args.workload}: {workloads.CONFIGS[cfg]}; N = {N} pairs, "
+        f"F_fwd = {f_fwd:.4g}, F_bwd = {f_bwd:.4g}")
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt).contiguous()
+    q, k, v, dO = up(w.q), up(w.k), up(w.v), up(w.dO)
+    idx = torch.from_numpy(np.ascontiguousarray(w.block_idx)).to(dev)
+    cu = None if not w.packed else torch.from_numpy(w.cu_seqlens).to(dev)
+    ms = w.max_seqlen if w.packed else None
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
+    stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms)
+    names = ("fwd", "prepare", "dq", "dkdv")
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse)
+        if evs is not None:
+            evs[1].record()
+        stages.prepare(o, dO)
+        if evs is not None:
+            evs[2].record()
+        stages.dq_stage(dO, lse)
+        if evs is not None:
+            evs[3].record()
+        stages.dkdv_stage(dO, lse)
+        if evs is not None:
+            evs[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {n: 0.0 for n in names}
+    for evs in events:
+        for j, n in enumerate(names):
+            stage_ms[n] += evs[j].elapsed_time(evs[j + 1])
+    stage_ms = {n: v / args.steps for n, v in stage_ms.items()}
+    ms_step = wall * 1e3 / args.steps
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"]
+    log(f"[bench] ms/step {ms_step:.3f}; stages (ms): " +
+        ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()))
+
+    dom = max(("fwd", "dq", "dkdv"), key=lambda n: stage_ms[n])
+    achieved = STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N / (stage_ms[dom] * 1e-3) / 1e12
+    src = source_hash()
+    kern = STAGE_KERNEL[dom]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(kern, args.workload, src), "kernel": kern,
+                "flops_per_launch": STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N,
+                "launch_ms": round(stage_ms[dom], 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle sample ({args.cpu_tokens} tokens per head) ...")
+        cpu = cpu_baseline(w, args.cpu_tokens)
+        log(f"[bench] CPU oracle: {cpu['value'] * 1e3:.2f} GFLOP/s in {cpu['seconds']} s "
+            f"on {cpu['cores']} threads")
+
+    if w.packed:
+        config = {"workload": args.workload, "description": workloads.CONFIGS[cfg],
+                  "n_seqs": w.n_seqs, "total_tokens": w.T, "max_seqlen": w.max_seqlen,
+                  "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "S": w.S}
+    else:
+        config = {"workload": args.workload, "description": workloads.CONFIGS[cfg], "B": w.B,
+                  "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size,
+                  "S": w.S}
+    config["useful_pairs"] = N
+    out = {
+        "metric": "fwd+bwd useful TFLOP/s (bf16, D128) + % of MI355X bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": config,
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(f_fwd / (stage_ms["fwd"] * 1e-3) / 1e12, 3),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
+        "bwd_frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "git": git_sha(),
+        "kernel_source_hash": src,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

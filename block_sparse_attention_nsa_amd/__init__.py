@@ -23,6 +23,7 @@ from . import _lib
 __all__ = [
     "nsa_sel_fwd",
     "nsa_sel_bwd",
+    "BwdStages",
     "nsa_sel_delta",
     "nsa_sel_invert",
     "bwd_workspace_bytes",
@@ -142,6 +143,41 @@ def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqle
                                  _ptr(ws), ws.numel(), _stream())
     _lib.check("nsa_sel_bwd", st)
     return dq, dk, dv
+
+
+class BwdStages:
+    """The backward as its three C-ABI stages on one workspace
+    (nsa_sel_bwd_prepare, nsa_sel_bwd_dq, nsa_sel_bwd_dkdv); calling them in
+    that order equals nsa_sel_bwd.  Buffers are allocated once here."""
+
+    def __init__(self, q, k, v, block_idx, block_size, scale=None, cu_seqlens=None,
+                 max_seqlen=None):
+        self.p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+        _check_tensors(q, k, v, block_idx, cu_seqlens, self.p)
+        self.q, self.k, self.v, self.idx, self.cu = q, k, v, block_idx, cu_seqlens
+        self.ws = torch.empty(max(bwd_workspace_bytes(self.p), 1), dtype=torch.uint8,
+                              device=q.device)
+        self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        self.lib = _lib.load()
+
+    def prepare(self, o, dO):
+        st = self.lib.nsa_sel_bwd_prepare(self.p, _ptr(o), _ptr(dO), _ptr(self.idx),
+                                          _ptr(self.cu), _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_prepare", st)
+
+    def dq_stage(self, dO, lse):
+        st = self.lib.nsa_sel_bwd_dq(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(dO),
+                                     _ptr(lse), _ptr(self.idx), _ptr(self.cu), _ptr(self.dq),
+                                     _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_dq", st)
+        return self.dq
+
+    def dkdv_stage(self, dO, lse):
+        st = self.lib.nsa_sel_bwd_dkdv(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                                       _ptr(dO), _ptr(lse), _ptr(self.cu), _ptr(self.dk),
+                                       _ptr(self.dv), _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_dkdv", st)
+        return self.dk, self.dv
 
 
 def nsa_sel_delta(o, dO, block_size, block_idx, k, scale=None, cu_seqlens=None, max_seqlen=None):

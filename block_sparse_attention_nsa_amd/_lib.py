@@ -16,6 +16,9 @@ EXPORTS = (
     "nsa_sel_fwd",
     "nsa_sel_bwd",
     "nsa_sel_bwd_workspace_bytes",
+    "nsa_sel_bwd_prepare",
+    "nsa_sel_bwd_dq",
+    "nsa_sel_bwd_dkdv",
     "nsa_sel_delta",
     "nsa_sel_invert",
     "nsa_sel_invert_tokens_capacity",
@@ -69,6 +72,12 @@ def load():
     lib.nsa_sel_bwd.restype = st
     lib.nsa_sel_bwd_workspace_bytes.argtypes = [P]
     lib.nsa_sel_bwd_workspace_bytes.restype = sz
+    lib.nsa_sel_bwd_prepare.argtypes = [P, vp, vp, ip, ip, vp, sz, vp]
+    lib.nsa_sel_bwd_prepare.restype = st
+    lib.nsa_sel_bwd_dq.argtypes = [P, vp, vp, vp, vp, fp, ip, ip, vp, vp, sz, vp]
+    lib.nsa_sel_bwd_dq.restype = st
+    lib.nsa_sel_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, fp, ip, vp, vp, vp, sz, vp]
+    lib.nsa_sel_bwd_dkdv.restype = st
     lib.nsa_sel_delta.argtypes = [P, vp, vp, ip, fp, vp]
     lib.nsa_sel_delta.restype = st
     lib.nsa_sel_invert.argtypes = [P, ip, ip, ip, ip, vp, sz, vp]

@@ -159,6 +159,80 @@ size_t elem_align(const nsa::HostProblem& hp) { return hp.dtype == NSA_BF16 ? 16
         if (e_ != hipSuccess) return hip_fail(e_, what); \
     } while (0)
 
+// Marks a tensor an entry point does not take (distinct from NULL, which is
+// an error for a non-empty tensor).
+const char g_absent_tag = 0;
+const void* const kAbsent = &g_absent_tag;
+
+// Shared checks of the backward entry points: problem, tensors (those given),
+// workspace size and alignment.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dO, *dq, *dk, *dv;
+    const float* lse;
+    const int32_t *idx, *cu;
+    void* ws;
+    size_t ws_bytes;
+};
+
+nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProblem& hp) {
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, a.cu));
+    const Sizes sz = sizes_of(hp);
+    const size_t al = elem_align(hp);
+    const struct {
+        const void* ptr;
+        int64_t n;
+        size_t al;
+        const char* name;
+    } ts[] = {{a.q, sz.q, al, "q"},     {a.k, sz.kv, al, "k"},      {a.v, sz.kv, al, "v"},
+              {a.o, sz.q, al, "o"},     {a.dO, sz.q, al, "dO"},     {a.dq, sz.q, al, "dq"},
+              {a.dk, sz.kv, al, "dk"},  {a.dv, sz.kv, al, "dv"},    {a.lse, sz.lse, 4, "lse"},
+              {a.idx, sz.idx, 4, "block_idx"}};
+    for (const auto& t : ts)
+        if (t.ptr != kAbsent) NSA_TRY(check_tensor(t.ptr, t.n, t.al, t.name));
+    const nsa::BwdWorkspace need = carve(hp, nullptr);
+    if (need.bytes && (!a.ws || a.ws_bytes < need.bytes))
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a.ws_bytes, need.bytes);
+    if (a.ws && misaligned(a.ws, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    hp.dev.cu = a.cu;
+    return NSA_OK;
+}
+
+nsa_status run_prepare(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
+    const nsa::BwdWorkspace ws = carve(hp, a.ws);
+    NSA_HIP(nsa::launch_delta(hp, a.o, a.dO, ws.delta, st), "delta launch");
+    NSA_HIP(nsa::launch_invert(hp, a.idx, ws, st), "inversion launch");
+    if (hp.dtype == NSA_BF16) NSA_HIP(nsa::launch_plan(hp, ws, st), "planner launch");
+    return NSA_OK;
+}
+
+nsa_status run_dq(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
+    const nsa::BwdWorkspace ws = carve(hp, a.ws);
+    if (hp.dtype == NSA_BF16) {
+        NSA_HIP(nsa::launch_dq_bf16(hp, a.q, a.k, a.v, a.dO, a.lse, ws.delta, a.idx, (void*)a.dq, st), "dQ launch");
+    } else {
+        NSA_HIP(nsa::launch_dq_f32(hp, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                                   (const float*)a.dO, a.lse, ws.delta, a.idx, (float*)a.dq, st),
+                "dQ launch");
+    }
+    return NSA_OK;
+}
+
+nsa_status run_dkdv(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
+    const nsa::BwdWorkspace ws = carve(hp, a.ws);
+    if (hp.dtype == NSA_BF16) {
+        NSA_HIP(nsa::launch_dkdv_bf16(hp, a.q, a.k, a.v, a.dO, a.lse, ws.delta, ws, (void*)a.dk,
+                                      (void*)a.dv, st),
+                "dK/dV launch");
+    } else {
+        NSA_HIP(nsa::launch_dkdv_f32(hp, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                                     (const float*)a.dO, a.lse, ws.delta, ws, (float*)a.dk,
+                                     (float*)a.dv, st),
+                "dK/dV launch");
+    }
+    return NSA_OK;
+}
+
 }  // namespace
 
 namespace nsa {
@@ -283,43 +357,51 @@ nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, c
                        void* dv, void* workspace, size_t workspace_bytes, nsa_stream_t stream) {
     g_last_error.clear();
     nsa::HostProblem hp;
-    NSA_TRY(make_problem(p, hp));
-    NSA_TRY(check_cu(hp, cu_seqlens));
-    const Sizes sz = sizes_of(hp);
-    const size_t a = elem_align(hp);
-    NSA_TRY(check_tensor(q, sz.q, a, "q"));
-    NSA_TRY(check_tensor(k, sz.kv, a, "k"));
-    NSA_TRY(check_tensor(v, sz.kv, a, "v"));
-    NSA_TRY(check_tensor(o, sz.q, a, "o"));
-    NSA_TRY(check_tensor(dO, sz.q, a, "dO"));
-    NSA_TRY(check_tensor(dq, sz.q, a, "dq"));
-    NSA_TRY(check_tensor(dk, sz.kv, a, "dk"));
-    NSA_TRY(check_tensor(dv, sz.kv, a, "dv"));
-    NSA_TRY(check_tensor(lse, sz.lse, 4, "lse"));
-    NSA_TRY(check_tensor(block_idx, sz.idx, 4, "block_idx"));
-    const nsa::BwdWorkspace need = carve(hp, nullptr);
-    if (need.bytes && (!workspace || workspace_bytes < need.bytes))
-        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need.bytes);
-    if (workspace && misaligned(workspace, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    if (sz.q == 0) return NSA_OK;
-    hp.dev.cu = cu_seqlens;
+    const BwdArgs a{q, k, v, o, dO, dq, dk, dv, lse, block_idx, cu_seqlens, workspace, workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const nsa::BwdWorkspace ws = carve(hp, workspace);
-    NSA_HIP(nsa::launch_delta(hp, o, dO, ws.delta, st), "delta launch");
-    NSA_HIP(nsa::launch_invert(hp, block_idx, ws, st), "inversion launch");
-    if (hp.dtype == NSA_BF16) {
-        NSA_HIP(nsa::launch_plan(hp, ws, st), "planner launch");
-        NSA_HIP(nsa::launch_dq_bf16(hp, q, k, v, dO, lse, ws.delta, block_idx, dq, st), "dQ launch");
-        NSA_HIP(nsa::launch_dkdv_bf16(hp, q, k, v, dO, lse, ws.delta, ws, dk, dv, st), "dK/dV launch");
-    } else {
-        NSA_HIP(nsa::launch_dq_f32(hp, (const float*)q, (const float*)k, (const float*)v,
-                                   (const float*)dO, lse, ws.delta, block_idx, (float*)dq, st),
-                "dQ launch");
-        NSA_HIP(nsa::launch_dkdv_f32(hp, (const float*)q, (const float*)k, (const float*)v,
-                                     (const float*)dO, lse, ws.delta, ws, (float*)dk, (float*)dv, st),
-                "dK/dV launch");
-    }
-    return NSA_OK;
+    NSA_TRY(run_prepare(hp, a, st));
+    NSA_TRY(run_dq(hp, a, st));
+    return run_dkdv(hp, a, st);
+}
+
+nsa_status nsa_sel_bwd_prepare(const nsa_sel_problem* p, const void* o, const void* dO,
+                               const int32_t* block_idx, const int32_t* cu_seqlens,
+                               void* workspace, size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{kAbsent, kAbsent, kAbsent, o,       dO,      kAbsent, kAbsent,
+                    kAbsent, (const float*)kAbsent, block_idx, cu_seqlens, workspace, workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    return run_prepare(hp, a, reinterpret_cast<hipStream_t>(stream));
+}
+
+nsa_status nsa_sel_bwd_dq(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                          const void* dO, const float* lse, const int32_t* block_idx,
+                          const int32_t* cu_seqlens, void* dq, void* workspace,
+                          size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{q, k, v, kAbsent, dO, dq, kAbsent, kAbsent, lse, block_idx, cu_seqlens,
+                    workspace, workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    return run_dq(hp, a, reinterpret_cast<hipStream_t>(stream));
+}
+
+nsa_status nsa_sel_bwd_dkdv(const nsa_sel_problem* p, const void* q, const void* k,
+                            const void* v, const void* dO, const float* lse,
+                            const int32_t* cu_seqlens, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{q, k, v, kAbsent, dO, kAbsent, dk, dv, lse, (const int32_t*)kAbsent,
+                    cu_seqlens, workspace, workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    return run_dkdv(hp, a, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -117,6 +117,25 @@ nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, c
                        void* dv, void* workspace, size_t workspace_bytes,
                        nsa_stream_t stream);
 
+/* The backward in three stages on one workspace; nsa_sel_bwd is exactly
+ * prepare, dq, dkdv in this order.  prepare computes Delta and the block ->
+ * query inversion (and the dK/dV work plan) into the workspace; dq and dkdv
+ * read them, so they need a workspace prepared for the same problem,
+ * block_idx, o and dO (a caller that reuses one block_idx with several
+ * q/k/v/dO may also keep the inversion: dkdv uses Delta, so o/dO must match).
+ * dkdv writes fp32 partials into the workspace. */
+nsa_status nsa_sel_bwd_prepare(const nsa_sel_problem* p, const void* o, const void* dO,
+                               const int32_t* block_idx, const int32_t* cu_seqlens,
+                               void* workspace, size_t workspace_bytes, nsa_stream_t stream);
+nsa_status nsa_sel_bwd_dq(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                          const void* dO, const float* lse, const int32_t* block_idx,
+                          const int32_t* cu_seqlens, void* dq, void* workspace,
+                          size_t workspace_bytes, nsa_stream_t stream);
+nsa_status nsa_sel_bwd_dkdv(const nsa_sel_problem* p, const void* q, const void* k,
+                            const void* v, const void* dO, const float* lse,
+                            const int32_t* cu_seqlens, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, nsa_stream_t stream);
+
 /* Delta preprocess alone: delta[row] = sum_d dO[row, d] * o[row, d] (float
  * accumulation), layout of lse.  The backward's first stage (page 3 names it
  * the do_dot step of its kernel chain). */

@@ -1,0 +1,42 @@
+"""Host-side pieces of bench.py (no GPU): its useful-pair count N agrees with
+the oracle's, and it refuses more than one GPU."""
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle
+import workloads
+from test_oracle_pins import _weird_idx
+
+
+def test_useful_pairs_matches_oracle_dense():
+    rng = np.random.default_rng(4)
+    idx = _weird_idx(rng, 2, 3, 97, 8, 5)
+    w = workloads.make_dense(2, 6, 3, 97, 16, 5, 8, "f32", block_idx=idx)
+    n = bench.useful_pairs(w.block_idx, 2, 8, bench.row_groups(w))
+    assert n == oracle.count_pairs(idx, 6, 8)
+
+
+def test_useful_pairs_matches_oracle_packed():
+    w = workloads.make_thd([30, 0, 64, 7], 8, 2, 16, 4, 8, "f32", "own_first_random", seed=2)
+    n = bench.useful_pairs(w.block_idx, 4, 8, bench.row_groups(w))
+    assert n == oracle.count_pairs_thd(w.block_idx, w.cu_seqlens, 8, 8)
+
+
+def test_config_pair_counts():
+    """Exact N of configs 0-3 (config 3 is dense causal: a closed form)."""
+    for cfg in (0, 1, 2):
+        w = workloads.make_config(cfg)
+        G = w.Hq // w.Hkv
+        n = bench.useful_pairs(w.block_idx, G, w.block_size, bench.row_groups(w))
+        assert n == oracle.count_pairs(w.block_idx, w.Hq, w.block_size)
+    w = workloads.make_config(3)
+    n = bench.useful_pairs(w.block_idx, 4, 64, bench.row_groups(w))
+    assert n == 4 * 32 * 4096 * 4097 // 2
+
+
+def test_refuses_several_gpus():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
