@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libnsa_sel.so")
-SOURCES = ["nsa_api.hip", "nsa_common.hip", "nsa_bf16.hip", "nsa_f32.hip"]
+SOURCES = ["nsa_api.hip", "nsa_common.hip", "nsa_query.hip", "nsa_bf16.hip", "nsa_f32.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # No packed-fp32 VALU instructions in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in VGPRs: avoids the AGPR<->VGPR copies the
+    # register allocator otherwise inserts around loop-carried MFMA chains.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

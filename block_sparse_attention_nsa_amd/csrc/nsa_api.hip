@@ -72,6 +72,9 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     if (NBmax > 8192) return fail(NSA_ERR_UNSUPPORTED, "ceil(max length / block_size) = %lld exceeds 8192", (long long)NBmax);
     const int G = p->Hq / p->Hkv;
     if ((int64_t)Tmax * G > (1ll << 30)) return fail(NSA_ERR_UNSUPPORTED, "max length * G exceeds 2^30 rows");
+    if ((int64_t)p->Hq * p->T * p->D >= (1ll << 31))
+        return fail(NSA_ERR_UNSUPPORTED, "Hq * T * D = %lld elements per batch entry exceeds 2^31 - 1",
+                    (long long)p->Hq * p->T * p->D);
     const int64_t ZH = (int64_t)Z * p->Hkv;
     if (ZH > 8192) return fail(NSA_ERR_UNSUPPORTED, "(batch or sequences) * Hkv = %lld exceeds 8192", (long long)ZH);
     const int64_t idx_rows = (int64_t)p->B * p->Hkv * p->T;
@@ -83,7 +86,12 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     d.Smin = (int)Smin; d.scale = p->scale; d.scale_log2 = p->scale * nsa::kLog2e; d.cu = nullptr;
     hp.dtype = p->dtype;
     hp.ZH = (int)ZH;
-    hp.CT = 64 * std::max(1, (Tmax + 64 * 64 - 1) / (64 * 64));
+    // Inversion chunks of CT tokens: small (16) for short sequences, growing
+    // so that the per-(z, hkv) chunk x block table stays within 2^14 entries.
+    {
+        const int64_t work = (int64_t)Tmax * NBmax;
+        hp.CT = 16 * (int)std::max<int64_t>(1, (work + (16ll << 14) - 1) / (16ll << 14));
+    }
     hp.C = (Tmax + hp.CT - 1) / hp.CT;
     hp.rows = (int64_t)p->B * p->Hq * p->T;
     hp.cap = Smin * idx_rows;
@@ -93,9 +101,9 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
     if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");
     hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
-    if (p->dtype == NSA_BF16 && nsa::fwd_bf16_lds_bytes(hp) > 65536)
+    if (p->dtype == NSA_BF16 && nsa::query_lds_bytes(hp) > 65536)
         return fail(NSA_ERR_UNSUPPORTED, "bf16 forward/dQ need %zu bytes of LDS for %lld blocks (max 65536)",
-                    nsa::fwd_bf16_lds_bytes(hp), (long long)NBmax);
+                    nsa::query_lds_bytes(hp), (long long)NBmax);
     return NSA_OK;
 }
 

@@ -93,37 +93,85 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
     return hipGetLastError();
 }
 
-// ---- inversion --------------------------------------------------------------
+// ---- inversion ----------------------------------------------------------------
+//
+// Per (z, hkv) the tokens are cut into C chunks of CT tokens.  count: per
+// chunk, how many of its tokens list each block (LDS histogram), stored
+// block-major [zh][u][c].  scan: one flat exclusive prefix over that
+// block-major array gives, for chunk c, where its first entry of block u goes
+// (all earlier blocks, then earlier chunks of u).  fill: one wave per chunk
+// walks its tokens in ascending order and appends each to its blocks' lists,
+// so every list is ascending (a stable counting sort; bit-exact).
+//
+// A row's entry u counts when 0 <= u < NBz and u*bs <= t, once however often
+// the row repeats it: the wave marks u in an LDS bitmap with an atomic OR
+// that returns the old word, so exactly one lane sees the bit clear.
 
-// Does slot si of this row contribute an entry for token t?  A block number
-// in [0, NBz) whose first key is <= t, and the first slot holding that block.
-__device__ __forceinline__ bool entry_valid(const int* row, int si, int u, int NBz, int bs, int t) {
-    if (u < 0 || u >= NBz || u * bs > t) return false;
-    for (int s2 = 0; s2 < si; ++s2)
-        if (row[s2] == u) return false;
-    return true;
+// Marks this lane's entry (if valid) in the wave's bitmap; true for the one
+// lane that set the bit first.
+__device__ __forceinline__ bool mark_first(uint32_t* seen, int u, bool valid) {
+    if (!valid) return false;
+    const uint32_t bit = 1u << (u & 31);
+    return !(atomicOr(&seen[u >> 5], bit) & bit);
+}
+__device__ __forceinline__ void unmark(uint32_t* seen, int u, bool valid) {
+    if (valid) atomicAnd(&seen[u >> 5], ~(1u << (u & 31)));
 }
 
-__global__ __launch_bounds__(256) void inv_count_kernel(Problem p, int CT, int C,
-                                                        const int* __restrict__ idx,
-                                                        int* __restrict__ chunk_pos) {
-    extern __shared__ int hist[];
+__device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t) {
+    return u >= 0 && u < NBz && u * bs <= t;
+}
+
+constexpr int kInvWaves = 4;
+constexpr int kRowStage = 4096;  // ints of block_idx staged in LDS at a time
+
+// Rows of tokens [t0, t1) of (z, hkv) are contiguous in block_idx: copy
+// them to LDS with coalesced loads (t1 - t0 <= kRowStage / S).
+__device__ __forceinline__ void stage_rows(const Problem& p, const Seq& s, const int* idx, int hkv,
+                                           int t0, int t1, int* buf) {
+    const int* src = idx_row(p, s, idx, hkv, t0);
+    const int n = (t1 - t0) * p.S;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) buf[i] = src[i];
+}
+
+__global__ __launch_bounds__(64 * kInvWaves) void inv_count_kernel(Problem p, int CT, int C,
+                                                                   const int* __restrict__ idx,
+                                                                   int* __restrict__ chunk_pos) {
+    extern __shared__ int sm[];
+    int* hist = sm;                                          // [NBmax]
+    const int NBW = (p.NBmax + 31) / 32;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t* seen = reinterpret_cast<uint32_t*>(sm + p.NBmax) + w * NBW;
+    int* rows = sm + p.NBmax + kInvWaves * NBW;              // [kRowStage]
     const int c = blockIdx.x, zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
     const int NBz = (s.len + p.bs - 1) / p.bs;
     for (int u = threadIdx.x; u < p.NBmax; u += blockDim.x) hist[u] = 0;
-    __syncthreads();
+    for (int i = lane; i < NBW; i += 64) seen[i] = 0u;
     const int t_end = min(c * CT + CT, s.len);
-    for (int t = c * CT + threadIdx.x; t < t_end; t += blockDim.x) {
-        const int* row = idx_row(p, s, idx, hkv, t);
-        for (int si = 0; si < p.S; ++si) {
-            int u = row[si];
-            if (entry_valid(row, si, u, NBz, p.bs, t)) atomicAdd(&hist[u], 1);
+    const int per = max(1, kRowStage / p.S);
+    for (int tb = c * CT; tb < t_end; tb += per) {
+        const int te = min(tb + per, t_end);
+        __syncthreads();
+        stage_rows(p, s, idx, hkv, tb, te, rows);
+        __syncthreads();
+        for (int t = tb + w; t < te; t += kInvWaves) {
+            const int* row = rows + (t - tb) * p.S;
+            for (int s0 = 0; s0 < p.S; s0 += 64) {
+                const int si = s0 + lane;
+                const int u = si < p.S ? row[si] : -1;
+                if (mark_first(seen, u, entry_ok(u, NBz, p.bs, t))) atomicAdd(&hist[u], 1);
+            }
+            for (int s0 = 0; s0 < p.S; s0 += 64) {
+                const int si = s0 + lane;
+                const int u = si < p.S ? row[si] : -1;
+                unmark(seen, u, entry_ok(u, NBz, p.bs, t));
+            }
         }
     }
     __syncthreads();
-    int* out = chunk_pos + ((int64_t)zh * C + c) * p.NBmax;
-    for (int u = threadIdx.x; u < p.NBmax; u += blockDim.x) out[u] = hist[u];
+    int* out = chunk_pos + (int64_t)zh * p.NBmax * C;
+    for (int u = threadIdx.x; u < p.NBmax; u += blockDim.x) out[(int64_t)u * C + c] = hist[u];
 }
 
 // Exclusive prefix sum of vals[0..n) (LDS) by one 256-thread block into
@@ -155,9 +203,43 @@ __device__ void block_excl_scan(const int* vals, int n, int* out, int* scratch) 
     __syncthreads();
 }
 
-// Per (z, hkv): list sizes, CSR offsets, per-chunk fill cursors, and the
+// In-place exclusive prefix sum of a global array by one 256-thread block,
+// 1024 entries per tile (coalesced int4 loads), tiles in order with a
+// running carry.  Returns the total to every thread.  scratch: 257 ints.
+__device__ int block_excl_scan_global(int* a, int64_t n, int* scratch) {
+    const int tid = threadIdx.x, nt = blockDim.x;  // nt == 256
+    int carry = 0;
+    for (int64_t base = 0; base < n; base += 4 * nt) {
+        const int64_t i0 = base + 4 * tid;
+        int v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (i0 + e < n) ? a[i0 + e] : 0;
+        const int sum = v[0] + v[1] + v[2] + v[3];
+        scratch[tid] = sum;
+        __syncthreads();
+        // Hillis-Steele inclusive scan of the 256 thread sums.
+        for (int off = 1; off < nt; off <<= 1) {
+            const int x = tid >= off ? scratch[tid - off] : 0;
+            __syncthreads();
+            scratch[tid] += x;
+            __syncthreads();
+        }
+        int run = carry + scratch[tid] - sum;
+        const int tile_total = scratch[nt - 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (i0 + e < n) a[i0 + e] = run;
+            run += v[e];
+        }
+        carry += tile_total;
+        __syncthreads();
+    }
+    return carry;
+}
+
+// Per (z, hkv): list cursors for every (block, chunk), CSR offsets, and the
 // number of dK/dV work items (ceil(rows / CR), rows = tokens * G) and fp32
-// partial slots (items, when a list needs more than one) per list.
+// partial slots (the items, when a list needs more than one) per list.
 __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
                                                        int* __restrict__ chunk_pos,
                                                        int* __restrict__ offsets,
@@ -167,25 +249,17 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     extern __shared__ int sm[];
     const int NB = p.NBmax;
     int* vals = sm;             // [NB]
-    int* scratch = sm + NB;     // [256]
+    int* scratch = sm + NB;     // [257]
     const int zh = blockIdx.x;
-    int* cp = chunk_pos + (int64_t)zh * C * NB;
+    int* cp = chunk_pos + (int64_t)zh * NB * C;
     int* off = offsets + (int64_t)zh * (NB + 1);
-    for (int u = threadIdx.x; u < NB; u += blockDim.x) {
-        int run = 0;
-        for (int c = 0; c < C; ++c) {
-            int x = cp[(int64_t)c * NB + u];
-            cp[(int64_t)c * NB + u] = run;
-            run += x;
-        }
-        vals[u] = run;
-    }
+    const int total = block_excl_scan_global(cp, (int64_t)NB * C, scratch);
+    for (int u = threadIdx.x; u < NB; u += blockDim.x) vals[u] = cp[(int64_t)u * C];
     __syncthreads();
-    block_excl_scan(vals, NB, off, scratch);
+    for (int u = threadIdx.x; u <= NB; u += blockDim.x) off[u] = u < NB ? vals[u] : total;
+    __syncthreads();
     for (int u = threadIdx.x; u < NB; u += blockDim.x) {
-        int o0 = off[u];
-        for (int c = 0; c < C; ++c) cp[(int64_t)c * NB + u] += o0;
-        int rows = vals[u] * p.G;
+        const int rows = (off[u + 1] - off[u]) * p.G;
         vals[u] = (rows + CR - 1) / CR;
     }
     __syncthreads();
@@ -202,38 +276,48 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
 }
 
 // Stable fill: one wave walks its chunk's tokens in ascending order and
-// appends each to the lists of the blocks it validly lists.
+// appends each to the lists of the blocks it validly lists (once each); the
+// rows are staged in LDS first.
 __global__ __launch_bounds__(64) void inv_fill_kernel(Problem p, int CT, int C,
                                                       const int* __restrict__ idx,
                                                       const int* __restrict__ chunk_pos,
                                                       int* __restrict__ tokens) {
     extern __shared__ int sm[];
-    int* cursor = sm;              // [NBmax]
-    int* rowbuf = sm + p.NBmax;    // [S]
+    const int NBW = (p.NBmax + 31) / 32;
+    int* cursor = sm;                                                    // [NBmax]
+    uint32_t* seen = reinterpret_cast<uint32_t*>(sm + p.NBmax);          // [NBW]
+    int* rows = sm + p.NBmax + NBW;                                      // [kRowStage]
     const int c = blockIdx.x, zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
     const int lane = threadIdx.x;
     const Seq s = seq_of(p, z);
     const int NBz = (s.len + p.bs - 1) / p.bs;
-    const int* cp = chunk_pos + ((int64_t)zh * C + c) * p.NBmax;
-    for (int u = lane; u < p.NBmax; u += 64) cursor[u] = cp[u];
+    const int* cp = chunk_pos + (int64_t)zh * p.NBmax * C;
+    for (int u = lane; u < p.NBmax; u += 64) cursor[u] = cp[(int64_t)u * C + c];
+    for (int i = lane; i < NBW; i += 64) seen[i] = 0u;
     int* out = tokens + region_base(p, s, hkv);
     const int t_end = min(c * CT + CT, s.len);
-    __syncthreads();
-    for (int t = c * CT; t < t_end; ++t) {
-        const int* row = idx_row(p, s, idx, hkv, t);
-        for (int si = lane; si < p.S; si += 64) rowbuf[si] = row[si];
+    const int per = max(1, kRowStage / p.S);
+    for (int tb = c * CT; tb < t_end; tb += per) {
+        const int te = min(tb + per, t_end);
         __syncthreads();
-        for (int s0 = 0; s0 < p.S; s0 += 64) {
-            int si = s0 + lane;
-            if (si < p.S) {
-                int u = rowbuf[si];
-                if (entry_valid(rowbuf, si, u, NBz, p.bs, t)) {
-                    int pos = cursor[u];
+        stage_rows(p, s, idx, hkv, tb, te, rows);
+        __syncthreads();
+        for (int t = tb; t < te; ++t) {
+            const int* row = rows + (t - tb) * p.S;
+            for (int s0 = 0; s0 < p.S; s0 += 64) {
+                const int si = s0 + lane;
+                const int u = si < p.S ? row[si] : -1;
+                if (mark_first(seen, u, entry_ok(u, NBz, p.bs, t))) {
+                    const int pos = cursor[u];
                     cursor[u] = pos + 1;
                     out[pos] = t;
                 }
             }
-            __syncthreads();
+            for (int s0 = 0; s0 < p.S; s0 += 64) {
+                const int si = s0 + lane;
+                const int u = si < p.S ? row[si] : -1;
+                unmark(seen, u, entry_ok(u, NBz, p.bs, t));
+            }
         }
     }
 }
@@ -255,16 +339,17 @@ __global__ __launch_bounds__(256) void plan_kernel(int ZH, const int* __restrict
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st) {
     const Problem& p = hp.dev;
-    if (hp.ZH == 0) return hipSuccess;
+    if (hp.ZH == 0 || hp.C == 0) return hipSuccess;
     dim3 grid(hp.C, hp.ZH);
-    size_t lds_count = sizeof(int) * p.NBmax;
-    hipLaunchKernelGGL(inv_count_kernel, grid, dim3(256), lds_count, st, p, hp.CT, hp.C,
-                       block_idx, ws.chunk_pos);
-    size_t lds_scan = sizeof(int) * (p.NBmax + 256);
+    const int NBW = (p.NBmax + 31) / 32;
+    size_t lds_count = sizeof(int) * (p.NBmax + kInvWaves * NBW + kRowStage);
+    hipLaunchKernelGGL(inv_count_kernel, grid, dim3(64 * kInvWaves), lds_count, st, p, hp.CT,
+                       hp.C, block_idx, ws.chunk_pos);
+    size_t lds_scan = sizeof(int) * (p.NBmax + 257);
     hipLaunchKernelGGL(inv_scan_kernel, dim3(hp.ZH), dim3(256), lds_scan, st, p, hp.C, hp.CR,
                        ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
                        ws.zh_base + 2 * (hp.ZH + 1));
-    size_t lds_fill = sizeof(int) * (p.NBmax + p.S);
+    size_t lds_fill = sizeof(int) * (p.NBmax + NBW + kRowStage);
     hipLaunchKernelGGL(inv_fill_kernel, grid, dim3(64), lds_fill, st, p, hp.CT, hp.C, block_idx,
                        ws.chunk_pos, ws.tokens);
     return hipGetLastError();
@@ -272,7 +357,7 @@ hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdW
 
 hipError_t launch_plan(const HostProblem& hp, const BwdWorkspace& ws, hipStream_t st) {
     if (hp.ZH == 0) return hipSuccess;
-    size_t lds = sizeof(int) * (hp.ZH + 256);
+    size_t lds = sizeof(int) * (hp.ZH + 257);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), lds, st, hp.ZH,
                        ws.zh_base + 2 * (hp.ZH + 1), ws.zh_base);
     return hipGetLastError();

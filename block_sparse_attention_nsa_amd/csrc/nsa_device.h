@@ -100,16 +100,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// Round to nearest even (inputs here are finite or +-inf; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// float -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 converts
+// two values per instruction (NaN stays NaN).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -140,6 +141,29 @@ __device__ __forceinline__ bf16x8 lds_col_operand(const uint16_t* tile, int stri
     uint2 lo = lds_read_tr(tile + (row_lo + 4 * g + r) * stride + col0 + 4 * c);
     uint2 hi = lds_read_tr(tile + (row_hi + 4 * g + r) * stride + col0 + 4 * c);
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Raw buffer access: a wave-uniform descriptor (base, size in bytes) and a
+// 32-bit per-lane byte offset.  Loads whose lane offset (+ immediate) lies
+// at or past the size return zeros, so a descriptor that ends at the last
+// valid row reads rows past it as 0.  (The scalar offset is not range
+// checked; it is only used for in-range strides.)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// The base and size must be wave-uniform; readfirstlane states it so the
+// compiler keeps the descriptor in SGPRs (no per-lane waterfall loop).
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(b, (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(buf_rsrc r, int voff, int soff) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {

@@ -65,6 +65,6 @@ hipError_t launch_dkdv_f32(const HostProblem& hp, const float* q, const float* k
                            const BwdWorkspace& ws, float* dk, float* dv, hipStream_t st);
 
 // Dynamic LDS the bf16 forward / dQ kernels need (0 if unsupported).
-size_t fwd_bf16_lds_bytes(const HostProblem& hp);
+size_t query_lds_bytes(const HostProblem& hp);
 
 }  // namespace nsa

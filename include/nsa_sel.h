@@ -49,7 +49,7 @@
  * 4 * (64 * (D + 8) + 6 * NBmax) <= 65536 bytes of forward/dQ LDS (NBmax =
  * ceil(max length / block_size); e.g. NBmax <= 1280 at D = 128).  For both:
  * S <= 4096, NBmax <= 8192, (B or n_seqs) * Hkv <= 8192, max length * G
- * <= 2^30.
+ * <= 2^30, Hq * T * D < 2^31 (per batch entry).
  */
 #ifndef NSA_SEL_H
 #define NSA_SEL_H
