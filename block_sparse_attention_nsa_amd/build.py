@@ -17,7 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(CSRC, "_build")
 LIB = os.path.join(HERE, "libnsa_sel.so")
-SOURCES = ["nsa_api.hip", "nsa_common.hip", "nsa_query.hip", "nsa_bf16.hip", "nsa_f32.hip"]
+SOURCES = ["nsa_api.hip", "nsa_common.hip", "nsa_query.hip", "nsa_dkdv.hip", "nsa_f32.hip"]
+# Kernels that keep matrix-core accumulators in AGPRs (one wave per SIMD,
+# up to 512 registers): built without the VGPR-only accumulator option.
+AGPR_SOURCES = {"nsa_dkdv.hip"}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -29,12 +32,14 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # No packed-fp32 VALU instructions in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Matrix-core accumulators in VGPRs: avoids the AGPR<->VGPR copies the
-    # register allocator otherwise inserts around loop-carried MFMA chains.
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
+
+
+# Matrix-core accumulators in VGPRs: avoids the AGPR<->VGPR copies the
+# register allocator otherwise inserts around loop-carried MFMA chains.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:
@@ -52,7 +57,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        extra = [] if src in AGPR_SOURCES else VGPR_FORM
+        cmd = [hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

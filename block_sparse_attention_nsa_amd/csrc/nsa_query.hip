@@ -38,7 +38,7 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // and the compacted union.
 template <int D>
 struct QLds {
-    static constexpr int kStride = D + 8;
+    static constexpr int kStride = D + 16;
     static constexpr int kTile = 32 * kStride;                 // elements per slice
     static constexpr int kStageBytes = 2 * 2 * kTile * 2;      // 2 stages x (K, V)
     static __host__ __device__ size_t bytes(int NBmax) {
