@@ -166,6 +166,70 @@ __device__ __forceinline__ uint4 buf_load16(buf_rsrc r, int voff, int soff) {
     return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
+// ---- 32-row tiles staged in LDS by buffer-to-LDS loads ---------------------
+// A 32-row x D bf16 tile, rows unpadded (each 1 KB buffer-to-LDS load fills
+// 1 KB of consecutive LDS: lane l writes bytes 16 l .. 16 l + 15), with the
+// 16-byte chunks of every row permuted so that both operand reads -- 16 rows
+// x one chunk (ds_read_b128) and 4 rows x 16 columns (ds_read_b64_tr_b16) --
+// spread evenly over the LDS banks.  The permutations were chosen by
+// measuring those two access patterns on gfx950 (a rotation by two chunks per
+// row for 256-byte rows, XOR swizzles for the shorter ones).
+template <int D>
+struct RowTile {
+    static constexpr int QCH = D / 8;       // 16-byte chunks per row
+    static constexpr int RB = 2 * D;        // bytes per row
+    static constexpr int TB = 32 * RB;      // bytes per tile
+    static constexpr int NI = TB / 1024;    // 1 KB loads per tile
+    // LDS slot of data chunk c of row r, and its inverse.
+    __host__ __device__ static constexpr int slot(int r, int c) {
+        return D == 128 ? ((c + 2 * r) & 15) : D == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
+    }
+    __host__ __device__ static constexpr int chunk(int r, int s) {
+        return D == 128 ? ((s - 2 * r) & 15) : D == 64 ? (s ^ (r & 7)) : (s ^ ((r >> 1) & 3));
+    }
+    // Byte offset of this lane's A operand (rows r = lane & 15, columns
+    // 32 kk + 8 (lane >> 4) .. + 7): one ds_read_b128; rows 16.. sit 16 RB
+    // further with the same slots.
+    __device__ static uint32_t a_off(int lane, int kk) {
+        const int r = lane & 15, g = lane >> 4;
+        return (uint32_t)(r * RB + 16 * slot(r, 4 * kk + g));
+    }
+    // Byte offset of this lane's transposed read (ds_read_b64_tr_b16) of rows
+    // 4 (lane >> 4) + (lane & 15) / 4, columns 16 dt + 4 (lane & 3) .. + 3.
+    __device__ static uint32_t t_off(int lane, int dt) {
+        const int rr = 4 * (lane >> 4) + ((lane & 15) >> 2), c = lane & 3;
+        return (uint32_t)(rr * RB + 16 * slot(rr, 2 * dt + (c >> 1)) + 8 * (c & 1));
+    }
+    static_assert(slot(16, 0) == slot(0, 0) && slot(17, 3) == slot(1, 3) && slot(31, 5) == slot(15, 5),
+                  "rows 16.. repeat the slots of rows 0..");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from the buffer into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(buf_rsrc r, void* dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, 0);
+}
+// 4 bytes per lane into LDS at dst + 4 * lane.
+__device__ __forceinline__ void dma4(buf_rsrc r, void* dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (int)voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order) and its LDS writes are done, then a
+// workgroup barrier.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.  Buffers written by buffer-to-LDS loads
+// are separate __shared__ variables, so the compiler can tell an access to
+// one stage from an in-flight load into another and adds no wait of its own.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
@@ -177,14 +241,26 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 
-// Max / sum over the four lanes l, l^16, l^32, l^48 (one C-layout column).
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one C-layout column),
+// with gfx950's lane-half swaps (v_permlane32_swap exchanges lanes 32..63 of
+// one operand with lanes 0..31 of the other, v_permlane16_swap the odd rows
+// of 16 lanes with the even ones): each lane ends up holding its own value
+// and its partner's, one in each result.
 __device__ __forceinline__ float col_max4(float v) {
-    v = fmaxf(v, shfl_xor(v, 16));
-    return fmaxf(v, shfl_xor(v, 32));
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t um = __float_as_uint(m);
+    const auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float col_sum4(float v) {
-    v += shfl_xor(v, 16);
-    return v + shfl_xor(v, 32);
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t um = __float_as_uint(m);
+    const auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Order this wave's LDS accesses: everything issued before is complete and

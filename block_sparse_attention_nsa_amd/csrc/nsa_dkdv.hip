@@ -27,29 +27,8 @@ namespace nsa {
 
 namespace {
 
-// ---- row tile layout ------------------------------------------------------
-// A 32-row x D bf16 tile, rows unpadded (each 1 KB buffer-to-LDS load fills
-// 1 KB of consecutive LDS), with the 16-byte chunks of every row permuted so
-// that both operand reads -- 16 rows x one chunk (ds_read_b128) and 4 rows x
-// 16 columns (ds_read_b64_tr_b16) -- spread evenly over the LDS banks.  The
-// permutations were chosen by measuring those two access patterns on gfx950.
-template <int D>
-struct Tile {
-    static constexpr int QCH = D / 8;       // 16-byte chunks per row
-    static constexpr int RB = 2 * D;        // bytes per row
-    static constexpr int TB = 32 * RB;      // bytes per tile
-    static constexpr int NI = TB / 1024;    // 1 KB loads per tile
-    // LDS slot of data chunk c of row r, and its inverse.
-    __device__ static constexpr int slot(int r, int c) {
-        return D == 128 ? ((c + 2 * r) & 15) : D == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
-    }
-    __device__ static constexpr int chunk(int r, int s) {
-        return D == 128 ? ((s - 2 * r) & 15) : D == 64 ? (s ^ (r & 7)) : (s ^ ((r >> 1) & 3));
-    }
-};
-
-// One stage of the ring: the Q and dO tiles of 32 rows and their per-row
-// token, lse and Delta.
+// One stage of the row ring: the Q and dO tiles of 32 rows (RowTile layout)
+// and their per-row token, lse and Delta.
 template <int D>
 struct alignas(16) Stage {
     uint16_t q[32 * D];
@@ -58,30 +37,6 @@ struct alignas(16) Stage {
     float lse[32];
     float dl[32];
 };
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from the buffer into LDS at dst + 16 * lane.
-__device__ __forceinline__ void dma16(buf_rsrc r, void* dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, 0);
-}
-// 4 bytes per lane into LDS at dst + 4 * lane.
-__device__ __forceinline__ void dma4(buf_rsrc r, void* dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (int)voff, 0, 0, 0);
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight
-// (they complete in issue order), and until its LDS writes are done; then a
-// workgroup barrier.  The asm statements keep the compiler from moving memory
-// accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (0 << 8) | (7 << 4) | ((N >> 4) << 14));
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 struct ItemRef {
     int zh, u, kitem, nitems;
@@ -160,7 +115,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
                  const int* __restrict__ zh_base, int CR, float* __restrict__ partials,
                  uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-    using L = Tile<D>;
+    using L = RowTile<D>;
     constexpr int NW = BS / 32, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
     constexpr int NJ = (NI + NW - 1) / NW;  // 1 KB row loads per tile for each wave (at most)
     __shared__ Stage<D> st0, st1, st2;
@@ -270,21 +225,13 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         }
     }
 
-    // LDS byte offsets inside a tile of this lane's operand reads.
-    //   A operand (16 rows x 32 columns): row r (+16 for the second row tile),
-    //   columns 32kk + 8g.., one ds_read_b128.
-    //   Transposed operand: rows 4g + (lane&15)/4 (+16), columns 16dt + 4(lane&3).
+    // LDS byte offsets inside a tile of this lane's operand reads (rows 16..
+    // of a tile sit 16 RB bytes further).
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) a_off[kk] = (uint32_t)(r * L::RB + 16 * L::slot(r, 4 * kk + g));
-    {
-        const int rr = 4 * g + (r >> 2), c = r & 3;
+    for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
-            t_off[dt] = (uint32_t)(rr * L::RB + 16 * L::slot(rr, 2 * dt + (c >> 1)) + 8 * (c & 1));
-    }
-    // Rows 16.. of a tile sit 16 * RB bytes further with the same slots.
-    static_assert(L::slot(16, 0) == L::slot(0, 0) && L::slot(17, 3) == L::slot(1, 3), "row period");
+    for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
 
     f32x4 dkt[2][ND], dvt[2][ND];
 #pragma unroll

@@ -6,9 +6,9 @@
 // of a GQA group share one block list and are stacked as the MFMA rows.  Each
 // wave holds RT tiles.  The workgroup walks the union of its tokens' listed
 // blocks in ascending order, 32 keys at a time ("jobs"); every K/V slice is
-// loaded from HBM once per workgroup (buffer loads, two jobs ahead) into a
-// double-buffered LDS stage and read by the waves whose tiles list that
-// block.  Per tile:
+// copied from HBM once per workgroup, straight into a three-stage LDS ring by
+// buffer loads that write LDS (two jobs ahead, no register staging), and read
+// by the waves whose tiles list that block.  Per tile:
 //   forward  S^T = K Q^T, mask, online softmax (base 2, lazy rescale),
 //            O^T += V^T P^T  (V read transposed from LDS: ds_read_b64_tr_b16)
 //   dQ       S^T = K Q^T, dP^T = V dO^T, dS = P (dP - Delta), dQ^T += K^T dS^T
@@ -33,16 +33,29 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
                                 pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
 }
 
-// LDS of one workgroup: two stages of K and V slices (32 keys x D, padded
-// rows), then per-block token masks (bit a = token T0 + a lists the block)
+// Keys per job: whole 64-key blocks (half blocks of 128), 32 for 32-key blocks.
+template <int BS>
+struct JobKeys {
+    static constexpr int JK = BS >= 64 ? 64 : 32;
+};
+
+// One stage of the K/V ring: JK-key slices of K and V, rows in the RowTile
+// layout (rows 32.. repeat the slots of rows 0..).
+template <int D, int JK>
+struct alignas(16) KVStage {
+    uint16_t k[JK * D];
+    uint16_t v[JK * D];
+};
+constexpr int kQStages = 3;
+
+// LDS of one workgroup: the ring (static, three separate variables) and, in
+// dynamic LDS, per-block token masks (bit a = token T0 + a lists the block)
 // and the compacted union.
-template <int D>
+template <int D, int JK>
 struct QLds {
-    static constexpr int kStride = D + 16;
-    static constexpr int kTile = 32 * kStride;                 // elements per slice
-    static constexpr int kStageBytes = 2 * 2 * kTile * 2;      // 2 stages x (K, V)
-    static __host__ __device__ size_t bytes(int NBmax) {
-        return (size_t)kStageBytes + (size_t)NBmax * 8 + (((size_t)NBmax * 2 + 15) & ~(size_t)15) + 16;
+    static constexpr size_t kStatic = (size_t)kQStages * sizeof(KVStage<D, JK>);
+    static __host__ __device__ size_t dynamic_bytes(int NBmax) {
+        return (size_t)NBmax * 8 + (((size_t)NBmax * 2 + 15) & ~(size_t)15) + 16;
     }
 };
 
@@ -134,7 +147,7 @@ __device__ int wg_union(const Problem& p, const Seq& s, const int* __restrict__ 
     return *n_out;
 }
 
-// The workgroup's walk: 32-key jobs (block ulist[iu], slice sb), slices that
+// The workgroup's walk: JK-key jobs (block ulist[iu], slice sb), slices that
 // start after the last token skipped.  All values wave-uniform.
 struct Job {
     int iu, sb, u, j0;
@@ -152,10 +165,11 @@ __device__ __forceinline__ Job first_job(const uint16_t* ulist, int nU) {
 }
 template <int BS>
 __device__ __forceinline__ Job next_job_q(Job c, const uint16_t* ulist, int nU, int t_last) {
+    constexpr int JK = JobKeys<BS>::JK;
     if (!c.ok) return c;
-    if (c.sb + 1 < BS / 32 && c.j0 + 32 <= t_last) {
+    if (c.sb + 1 < BS / JK && c.j0 + JK <= t_last) {
         ++c.sb;
-        c.j0 += 32;
+        c.j0 += JK;
         return c;
     }
     if (c.iu + 1 >= nU) {
@@ -169,50 +183,58 @@ __device__ __forceinline__ Job next_job_q(Job c, const uint16_t* ulist, int nU, 
     return c;
 }
 
-// This thread's share of one job's K and V slices (CH 16-byte chunks each).
-template <int D, int NT>
-struct SliceShare {
-    static constexpr int VCH = D / 8;                      // chunks per key row
-    static constexpr int CH = (32 * VCH + NT - 1) / NT;   // chunks per thread per tensor
-};
-template <int D, int NT>
-struct SliceRegs {
-    uint4 k[SliceShare<D, NT>::CH], v[SliceShare<D, NT>::CH];
-};
-
-template <int D, int NT>
-__device__ __forceinline__ void slice_load(const uint16_t* kb, const uint16_t* vb, int kst2, int j0,
-                                           int len, SliceRegs<D, NT>& sr) {
-    constexpr int VCH = SliceShare<D, NT>::VCH;
-    const char* kbase = reinterpret_cast<const char*>(kb) + (int64_t)j0 * kst2;
-    const char* vbase = reinterpret_cast<const char*>(vb) + (int64_t)j0 * kst2;
-    const uint32_t bytes = (uint32_t)((len - 1 - j0) * kst2 + 2 * D);
-    const buf_rsrc rk = make_rsrc(kbase, bytes), rv = make_rsrc(vbase, bytes);
+// Buffer-to-LDS loads of one job's K and V slices (JK keys from key j0):
+// 1 KB load jj (< 2 NI; K for jj < NI, V after) is issued by wave jj % NW,
+// lane l writing RowTile position 64 (jj % NI) + l.  Keys past the sequence
+// lie past the descriptors and load as zeros.
+template <int D, int NW, int JK>
+struct KVLoad {
+    using L = RowTile<D>;
+    static constexpr int NI = JK * 2 * D / 1024;
+    static constexpr int NJ = (2 * NI + NW - 1) / NW;  // loads per wave (at most)
+    uint32_t voff[NJ];   // byte offset of this lane's 16 bytes inside the slice
+    int jj[NJ];          // load index (>= 2 NI: none)
+    // w must be wave-uniform (it selects the descriptor of each load).
+    __device__ void init(int w, int lane, int kst2) {
+        w = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-    for (int i = 0; i < SliceShare<D, NT>::CH; ++i) {
-        const int c = i * NT + (int)threadIdx.x;
-        const int off = (c / VCH) * kst2 + 16 * (c % VCH);
-        // Chunks past the slice (c >= 32 * VCH) read past the descriptor and
-        // come back as zero; they are not stored.
-        const int voff = c < 32 * VCH ? off : 0x7fffffff;
-        sr.k[i] = buf_load16(rk, voff, 0);
-        sr.v[i] = buf_load16(rv, voff, 0);
-    }
-}
-
-template <int D, int NT>
-__device__ __forceinline__ void slice_store(const SliceRegs<D, NT>& sr, uint16_t* ks, uint16_t* vs) {
-    constexpr int VCH = SliceShare<D, NT>::VCH, ST = QLds<D>::kStride;
-#pragma unroll
-    for (int i = 0; i < SliceShare<D, NT>::CH; ++i) {
-        const int c = i * NT + (int)threadIdx.x;
-        if (c < 32 * VCH) {
-            const int o_ = (c / VCH) * ST + 8 * (c % VCH);
-            *reinterpret_cast<uint4*>(ks + o_) = sr.k[i];
-            *reinterpret_cast<uint4*>(vs + o_) = sr.v[i];
+        for (int j = 0; j < NJ; ++j) {
+            jj[j] = w + NW * j;
+            const int pos = 64 * (jj[j] % NI) + lane, row = pos / L::QCH;
+            voff[j] = (uint32_t)(row * kst2 + 16 * L::chunk(row, pos % L::QCH));
         }
     }
-}
+    // Loads this wave issues per job when it has its full share; kEven: all
+    // waves have it.
+    static constexpr int kPerWave = NJ;
+    static constexpr bool kEven = (2 * NI) % NW == 0;
+    __device__ bool full_share() const { return jj[NJ - 1] < 2 * NI; }
+    // Issued for every job slot, also past the last job (ok == false): those
+    // loads see an empty descriptor and write zeros into a free stage, so a
+    // wave always has the same number of loads in flight.
+    __device__ void issue(const uint16_t* kb, const uint16_t* vb, int kst2, int j0, int len,
+                          bool ok, KVStage<D, JK>& st) const {
+        j0 = ok ? j0 : 0;
+        const int64_t base = (int64_t)j0 * kst2;
+        const uint32_t bytes = ok ? (uint32_t)((int64_t)(len - 1 - j0) * kst2 + 2 * D) : 0u;
+        const buf_rsrc rk = make_rsrc(reinterpret_cast<const char*>(kb) + base, bytes);
+        const buf_rsrc rv = make_rsrc(reinterpret_cast<const char*>(vb) + base, bytes);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if constexpr (kEven) {
+                // Every wave has NJ loads: pick K or V without branching, so
+                // the count of loads in flight is the same on every path.
+                const bool isk = jj[j] < NI;
+                uint8_t* dst = isk ? reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j]
+                                   : reinterpret_cast<uint8_t*>(st.v) + 1024 * (jj[j] - NI);
+                dma16(isk ? rk : rv, dst, voff[j]);
+            } else {
+                if (jj[j] < NI) dma16(rk, reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j], voff[j]);
+                else if (jj[j] < 2 * NI) dma16(rv, reinterpret_cast<uint8_t*>(st.v) + 1024 * (jj[j] - NI), voff[j]);
+            }
+        }
+    }
+};
 
 }  // namespace
 
@@ -227,13 +249,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                                                         const int* __restrict__ idx,
                                                         uint16_t* __restrict__ o,
                                                         float* __restrict__ lse) {
-    constexpr int NT = NW * 64, KD = D / 32, ND = D / 16, ST = QLds<D>::kStride;
-    constexpr int TILE = QLds<D>::kTile;
+    using L = RowTile<D>;
+    constexpr int KD = D / 32, ND = D / 16, JK = JobKeys<BS>::JK, NKT = JK / 16, NKS = JK / 32;
+    __shared__ KVStage<D, JK> st0, st1, st2;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* stage = reinterpret_cast<uint16_t*>(smem);  // [2][K,V][TILE]
-    unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem + QLds<D>::kStageBytes);
+    unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
-    int* n_u = reinterpret_cast<int*>(smem + QLds<D>::bytes(p.NBmax) - 16);
+    int* n_u = reinterpret_cast<int*>(smem + QLds<D, JK>::dynamic_bytes(p.NBmax) - 16);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const WgCoord wc = wg_coord(p, qg);
@@ -245,6 +267,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const int kst2 = (int)s.k_st * 2;
     const uint16_t* kb = k + s.k_base + wc.hkv * s.k_sh;
     const uint16_t* vb = v + s.k_base + wc.hkv * s.k_sh;
+    using LD = KVLoad<D, NW, JK>;
+    LD ld;
+    ld.init(w, lane, kst2);
+    uint32_t a_off[KD], t_off[ND];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
 
     // Per-tile state of this lane's row.
     TileRow tr[RT];
@@ -269,103 +299,122 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
 
-    // Pipeline: slices loaded two jobs ahead (registers A/B), LDS stages 0/1.
-    Job j0 = first_job<BS>(ulist, nU);
-    Job j1 = next_job_q<BS>(j0, ulist, nU, t_last);
-    Job j2 = next_job_q<BS>(j1, ulist, nU, t_last);
-    SliceRegs<D, NT> ra, rb;
-    if (j0.ok) slice_load<D, NT>(kb, vb, kst2, j0.j0, s.len, ra);
-    if (j1.ok) slice_load<D, NT>(kb, vb, kst2, j1.j0, s.len, rb);
-    if (j0.ok) slice_store<D, NT>(ra, stage, stage + TILE);
-    __syncthreads();
-
-    auto do_job = [&](const Job& cur, int buf, SliceRegs<D, NT>& next2, const Job& jn2,
-                      SliceRegs<D, NT>& next1, const Job& jn1) {
-        if (jn2.ok) slice_load<D, NT>(kb, vb, kst2, jn2.j0, s.len, next2);
-        const uint16_t* ks = stage + buf * 2 * TILE;
-        const uint16_t* vs = ks + TILE;
+    auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
+        const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
+        const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
         const uint64_t bm = umask[cur.u];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < RT; ++i) any |= (bm & tmask[i]) != 0ull;
-        if (any) {
-            bf16x8 ka[2][KD];
+        if (!__builtin_amdgcn_readfirstlane((int)any)) return;
+        bf16x8 ka[NKT][KD];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int kk = 0; kk < KD; ++kk)
-                    ka[kt][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (16 * kt + r) * ST + 32 * kk + 8 * g));
+            for (int kk = 0; kk < KD; ++kk)
+                ka[kt][kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                if ((bm & tmask[i]) == 0ull) continue;
-                f32x4 sc[2];
+        for (int i = 0; i < RT; ++i) {
+            if ((bm & tmask[i]) == 0ull) continue;
+            f32x4 sc[NKT];
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < NKT; ++kt) {
+                sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) sc[kt] = mfma(ka[kt][kk], qf[i][kk], sc[kt]);
-                }
-                // No mask when every token of the tile lists the block, the
-                // slice ends before the tile's first token, and all rows exist.
-                const bool full = ((bm & tmask[i]) == tmask[i]) && (cur.j0 + 31 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) && tr[i].valid;
-                float mloc = kNegInfQ;
-                if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
+                for (int kk = 0; kk < KD; ++kk) sc[kt] = mfma(ka[kt][kk], qf[i][kk], sc[kt]);
+            }
+            // No mask when every token of the tile lists the block, the slice
+            // ends before the tile's first token, and all rows exist.
+            const bool full = ((bm & tmask[i]) == tmask[i]) &&
+                              (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
+                              tr[i].valid;
+            float mloc = kNegInfQ;
+            if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, sc[kt][e]);
-                } else {
-                    const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
-                    const int lim = sel ? tr[i].t - cur.j0 : -1;
+                    for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, sc[kt][e]);
+            } else {
+                const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
+                const int lim = sel ? tr[i].t - cur.j0 : -1;
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
-                            mloc = fmaxf(mloc, sc[kt][e]);
-                        }
-                }
-                const float mblk = col_max4(mloc);
-                const bool grow = mblk * c2 > m_run[i] * c2 + kLazyQ;
-                if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
-                    const float m_new = grow ? mblk : m_run[i];
-                    const float alpha = grow ? fast_exp2((m_run[i] - m_new) * c2) : 1.f;
-#pragma unroll
-                    for (int dt = 0; dt < ND; ++dt) acc[i][dt] *= alpha;
-                    l_run[i] *= alpha;
-                    m_run[i] = m_new;
-                }
-                const float mc = m_run[i] == kNegInfQ ? 0.f : m_run[i] * c2;
-                float pv[2][4];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        pv[kt][e] = fast_exp2(fmaf(sc[kt][e], c2, -mc));
-                        l_run[i] += pv[kt][e];
+                        if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
+                        mloc = fmaxf(mloc, sc[kt][e]);
                     }
-                const bf16x8 pb = pack8(pv[0], pv[1]);
+            }
+            const float mblk = col_max4(mloc);
+            const bool grow = mblk * c2 > m_run[i] * c2 + kLazyQ;
+            if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
+                const float m_new = grow ? mblk : m_run[i];
+                const float alpha = grow ? fast_exp2((m_run[i] - m_new) * c2) : 1.f;
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) acc[i][dt] *= alpha;
+                l_run[i] *= alpha;
+                m_run[i] = m_new;
+            }
+            const float mc = m_run[i] == kNegInfQ ? 0.f : m_run[i] * c2;
+            float pv[NKT][4];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pv[kt][e] = fast_exp2(fmaf(sc[kt][e], c2, -mc));
+                    l_run[i] += pv[kt][e];
+                }
+            // O^T += V^T P^T, 32 keys per step: keys 32ks + 4g + e and
+            // 32ks + 16 + 4g + e are the ones the C layout of S gave this lane.
+#pragma unroll
+            for (int ks_ = 0; ks_ < NKS; ++ks_) {
+                const bf16x8 pb = pack8(pv[2 * ks_], pv[2 * ks_ + 1]);
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) {
-                    const bf16x8 va = lds_col_operand(vs, ST, 0, 16, 16 * dt, lane);
+                    const uint8_t* vb0 = vs + t_off[dt] + 32 * ks_ * L::RB;
+                    const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
+                    const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
                     acc[i][dt] = mfma(va, pb, acc[i][dt]);
                 }
             }
         }
-        if (jn1.ok) slice_store<D, NT>(next1, stage + (buf ^ 1) * 2 * TILE, stage + (buf ^ 1) * 2 * TILE + TILE);
-        __syncthreads();
     };
 
-    while (j0.ok) {
-        Job j3 = next_job_q<BS>(j2, ulist, nU, t_last);
-        do_job(j0, 0, ra, j2, rb, j1);
-        if (!j1.ok) break;
-        Job j4 = next_job_q<BS>(j3, ulist, nU, t_last);
-        do_job(j1, 1, rb, j3, ra, j2);
-        j0 = j2;
-        j1 = j3;
-        j2 = j4;
+    // Ring: job i computes stage i % 3 while job i + 2 loads into stage
+    // (i + 2) % 3 (last read by job i - 1; the barrier ending it freed it).
+    const bool full_share = ld.full_share();
+    auto ring_wait = [&]() {
+        if constexpr (LD::kEven) {
+            wait_vm_barrier<LD::kPerWave>();
+        } else {
+            if (full_share) wait_vm_barrier<LD::kPerWave>(); else wait_vm_barrier<0>();
+        }
+    };
+    auto step = [&](const Job& cur, const KVStage<D, JK>& sc_, const Job& nx2, KVStage<D, JK>& sn2) {
+        ld.issue(kb, vb, kst2, nx2.j0, s.len, nx2.ok, sn2);
+        compute(cur, sc_);
+        ring_wait();
+    };
+    Job jc = first_job<BS>(ulist, nU);
+    Job jn1 = next_job_q<BS>(jc, ulist, nU, t_last);
+    Job jn2 = next_job_q<BS>(jn1, ulist, nU, t_last);
+    ld.issue(kb, vb, kst2, jc.j0, s.len, jc.ok, st0);
+    ld.issue(kb, vb, kst2, jn1.j0, s.len, jn1.ok, st1);
+    ring_wait();
+    while (jc.ok) {
+        step(jc, st0, jn2, st2);
+        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, st1, jn2, st0);
+        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, st2, jn2, st1);
+        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
     }
+    // The ring's last loads (of job slots past the end) finish before the
+    // wave leaves, so none writes LDS after the workgroup is gone.
+    wait_vm_barrier<0>();
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -394,13 +443,13 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     Problem p, QGeo qg, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     const float* __restrict__ delta, const int* __restrict__ idx, uint16_t* __restrict__ dq) {
-    constexpr int NT = NW * 64, KD = D / 32, ND = D / 16, ST = QLds<D>::kStride;
-    constexpr int TILE = QLds<D>::kTile;
+    using L = RowTile<D>;
+    constexpr int KD = D / 32, ND = D / 16, JK = JobKeys<BS>::JK, NKT = JK / 16, NKS = JK / 32;
+    __shared__ KVStage<D, JK> st0, st1, st2;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
-    unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem + QLds<D>::kStageBytes);
+    unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
-    int* n_u = reinterpret_cast<int*>(smem + QLds<D>::bytes(p.NBmax) - 16);
+    int* n_u = reinterpret_cast<int*>(smem + QLds<D, JK>::dynamic_bytes(p.NBmax) - 16);
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const WgCoord wc = wg_coord(p, qg);
@@ -412,6 +461,14 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const int kst2 = (int)s.k_st * 2;
     const uint16_t* kb = k + s.k_base + wc.hkv * s.k_sh;
     const uint16_t* vb = v + s.k_base + wc.hkv * s.k_sh;
+    using LD = KVLoad<D, NW, JK>;
+    LD ld;
+    ld.init(w, lane, kst2);
+    uint32_t a_off[KD], t_off[ND];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
 
     TileRow tr[RT];
     uint64_t tmask[RT];
@@ -441,88 +498,98 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
 
-    Job j0 = first_job<BS>(ulist, nU);
-    Job j1 = next_job_q<BS>(j0, ulist, nU, t_last);
-    Job j2 = next_job_q<BS>(j1, ulist, nU, t_last);
-    SliceRegs<D, NT> ra, rb;
-    if (j0.ok) slice_load<D, NT>(kb, vb, kst2, j0.j0, s.len, ra);
-    if (j1.ok) slice_load<D, NT>(kb, vb, kst2, j1.j0, s.len, rb);
-    if (j0.ok) slice_store<D, NT>(ra, stage, stage + TILE);
-    __syncthreads();
-
-    auto do_job = [&](const Job& cur, int buf, SliceRegs<D, NT>& next2, const Job& jn2,
-                      SliceRegs<D, NT>& next1, const Job& jn1) {
-        if (jn2.ok) slice_load<D, NT>(kb, vb, kst2, jn2.j0, s.len, next2);
-        const uint16_t* ks = stage + buf * 2 * TILE;
-        const uint16_t* vs = ks + TILE;
+    auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
+        const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
+        const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
         const uint64_t bm = umask[cur.u];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < RT; ++i) any |= (bm & tmask[i]) != 0ull;
-        if (any) {
-            bf16x8 ka[2][KD], va[2][KD];
+        if (!__builtin_amdgcn_readfirstlane((int)any)) return;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+        for (int i = 0; i < RT; ++i) {
+            if ((bm & tmask[i]) == 0ull) continue;
+            f32x4 sc[NKT], dp[NKT];
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) {
-                    const int o_ = (16 * kt + r) * ST + 32 * kk + 8 * g;
-                    ka[kt][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(ks + o_));
-                    va[kt][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(vs + o_));
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
+                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + a_off[kk] + kt * 16 * L::RB);
+                    sc[kt] = mfma(ka, qf[i][kk], sc[kt]);
+                    dp[kt] = mfma(va, df[i][kk], dp[kt]);
                 }
+            }
+            const bool full = ((bm & tmask[i]) == tmask[i]) &&
+                              (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
+                              tr[i].valid;
+            if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
+                const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
+                const int lim = sel ? tr[i].t - cur.j0 : -1;
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                if ((bm & tmask[i]) == 0ull) continue;
-                f32x4 sc[2], dp[2];
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int e = 0; e < 4; ++e)
+                        if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
+            }
+            float ds[NKT][4];
 #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) {
-                        sc[kt] = mfma(ka[kt][kk], qf[i][kk], sc[kt]);
-                        dp[kt] = mfma(va[kt][kk], df[i][kk], dp[kt]);
-                    }
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float P = fast_exp2(fmaf(sc[kt][e], c2, nlse2[i]));
+                    ds[kt][e] = P * (dp[kt][e] - dl[i]);
                 }
-                const bool full = ((bm & tmask[i]) == tmask[i]) && (cur.j0 + 31 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) && tr[i].valid;
-                if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
-                    const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
-                    const int lim = sel ? tr[i].t - cur.j0 : -1;
+            // dQ^T += K^T dS^T, 32 keys per step.
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
-                }
-                float ds[2][4];
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float P = fast_exp2(fmaf(sc[kt][e], c2, nlse2[i]));
-                        ds[kt][e] = P * (dp[kt][e] - dl[i]);
-                    }
-                const bf16x8 dsb = pack8(ds[0], ds[1]);
+            for (int ks_ = 0; ks_ < NKS; ++ks_) {
+                const bf16x8 dsb = pack8(ds[2 * ks_], ds[2 * ks_ + 1]);
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) {
-                    const bf16x8 kta = lds_col_operand(ks, ST, 0, 16, 16 * dt, lane);
+                    const uint8_t* kb0 = ks + t_off[dt] + 32 * ks_ * L::RB;
+                    const uint2 k0 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0));
+                    const uint2 k1 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0 + 16 * L::RB));
+                    const bf16x8 kta = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
                     acc[i][dt] = mfma(kta, dsb, acc[i][dt]);
                 }
             }
         }
-        if (jn1.ok) slice_store<D, NT>(next1, stage + (buf ^ 1) * 2 * TILE, stage + (buf ^ 1) * 2 * TILE + TILE);
-        __syncthreads();
     };
 
-    while (j0.ok) {
-        Job j3 = next_job_q<BS>(j2, ulist, nU, t_last);
-        do_job(j0, 0, ra, j2, rb, j1);
-        if (!j1.ok) break;
-        Job j4 = next_job_q<BS>(j3, ulist, nU, t_last);
-        do_job(j1, 1, rb, j3, ra, j2);
-        j0 = j2;
-        j1 = j3;
-        j2 = j4;
+    const bool full_share = ld.full_share();
+    auto ring_wait = [&]() {
+        if constexpr (LD::kEven) {
+            wait_vm_barrier<LD::kPerWave>();
+        } else {
+            if (full_share) wait_vm_barrier<LD::kPerWave>(); else wait_vm_barrier<0>();
+        }
+    };
+    auto step = [&](const Job& cur, const KVStage<D, JK>& sc_, const Job& nx2, KVStage<D, JK>& sn2) {
+        ld.issue(kb, vb, kst2, nx2.j0, s.len, nx2.ok, sn2);
+        compute(cur, sc_);
+        ring_wait();
+    };
+    Job jc = first_job<BS>(ulist, nU);
+    Job jn1 = next_job_q<BS>(jc, ulist, nU, t_last);
+    Job jn2 = next_job_q<BS>(jn1, ulist, nU, t_last);
+    ld.issue(kb, vb, kst2, jc.j0, s.len, jc.ok, st0);
+    ld.issue(kb, vb, kst2, jn1.j0, s.len, jn1.ok, st1);
+    ring_wait();
+    while (jc.ok) {
+        step(jc, st0, jn2, st2);
+        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, st1, jn2, st0);
+        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, st2, jn2, st1);
+        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
     }
+    // The ring's last loads (of job slots past the end) finish before the
+    // wave leaves, so none writes LDS after the workgroup is gone.
+    wait_vm_barrier<0>();
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -564,12 +631,23 @@ QGeo q_geo(const HostProblem& hp) {
 
 size_t query_lds_bytes(const HostProblem& hp) {
     switch (hp.dev.D) {
-        case 32: return QLds<32>::bytes(hp.dev.NBmax);
-        case 64: return QLds<64>::bytes(hp.dev.NBmax);
-        case 128: return QLds<128>::bytes(hp.dev.NBmax);
+        case 32: return (hp.dev.bs >= 64 ? QLds<32, 64>::kStatic : QLds<32, 32>::kStatic) + QLds<32, 32>::dynamic_bytes(hp.dev.NBmax);
+        case 64: return (hp.dev.bs >= 64 ? QLds<64, 64>::kStatic : QLds<64, 32>::kStatic) + QLds<64, 32>::dynamic_bytes(hp.dev.NBmax);
+        case 128: return (hp.dev.bs >= 64 ? QLds<128, 64>::kStatic : QLds<128, 32>::kStatic) + QLds<128, 32>::dynamic_bytes(hp.dev.NBmax);
     }
     return 0;
 }
+
+namespace {
+size_t query_dynamic_lds(const HostProblem& hp) {
+    switch (hp.dev.D) {
+        case 32: return QLds<32, 32>::dynamic_bytes(hp.dev.NBmax);
+        case 64: return QLds<64, 32>::dynamic_bytes(hp.dev.NBmax);
+        case 128: return QLds<128, 32>::dynamic_bytes(hp.dev.NBmax);
+    }
+    return 0;
+}
+}  // namespace
 
 // Waves actually holding tiles (tiles beyond TW*tiles-per-token are idle but
 // still take part in staging).
@@ -592,7 +670,7 @@ hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, 
     const QGeo qg = q_geo(hp);
     const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
     if (grid == 0) return hipSuccess;
-    const size_t lds = query_lds_bytes(hp);
+    const size_t lds = query_dynamic_lds(hp);
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
                    hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT, kNW>), dim3(grid), dim3(kNW * 64), lds,
                                       st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
@@ -606,7 +684,7 @@ hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, c
     const QGeo qg = q_geo(hp);
     const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
     if (grid == 0) return hipSuccess;
-    const size_t lds = query_lds_bytes(hp);
+    const size_t lds = query_dynamic_lds(hp);
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
                    hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT, kNW>), dim3(grid), dim3(kNW * 64), lds,
                                       st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,

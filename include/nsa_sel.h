@@ -46,8 +46,9 @@
  * Supported (else NSA_ERR_UNSUPPORTED): dtype f32 with D in {16, 32, 64,
  * 128} and any block_size >= 1 (vector-ALU kernels); dtype bf16 with D in
  * {32, 64, 128} and block_size in {32, 64, 128} (matrix-core kernels), and
- * 256 * (D + 16) + 10 * NBmax + 32 <= 65536 bytes of forward/dQ LDS (NBmax =
- * ceil(max length / block_size); e.g. NBmax <= 2864 at D = 128).  For both:
+ * 12 * JK * D + 10 * NBmax + 32 <= 163840 bytes of forward/dQ LDS (JK = 64
+ * for block_size >= 64, else 32; NBmax = ceil(max length / block_size); e.g.
+ * NBmax <= 6550 at D = 128, block_size 64).  For both:
  * S <= 4096, NBmax <= 8192, (B or n_seqs) * Hkv <= 8192, max length * G
  * <= 2^30, Hq * T * D < 2^31 (per batch entry).
  */

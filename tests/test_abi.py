@@ -70,7 +70,7 @@ def _fwd(p, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cu=None, o=FAKE, lse=FAKE):
     (dict(D=24), _lib.NSA_ERR_UNSUPPORTED, "D in"),
     (dict(T=1 << 20, block_size=16), _lib.NSA_ERR_UNSUPPORTED, "8192"),
     (dict(S=5000), _lib.NSA_ERR_UNSUPPORTED, "slots"),
-    (dict(dtype=1, D=128, block_size=32, T=32 * 4000), _lib.NSA_ERR_UNSUPPORTED, "LDS"),
+    (dict(dtype=1, D=128, block_size=64, T=64 * 7000), _lib.NSA_ERR_UNSUPPORTED, "LDS"),
     (dict(B=9000, Hkv=1, Hq=1), _lib.NSA_ERR_UNSUPPORTED, "exceeds 8192"),
     (dict(layout=1, B=2), _lib.NSA_ERR_INVALID_ARG, "B == 1"),
     (dict(layout=1, n_seqs=2, max_seqlen=300), _lib.NSA_ERR_INVALID_ARG, "max_seqlen"),
