@@ -46,14 +46,15 @@ struct alignas(16) KVStage {
     uint16_t k[JK * D];
     uint16_t v[JK * D];
 };
-constexpr int kQStages = 3;
+constexpr int kQStages = 4;  // ring depth
+constexpr int kQAhead = 2;   // jobs between issuing a stage's loads and computing it
 
-// LDS of one workgroup: the ring (static, three separate variables) and, in
+// LDS of one workgroup: the ring (static, separate variables) and, in
 // dynamic LDS, per-block token masks (bit a = token T0 + a lists the block)
 // and the compacted union.
 template <int D, int JK>
 struct QLds {
-    static constexpr size_t kStatic = (size_t)kQStages * sizeof(KVStage<D, JK>);
+    static constexpr size_t kStatic = (size_t)kQStages * sizeof(KVStage<D, JK>) + 64;
     static __host__ __device__ size_t dynamic_bytes(int NBmax) {
         return (size_t)NBmax * 8 + (((size_t)NBmax * 2 + 15) & ~(size_t)15) + 16;
     }
@@ -236,6 +237,117 @@ struct KVLoad {
     }
 };
 
+// vmcnt(N) alone (no barrier).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+
+// LDS address of a __shared__ int (for the counter instructions below).
+__device__ __forceinline__ uint32_t lds_addr(const int* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)p;
+}
+
+// Waits until the LDS counter reaches target.  Every wave of the workgroup
+// eventually adds its share (see q_ring), so the wait ends; the iteration cap
+// only bounds it should that ever fail.  The counter is read with a plain
+// ds_read_b32 in asm: to the compiler it is unrelated to the stages that
+// buffer-to-LDS loads are filling, so it adds no vector-memory wait.
+__device__ __forceinline__ void spin_ge(const int* ctr, int target) {
+    const uint32_t a = lds_addr(ctr);
+    for (int it = 0; it < (1 << 18); ++it) {
+        int v;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+    }
+}
+// One count from this wave (LDS operations of a wave are processed in order,
+// so its earlier LDS reads and writes are done first).
+__device__ __forceinline__ void signal(int* ctr, int lane) {
+    if (lane == 0) asm volatile("ds_add_u32 %0, %1" : : "v"(lds_addr(ctr)), "v"(1) : "memory");
+}
+
+// The workgroup's walk over its jobs with a ring of kQStages K/V stages and
+// no workgroup barrier per job: waves advance at their own pace, at most one
+// job apart (slack kQAhead - 1), synchronised by two counters per stage.
+//   landed[s]: waves whose share of the stage's job has arrived in LDS;
+//   done[s]:   waves that finished computing the stage's job.
+// Job j lives in stage j % kQStages.  In its step j a wave
+//   1. waits until every wave finished job j + A - NS (the last user of the
+//      stage job j + A goes to), then issues its share of job j + A;
+//   2. waits for its own share of job j + 1 (vmcnt) and counts it in landed;
+//   3. waits until all shares of job j landed, computes job j, counts done.
+// The slowest wave can always proceed (everything it waits for was counted
+// by waves at or ahead of it), so the walk ends.  Counts are cumulative: the
+// u-th use of a stage is complete at NW * (u + 1).
+template <int D, int BS, int NW, class Compute>
+__device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const uint16_t* kb,
+                                       const uint16_t* vb, int kst2, int len,
+                                       const uint16_t* ulist, int nU, int t_last, int lane,
+                                       Compute&& compute) {
+    constexpr int JK = JobKeys<BS>::JK, NS = kQStages, A = kQAhead;
+    using LD = KVLoad<D, NW, JK>;
+    static_assert(NS == 4 && A == 2, "the unrolled walk below is written for 4 stages, 2 ahead");
+    __shared__ KVStage<D, JK> s0, s1, s2, s3;
+    __shared__ int landed[NS], done[NS];
+    if (threadIdx.x < NS) {
+        landed[threadIdx.x] = 0;
+        done[threadIdx.x] = 0;
+    }
+    __syncthreads();
+    const bool full = ld.full_share();
+    auto own_landed = [&]() {
+        if constexpr (LD::kEven) {
+            wait_vm<(A - 1) * LD::kPerWave>();
+        } else {
+            if (full) wait_vm<(A - 1) * LD::kPerWave>(); else wait_vm<0>();
+        }
+    };
+    int j = 0;
+    auto step = [&](const Job& cur, const Job& iss, const KVStage<D, JK>& cs, KVStage<D, JK>& is,
+                    int* land_c, int* land_n, int* done_c, int* done_i) {
+        const int jf = j + A - NS;
+        if (jf >= 0) spin_ge(done_i, NW * (jf / NS + 1));
+        ld.issue(kb, vb, kst2, iss.j0, len, iss.ok, is);
+        own_landed();
+        signal(land_n, lane);
+        spin_ge(land_c, NW * (j / NS + 1));
+        compute(cur, cs);
+        signal(done_c, lane);
+        ++j;
+    };
+    Job jc = first_job<BS>(ulist, nU);
+    Job ji = jc;
+    ld.issue(kb, vb, kst2, ji.j0, len, ji.ok, s0);
+    ji = next_job_q<BS>(ji, ulist, nU, t_last);
+    ld.issue(kb, vb, kst2, ji.j0, len, ji.ok, s1);
+    ji = next_job_q<BS>(ji, ulist, nU, t_last);
+    own_landed();
+    signal(&landed[0], lane);
+    while (jc.ok) {
+        step(jc, ji, s0, s2, &landed[0], &landed[1], &done[0], &done[2]);
+        jc = next_job_q<BS>(jc, ulist, nU, t_last);
+        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, ji, s1, s3, &landed[1], &landed[2], &done[1], &done[3]);
+        jc = next_job_q<BS>(jc, ulist, nU, t_last);
+        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, ji, s2, s0, &landed[2], &landed[3], &done[2], &done[0]);
+        jc = next_job_q<BS>(jc, ulist, nU, t_last);
+        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        if (!jc.ok) break;
+        step(jc, ji, s3, s1, &landed[3], &landed[0], &done[3], &done[1]);
+        jc = next_job_q<BS>(jc, ulist, nU, t_last);
+        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+    }
+    // Loads of job slots past the end finish before the wave leaves.
+    wait_vm<0>();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -251,7 +363,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                                                         float* __restrict__ lse) {
     using L = RowTile<D>;
     constexpr int KD = D / 32, ND = D / 16, JK = JobKeys<BS>::JK, NKT = JK / 16, NKS = JK / 32;
-    __shared__ KVStage<D, JK> st0, st1, st2;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
@@ -381,40 +492,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         }
     };
 
-    // Ring: job i computes stage i % 3 while job i + 2 loads into stage
-    // (i + 2) % 3 (last read by job i - 1; the barrier ending it freed it).
-    const bool full_share = ld.full_share();
-    auto ring_wait = [&]() {
-        if constexpr (LD::kEven) {
-            wait_vm_barrier<LD::kPerWave>();
-        } else {
-            if (full_share) wait_vm_barrier<LD::kPerWave>(); else wait_vm_barrier<0>();
-        }
-    };
-    auto step = [&](const Job& cur, const KVStage<D, JK>& sc_, const Job& nx2, KVStage<D, JK>& sn2) {
-        ld.issue(kb, vb, kst2, nx2.j0, s.len, nx2.ok, sn2);
-        compute(cur, sc_);
-        ring_wait();
-    };
-    Job jc = first_job<BS>(ulist, nU);
-    Job jn1 = next_job_q<BS>(jc, ulist, nU, t_last);
-    Job jn2 = next_job_q<BS>(jn1, ulist, nU, t_last);
-    ld.issue(kb, vb, kst2, jc.j0, s.len, jc.ok, st0);
-    ld.issue(kb, vb, kst2, jn1.j0, s.len, jn1.ok, st1);
-    ring_wait();
-    while (jc.ok) {
-        step(jc, st0, jn2, st2);
-        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
-        if (!jc.ok) break;
-        step(jc, st1, jn2, st0);
-        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
-        if (!jc.ok) break;
-        step(jc, st2, jn2, st1);
-        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
-    }
-    // The ring's last loads (of job slots past the end) finish before the
-    // wave leaves, so none writes LDS after the workgroup is gone.
-    wait_vm_barrier<0>();
+    q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -445,7 +523,6 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const float* __restrict__ delta, const int* __restrict__ idx, uint16_t* __restrict__ dq) {
     using L = RowTile<D>;
     constexpr int KD = D / 32, ND = D / 16, JK = JobKeys<BS>::JK, NKT = JK / 16, NKS = JK / 32;
-    __shared__ KVStage<D, JK> st0, st1, st2;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
@@ -558,38 +635,7 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
         }
     };
 
-    const bool full_share = ld.full_share();
-    auto ring_wait = [&]() {
-        if constexpr (LD::kEven) {
-            wait_vm_barrier<LD::kPerWave>();
-        } else {
-            if (full_share) wait_vm_barrier<LD::kPerWave>(); else wait_vm_barrier<0>();
-        }
-    };
-    auto step = [&](const Job& cur, const KVStage<D, JK>& sc_, const Job& nx2, KVStage<D, JK>& sn2) {
-        ld.issue(kb, vb, kst2, nx2.j0, s.len, nx2.ok, sn2);
-        compute(cur, sc_);
-        ring_wait();
-    };
-    Job jc = first_job<BS>(ulist, nU);
-    Job jn1 = next_job_q<BS>(jc, ulist, nU, t_last);
-    Job jn2 = next_job_q<BS>(jn1, ulist, nU, t_last);
-    ld.issue(kb, vb, kst2, jc.j0, s.len, jc.ok, st0);
-    ld.issue(kb, vb, kst2, jn1.j0, s.len, jn1.ok, st1);
-    ring_wait();
-    while (jc.ok) {
-        step(jc, st0, jn2, st2);
-        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
-        if (!jc.ok) break;
-        step(jc, st1, jn2, st0);
-        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
-        if (!jc.ok) break;
-        step(jc, st2, jn2, st1);
-        jc = jn1; jn1 = jn2; jn2 = next_job_q<BS>(jn2, ulist, nU, t_last);
-    }
-    // The ring's last loads (of job slots past the end) finish before the
-    // wave leaves, so none writes LDS after the workgroup is gone.
-    wait_vm_barrier<0>();
+    q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
