@@ -3,8 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload cfg2|cfg3|cfg4|cfg1]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-nsa_sel_fwd, then the backward's three stages (Delta + block->query
-inversion + plan, dQ, dK/dV).  Inputs are resident in HBM before timing.
+nsa_sel_fwd, then the backward's stages (Delta + block->query inversion +
+plan, dQ, the dK/dV block kernel, the dK/dV partial reduction).  Inputs are
+resident in HBM before timing.
 The metric is useful TFLOP/s: F_fwd = 4*D*N and F_bwd = 10*D*N with N the
 exact number of (query-head row, key) pairs the block lists select (counted
 here from block_idx), per step, over the wall time of K steps bracketed by
@@ -16,7 +17,6 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import subprocess
@@ -36,7 +36,8 @@ WORKLOADS = {"cfg1": 1, "cfg2": 2, "cfg3": 3, "cfg4": 4}
 # fwd S and PV; dq recomputes S and dP and forms dS K; dkdv recomputes S and
 # dP and forms dV and dK.
 STAGE_FLOPS_PER_PAIR_D = {"fwd": 4, "dq": 6, "dkdv": 8}
-STAGE_KERNEL = {"fwd": "fwd_bf16_kernel", "dq": "dq_bf16_kernel", "dkdv": "dkdv_bf16_kernel"}
+# The one kernel each of these stages launches (bf16 path).
+STAGE_KERNEL = {"fwd": "fwd_q_kernel", "dq": "dq_q_kernel", "dkdv": "dkdv_kernel"}
 
 
 def log(*a):
@@ -76,15 +77,6 @@ def row_groups(w):
         for z in range(w.B):
             for h in range(w.Hkv):
                 yield w.block_idx[z, h], w.T
-
-
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for d in ("block_sparse_attention_nsa_amd/csrc", "include"):
-        for f in sorted(os.listdir(os.path.join(ROOT, d))):
-            if f.endswith((".hip", ".h")):
-                h.update(open(os.path.join(ROOT, d, f), "rb").read())
-    return h.hexdigest()[:16]
 
 
 def git_sha() -> str:
@@ -144,9 +136,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens per (entry, head) of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the timed steps, convert a bf16 tensor of this many MiB to "
+                         "float32 once (a kernel of known traffic for scaling counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -180,7 +175,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
     stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms)
-    names = ("fwd", "prepare", "dq", "dkdv")
+    names = ("fwd", "prepare", "dq", "dkdv", "dkdv_reduce")
 
     def step(evs=None):
         if evs is not None:
@@ -194,14 +189,18 @@ def main():
         stages.dq_stage(dO, lse)
         if evs is not None:
             evs[3].record()
-        stages.dkdv_stage(dO, lse)
+        stages.dkdv_blocks(dO, lse)
         if evs is not None:
             evs[4].record()
+        stages.dkdv_reduce()
+        if evs is not None:
+            evs[5].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -215,12 +214,13 @@ def main():
     stage_ms = {n: v / args.steps for n, v in stage_ms.items()}
     ms_step = wall * 1e3 / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"]
+    bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"] + stage_ms["dkdv_reduce"]
     log(f"[bench] ms/step {ms_step:.3f}; stages (ms): " +
         ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()))
 
     dom = max(("fwd", "dq", "dkdv"), key=lambda n: stage_ms[n])
     achieved = STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N / (stage_ms[dom] * 1e-3) / 1e12
+    from block_sparse_attention_nsa_amd.traffic import source_hash
     src = source_hash()
     kern = STAGE_KERNEL[dom]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -228,6 +228,16 @@ def main():
                 "traffic": stored_traffic(kern, args.workload, src), "kernel": kern,
                 "flops_per_launch": STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N,
                 "launch_ms": round(stage_ms[dom], 4)}
+
+    if args.calibrate_copy_mb:
+        src_t = torch.randn(args.calibrate_copy_mb << 19, device=dev).to(torch.bfloat16)
+        dst_t = torch.empty(src_t.numel(), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {src_t.numel() * 2} bytes read, "
+            f"{dst_t.numel() * 4} bytes written")
+        del src_t, dst_t
 
     cpu = None
     if not args.no_cpu_baseline:

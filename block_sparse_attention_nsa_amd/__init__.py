@@ -179,6 +179,21 @@ class BwdStages:
         _lib.check("nsa_sel_bwd_dkdv", st)
         return self.dk, self.dv
 
+    def dkdv_blocks(self, dO, lse):
+        """First kernel of the dK/dV stage (nsa_sel_bwd_dkdv_blocks)."""
+        st = self.lib.nsa_sel_bwd_dkdv_blocks(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                                              _ptr(dO), _ptr(lse), _ptr(self.cu), _ptr(self.dk),
+                                              _ptr(self.dv), _ptr(self.ws), self.ws.numel(),
+                                              _stream())
+        _lib.check("nsa_sel_bwd_dkdv_blocks", st)
+
+    def dkdv_reduce(self):
+        """Second kernel of the dK/dV stage (nsa_sel_bwd_dkdv_reduce)."""
+        st = self.lib.nsa_sel_bwd_dkdv_reduce(self.p, _ptr(self.cu), _ptr(self.dk), _ptr(self.dv),
+                                              _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_dkdv_reduce", st)
+        return self.dk, self.dv
+
 
 def nsa_sel_delta(o, dO, block_size, block_idx, k, scale=None, cu_seqlens=None, max_seqlen=None):
     """Delta = rowsum(dO * o) (nsa_sel_delta), laid out like lse."""

@@ -19,6 +19,8 @@ EXPORTS = (
     "nsa_sel_bwd_prepare",
     "nsa_sel_bwd_dq",
     "nsa_sel_bwd_dkdv",
+    "nsa_sel_bwd_dkdv_blocks",
+    "nsa_sel_bwd_dkdv_reduce",
     "nsa_sel_delta",
     "nsa_sel_invert",
     "nsa_sel_invert_tokens_capacity",
@@ -78,6 +80,10 @@ def load():
     lib.nsa_sel_bwd_dq.restype = st
     lib.nsa_sel_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, fp, ip, vp, vp, vp, sz, vp]
     lib.nsa_sel_bwd_dkdv.restype = st
+    lib.nsa_sel_bwd_dkdv_blocks.argtypes = [P, vp, vp, vp, vp, fp, ip, vp, vp, vp, sz, vp]
+    lib.nsa_sel_bwd_dkdv_blocks.restype = st
+    lib.nsa_sel_bwd_dkdv_reduce.argtypes = [P, ip, vp, vp, vp, sz, vp]
+    lib.nsa_sel_bwd_dkdv_reduce.restype = st
     lib.nsa_sel_delta.argtypes = [P, vp, vp, ip, fp, vp]
     lib.nsa_sel_delta.restype = st
     lib.nsa_sel_invert.argtypes = [P, ip, ip, ip, ip, vp, sz, vp]

@@ -226,13 +226,16 @@ nsa_status run_dq(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) 
     return NSA_OK;
 }
 
-nsa_status run_dkdv(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
+nsa_status run_dkdv(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st,
+                    int parts = nsa::kDkdvAll) {
     const nsa::BwdWorkspace ws = carve(hp, a.ws);
     if (hp.dtype == NSA_BF16) {
         NSA_HIP(nsa::launch_dkdv_bf16(hp, a.q, a.k, a.v, a.dO, a.lse, ws.delta, ws, (void*)a.dk,
-                                      (void*)a.dv, st),
+                                      (void*)a.dv, st, parts),
                 "dK/dV launch");
     } else {
+        // One vector-ALU kernel does all of it; the reduce part is empty.
+        if (!(parts & nsa::kDkdvBlocks)) return NSA_OK;
         NSA_HIP(nsa::launch_dkdv_f32(hp, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                                      (const float*)a.dO, a.lse, ws.delta, ws, (float*)a.dk,
                                      (float*)a.dv, st),
@@ -410,6 +413,32 @@ nsa_status nsa_sel_bwd_dkdv(const nsa_sel_problem* p, const void* q, const void*
     NSA_TRY(check_bwd(p, a, hp));
     if (sizes_of(hp).q == 0) return NSA_OK;
     return run_dkdv(hp, a, reinterpret_cast<hipStream_t>(stream));
+}
+
+nsa_status nsa_sel_bwd_dkdv_blocks(const nsa_sel_problem* p, const void* q, const void* k,
+                                   const void* v, const void* dO, const float* lse,
+                                   const int32_t* cu_seqlens, void* dk, void* dv, void* workspace,
+                                   size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{q, k, v, kAbsent, dO, kAbsent, dk, dv, lse, (const int32_t*)kAbsent,
+                    cu_seqlens, workspace, workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    return run_dkdv(hp, a, reinterpret_cast<hipStream_t>(stream), nsa::kDkdvBlocks);
+}
+
+nsa_status nsa_sel_bwd_dkdv_reduce(const nsa_sel_problem* p, const int32_t* cu_seqlens, void* dk,
+                                   void* dv, void* workspace, size_t workspace_bytes,
+                                   nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{kAbsent, kAbsent, kAbsent, kAbsent, kAbsent, kAbsent, dk, dv,
+                    (const float*)kAbsent, (const int32_t*)kAbsent, cu_seqlens, workspace,
+                    workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    return run_dkdv(hp, a, reinterpret_cast<hipStream_t>(stream), nsa::kDkdvReduce);
 }
 
 }  // extern "C"

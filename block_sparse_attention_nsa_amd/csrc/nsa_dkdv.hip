@@ -447,10 +447,11 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
 
 hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                             const void* dO, const float* lse, const float* delta,
-                            const BwdWorkspace& ws, void* dk, void* dv, hipStream_t st) {
+                            const BwdWorkspace& ws, void* dk, void* dv, hipStream_t st,
+                            int parts) {
     if (hp.ZH == 0) return hipSuccess;
-    const unsigned items = (unsigned)hp.items_ub;
-    const unsigned nred = (unsigned)((int64_t)hp.ZH * hp.dev.NBmax);
+    const unsigned items = (parts & kDkdvBlocks) ? (unsigned)hp.items_ub : 0u;
+    const unsigned nred = (parts & kDkdvReduce) ? (unsigned)((int64_t)hp.ZH * hp.dev.NBmax) : 0u;
     if (items) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
                           hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 32 * 64), 0,

@@ -51,9 +51,14 @@ hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, 
 hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                           const void* dO, const float* lse, const float* delta,
                           const int* block_idx, void* dq, hipStream_t st);
+// parts: kDkdvBlocks (the per-block kernel: whole lists straight to dk/dv,
+// split lists as fp32 partials), kDkdvReduce (partials summed, unattended
+// blocks zeroed), or both.
+constexpr int kDkdvBlocks = 1, kDkdvReduce = 2, kDkdvAll = 3;
 hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                             const void* dO, const float* lse, const float* delta,
-                            const BwdWorkspace& ws, void* dk, void* dv, hipStream_t st);
+                            const BwdWorkspace& ws, void* dk, void* dv, hipStream_t st,
+                            int parts = kDkdvAll);
 
 hipError_t launch_fwd_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
                           const int* block_idx, float* o, float* lse, hipStream_t st);

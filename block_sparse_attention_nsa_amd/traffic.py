@@ -1,0 +1,107 @@
+"""HBM traffic per launch of one kernel, from rocprofv3 counters.
+
+Two counter runs of bench.py (each with --calibrate-copy-mb M), one with
+FETCH_SIZE and one with WRITE_SIZE, give per-dispatch KiB for every kernel.
+The calibration dispatch converts M MiB of bf16 to float32: it reads exactly
+M MiB and writes 2M MiB, so read and write counts are scaled by
+known / counted of that dispatch.  The result is written as JSON with the
+hash of the kernel sources it was taken on; bench.py reports it as
+roofline.traffic only while that hash still matches.
+
+    rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "(dq_q_kernel|copy)" \\
+        --output-format csv -d <F> -o run -- python bench.py --workload cfg2 \\
+        --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy-mb 512
+    (the same with WRITE_SIZE into <W>)
+    python -m block_sparse_attention_nsa_amd.traffic --kernel dq_q_kernel \\
+        --workload cfg2 --copy-mb 512 --fetch <F>/run_counter_collection.csv \\
+        --write <W>/run_counter_collection.csv --out profiles/dq_q_kernel_cfg2_traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources and the public header."""
+    h = hashlib.sha256()
+    for d in (os.path.join(HERE, "csrc"), os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h")):
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _per_dispatch(path: str, counter: str):
+    """[(dispatch id, kernel name, KiB)] of one counter collection."""
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            key = int(row["Dispatch_Id"])
+            name, val = row["Kernel_Name"], float(row["Counter_Value"])
+            prev = out.get(key)
+            out[key] = (name, val + (prev[1] if prev else 0.0))
+    return [(k, n, v) for k, (n, v) in sorted(out.items())]
+
+
+def _kernel_mean(disp, pattern: str) -> float:
+    vals = [v for _, n, v in disp if re.search(pattern, n)]
+    if not vals:
+        raise SystemExit(f"no dispatch of {pattern!r} in the counter file")
+    return sum(vals) / len(vals)
+
+
+def _copy_value(disp) -> float:
+    """KiB of the calibration conversion: bench.py runs it after every other
+    kernel, so it is the last copy dispatch."""
+    vals = [v for _, n, v in disp if "copy" in n]
+    if not vals:
+        raise SystemExit("no copy kernel dispatch in the counter file")
+    return vals[-1]
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--kernel", required=True, help="regex of the kernel name (e.g. dq_q_kernel)")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--copy-mb", type=int, required=True)
+    ap.add_argument("--fetch", required=True, help="run_counter_collection.csv with FETCH_SIZE")
+    ap.add_argument("--write", required=True, help="run_counter_collection.csv with WRITE_SIZE")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", default="", help="the profiling commands, recorded in the JSON")
+    a = ap.parse_args()
+    fd, wd = _per_dispatch(a.fetch, "FETCH_SIZE"), _per_dispatch(a.write, "WRITE_SIZE")
+    read_known, write_known = a.copy_mb * 2 ** 20, 2 * a.copy_mb * 2 ** 20
+    f_scale = read_known / (_copy_value(fd) * 1024.0)
+    w_scale = write_known / (_copy_value(wd) * 1024.0)
+    fetch = _kernel_mean(fd, a.kernel) * 1024.0 * f_scale
+    write = _kernel_mean(wd, a.kernel) * 1024.0 * w_scale
+    rec = {
+        "kernel": a.kernel,
+        "workload": a.workload,
+        "source_hash": source_hash(),
+        "fetch_bytes_per_launch": round(fetch),
+        "write_bytes_per_launch": round(write),
+        "hbm_bytes_per_launch": round(fetch + write),
+        "copy_calibration": {"mib": a.copy_mb, "fetch_scale": round(f_scale, 4),
+                             "write_scale": round(w_scale, 4)},
+        "command": a.command,
+    }
+    with open(a.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

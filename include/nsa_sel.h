@@ -137,6 +137,21 @@ nsa_status nsa_sel_bwd_dkdv(const nsa_sel_problem* p, const void* q, const void*
                             const int32_t* cu_seqlens, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, nsa_stream_t stream);
 
+/* nsa_sel_bwd_dkdv in its two kernels, same arguments and workspace:
+ * _blocks runs the per-key-block kernel (a list handled by one work item
+ * goes straight to dk/dv, a longer list to fp32 partials in the workspace),
+ * then _reduce sums the partials in a fixed order and writes zeros for
+ * blocks no row attends to.  Calling both in this order equals
+ * nsa_sel_bwd_dkdv (for dtype f32 all work is in _blocks and _reduce does
+ * nothing).  _reduce takes no q/k/v/dO/lse. */
+nsa_status nsa_sel_bwd_dkdv_blocks(const nsa_sel_problem* p, const void* q, const void* k,
+                                   const void* v, const void* dO, const float* lse,
+                                   const int32_t* cu_seqlens, void* dk, void* dv, void* workspace,
+                                   size_t workspace_bytes, nsa_stream_t stream);
+nsa_status nsa_sel_bwd_dkdv_reduce(const nsa_sel_problem* p, const int32_t* cu_seqlens, void* dk,
+                                   void* dv, void* workspace, size_t workspace_bytes,
+                                   nsa_stream_t stream);
+
 /* Delta preprocess alone: delta[row] = sum_d dO[row, d] * o[row, d] (float
  * accumulation), layout of lse.  The backward's first stage (page 3 names it
  * the do_dot step of its kernel chain). */

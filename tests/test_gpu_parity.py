@@ -283,6 +283,27 @@ def test_deterministic_bitwise():
         assert np.array_equal(a[name], b[name]), name
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_staged_backward_equals_one_call(cfg):
+    """prepare, dq, dkdv_blocks, dkdv_reduce in order equal nsa_sel_bwd bit for
+    bit (config 2 has lists long enough to be split into fp32 partials)."""
+    w = workloads.make_config(cfg)
+    d = to_dev(w)
+    cu = d.get("cu")
+    ms = w.max_seqlen if w.packed else None
+    o, lse = nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms)
+    dq, dk, dv = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"], w.block_size,
+                                 w.scale, cu, ms)
+    st = nsa.BwdStages(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms)
+    st.prepare(o, d["dO"])
+    dq2 = st.dq_stage(d["dO"], lse)
+    st.dkdv_blocks(d["dO"], lse)
+    dk2, dv2 = st.dkdv_reduce()
+    torch.cuda.synchronize()
+    for a, b, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
+        assert torch.equal(a, b), n
+
+
 def test_runs_on_caller_stream():
     """All work is queued on the caller's (non-default) stream."""
     w = workloads.make_config(1)
