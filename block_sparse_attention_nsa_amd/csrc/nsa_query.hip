@@ -410,29 +410,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
 
+    // One job: for each tile whose tokens list the block, S^T = K Q^T (all
+    // K operand reads in flight at once), the softmax, then O^T += V^T P^T
+    // with the transposed V reads of each 32-key step issued together.  The
+    // K operands die before the O step, which leaves the registers for that.
     auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
         const uint64_t bm = umask[cur.u];
-        bool any = false;
-#pragma unroll
-        for (int i = 0; i < RT; ++i) any |= (bm & tmask[i]) != 0ull;
-        if (!__builtin_amdgcn_readfirstlane((int)any)) return;
-        bf16x8 ka[NKT][KD];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int kk = 0; kk < KD; ++kk)
-                ka[kt][kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            if ((bm & tmask[i]) == 0ull) continue;
+            if (!__builtin_amdgcn_readfirstlane((int)((bm & tmask[i]) != 0ull))) continue;
             f32x4 sc[NKT];
+            {
+                bf16x8 ka[NKT][KD];
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int kk = 0; kk < KD; ++kk) sc[kt] = mfma(ka[kt][kk], qf[i][kk], sc[kt]);
+                    for (int kk = 0; kk < KD; ++kk)
+                        ka[kt][kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) sc[kt] = mfma(ka[kt][kk], qf[i][kk], sc[kt]);
+                }
             }
             // No mask when every token of the tile lists the block, the slice
             // ends before the tile's first token, and all rows exist.
@@ -467,27 +469,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                 m_run[i] = m_new;
             }
             const float mc = m_run[i] == kNegInfQ ? 0.f : m_run[i] * c2;
-            float pv[NKT][4];
+            float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+            bf16x8 pb[NKS];
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
+            for (int ks_ = 0; ks_ < NKS; ++ks_) {
+                float p0[4], p1[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    pv[kt][e] = fast_exp2(fmaf(sc[kt][e], c2, -mc));
-                    l_run[i] += pv[kt][e];
+                    p0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, -mc));
+                    p1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, -mc));
+                    lsum[e] += p0[e] + p1[e];
                 }
+                pb[ks_] = pack8(p0, p1);
+            }
+            l_run[i] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
             // O^T += V^T P^T, 32 keys per step: keys 32ks + 4g + e and
             // 32ks + 16 + 4g + e are the ones the C layout of S gave this lane.
 #pragma unroll
             for (int ks_ = 0; ks_ < NKS; ++ks_) {
-                const bf16x8 pb = pack8(pv[2 * ks_], pv[2 * ks_ + 1]);
+                bf16x8 vop[ND];
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) {
                     const uint8_t* vb0 = vs + t_off[dt] + 32 * ks_ * L::RB;
                     const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
                     const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    acc[i][dt] = mfma(va, pb, acc[i][dt]);
+                    vop[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
                 }
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(vop[dt], pb[ks_], acc[i][dt]);
             }
         }
     };
@@ -575,28 +584,32 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
 
+    // One job: for each tile whose tokens list the block, S^T = K Q^T and
+    // dP^T = V dO^T (all K and V operand reads in flight at once), dS, then
+    // dQ^T += K^T dS^T with the transposed K reads of each 32-key step issued
+    // together.
     auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
         const uint64_t bm = umask[cur.u];
-        bool any = false;
-#pragma unroll
-        for (int i = 0; i < RT; ++i) any |= (bm & tmask[i]) != 0ull;
-        if (!__builtin_amdgcn_readfirstlane((int)any)) return;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            if ((bm & tmask[i]) == 0ull) continue;
+            if (!__builtin_amdgcn_readfirstlane((int)((bm & tmask[i]) != 0ull))) continue;
             f32x4 sc[NKT], dp[NKT];
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
+                bf16x8 ka[KD], va[KD];
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) {
+                    ka[kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
+                    va[kk] = *reinterpret_cast<const bf16x8*>(vs + a_off[kk] + kt * 16 * L::RB);
+                }
                 sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + a_off[kk] + kt * 16 * L::RB);
-                    sc[kt] = mfma(ka, qf[i][kk], sc[kt]);
-                    dp[kt] = mfma(va, df[i][kk], dp[kt]);
+                    sc[kt] = mfma(ka[kk], qf[i][kk], sc[kt]);
+                    dp[kt] = mfma(va[kk], df[i][kk], dp[kt]);
                 }
             }
             const bool full = ((bm & tmask[i]) == tmask[i]) &&
@@ -611,26 +624,30 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
                     for (int e = 0; e < 4; ++e)
                         if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
             }
-            float ds[NKT][4];
+            bf16x8 dsb[NKS];
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
+            for (int ks_ = 0; ks_ < NKS; ++ks_) {
+                float d0[4], d1[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float P = fast_exp2(fmaf(sc[kt][e], c2, nlse2[i]));
-                    ds[kt][e] = P * (dp[kt][e] - dl[i]);
+                    d0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, nlse2[i])) * (dp[2 * ks_][e] - dl[i]);
+                    d1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, nlse2[i])) * (dp[2 * ks_ + 1][e] - dl[i]);
                 }
+                dsb[ks_] = pack8(d0, d1);
+            }
             // dQ^T += K^T dS^T, 32 keys per step.
 #pragma unroll
             for (int ks_ = 0; ks_ < NKS; ++ks_) {
-                const bf16x8 dsb = pack8(ds[2 * ks_], ds[2 * ks_ + 1]);
+                bf16x8 kop[ND];
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) {
                     const uint8_t* kb0 = ks + t_off[dt] + 32 * ks_ * L::RB;
                     const uint2 k0 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0));
                     const uint2 k1 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0 + 16 * L::RB));
-                    const bf16x8 kta = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
-                    acc[i][dt] = mfma(kta, dsb, acc[i][dt]);
+                    kop[dt] = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
                 }
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(kop[dt], dsb[ks_], acc[i][dt]);
             }
         }
     };
