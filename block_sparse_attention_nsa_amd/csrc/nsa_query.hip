@@ -107,13 +107,28 @@ __device__ __forceinline__ uint64_t tile_tokens(const Problem& p, const QGeo& qg
 struct WgCoord {
     int z, hkv, T0;
 };
+// Dense inputs: the workgroups of one (z, hkv) run on one XCD (consecutive
+// logical indices) and share its K/V in that L2; every (z, hkv) has the same
+// work, so the XCDs stay balanced.  Packed inputs: sequences differ in length,
+// so workgroups are ordered latest token first across all (z, hkv) and dealt
+// round-robin over the XCDs, which balances them (K/V then come from HBM or
+// the memory-side cache more often).  Within either order the heaviest
+// (latest) token windows start first.
 __device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
     WgCoord c;
-    const int zh = L / qg.wg_per_zh;
+    int zh, w;
+    if (p.packed) {
+        const int ZH = p.Z * p.Hkv;
+        zh = (int)blockIdx.x % ZH;
+        w = (int)blockIdx.x / ZH;
+    } else {
+        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        zh = L / qg.wg_per_zh;
+        w = L % qg.wg_per_zh;
+    }
     c.z = zh / p.Hkv;
     c.hkv = zh % p.Hkv;
-    c.T0 = (qg.wg_per_zh - 1 - (L % qg.wg_per_zh)) * qg.TW;  // heaviest (latest) first
+    c.T0 = (qg.wg_per_zh - 1 - w) * qg.TW;
     return c;
 }
 
@@ -671,10 +686,11 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kRT = 2;  // row tiles per wave
-constexpr int kNW = 8;  // waves per workgroup
+// Tiles per wave and waves per workgroup (16 tiles per workgroup).
+constexpr int kRT_F = 2, kNW_F = 8;
+constexpr int kRT_Q = 2, kNW_Q = 8;
 
-QGeo q_geo(const HostProblem& hp) {
+QGeo q_geo(const HostProblem& hp, int kRT, int kNW) {
     const Problem& p = hp.dev;
     QGeo qg;
     const int tiles = kNW * kRT;
@@ -730,12 +746,12 @@ size_t query_dynamic_lds(const HostProblem& hp) {
 
 hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                            const int* block_idx, void* o, float* lse, hipStream_t st) {
-    const QGeo qg = q_geo(hp);
+    const QGeo qg = q_geo(hp, kRT_F, kNW_F);
     const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
     if (grid == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
-                   hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT, kNW>), dim3(grid), dim3(kNW * 64), lds,
+                   hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT_F, kNW_F>), dim3(grid), dim3(kNW_F * 64), lds,
                                       st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
                                       (const uint16_t*)v, block_idx, (uint16_t*)o, lse));
     return hipGetLastError();
@@ -744,12 +760,12 @@ hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, 
 hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                           const void* dO, const float* lse, const float* delta,
                           const int* block_idx, void* dq, hipStream_t st) {
-    const QGeo qg = q_geo(hp);
+    const QGeo qg = q_geo(hp, kRT_Q, kNW_Q);
     const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
     if (grid == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
-                   hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT, kNW>), dim3(grid), dim3(kNW * 64), lds,
+                   hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT_Q, kNW_Q>), dim3(grid), dim3(kNW_Q * 64), lds,
                                       st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
                                       (const uint16_t*)v, (const uint16_t*)dO, lse, delta, block_idx,
                                       (uint16_t*)dq));
