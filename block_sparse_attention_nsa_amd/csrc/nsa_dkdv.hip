@@ -1,8 +1,8 @@
 // nsa_dkdv.hip -- key-major dK / dV for bf16 on gfx950 matrix cores
 // (v_mfma_f32_16x16x32_bf16).
 //
-// One workgroup = one key block u (BS keys: BS/32 waves of 32 keys each) and
-// one chunk of the block's inverted list of query rows (token, head).  The
+// One workgroup = one key block u (BS keys, KPW of them per wave) and one
+// chunk of the block's inverted list of query rows (token, head).  The
 // rows are taken 32 at a time, newest token first, and copied from HBM
 // straight into a three-stage LDS ring by buffer loads that write LDS (no
 // register staging), two steps ahead of their use.  Every wave reads the
@@ -106,8 +106,18 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-template <int D, int BS>
-__global__ __launch_bounds__(BS / 32 * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Keys per wave: 16 keeps a wave within 256 registers (two or more waves per
+// SIMD hide each other's LDS and load latency) at twice the LDS operand reads
+// per matrix op of 32 keys per wave (one wave per SIMD).
+#ifndef NSA_DKDV_KPW
+#define NSA_DKDV_KPW 16
+#endif
+constexpr int kDkdvKpw = NSA_DKDV_KPW;
+static_assert(kDkdvKpw == 16 || kDkdvKpw == 32, "keys per wave");
+
+template <int D, int BS, int KPW>
+__global__ __launch_bounds__(BS / KPW * 64)
+__attribute__((amdgpu_waves_per_eu(KPW == 16 ? 2 : 1, KPW == 16 ? 8 : 1)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                  const float* __restrict__ lse, const float* __restrict__ delta,
@@ -116,7 +126,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  const int* __restrict__ zh_base, int CR, float* __restrict__ partials,
                  uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     using L = RowTile<D>;
-    constexpr int NW = BS / 32, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
+    constexpr int NW = BS / KPW, NT = KPW / 16, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
     constexpr int NJ = (NI + NW - 1) / NW;  // 1 KB row loads per tile for each wave (at most)
     __shared__ Stage<D> st0, st1, st2;
     __shared__ __attribute__((aligned(16))) int tk0[32], tk1[32], tk2[32];
@@ -209,12 +219,12 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         retreat32(cm, G, q32, r32, l_r32, l_G);
     };
 
-    // K and V of this wave's 32 keys as MFMA B operands: kf[kt][kk] holds
+    // K and V of this wave's KPW keys as MFMA B operands: kf[kt][kk] holds
     // K[key 16kt + r][32kk + 8g .. + 7].
-    const int kbase = u * BS + 32 * w;
-    bf16x8 kf[2][KD], vf[2][KD];
+    const int kbase = u * BS + KPW * w;
+    bf16x8 kf[NT][KD], vf[NT][KD];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < NT; ++kt) {
         const int key = kbase + 16 * kt + r;
         const bool in = key < s.len;
         const int64_t ko = k_off(s, hkv, in ? key : 0);
@@ -233,9 +243,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
 
-    f32x4 dkt[2][ND], dvt[2][ND];
+    f32x4 dkt[NT][ND], dvt[NT][ND];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
             dkt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -246,11 +256,11 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     auto compute = [&](const Stage<D>& sg) {
         const uint8_t* tq = reinterpret_cast<const uint8_t*>(sg.q);
         const uint8_t* td = reinterpret_cast<const uint8_t*>(sg.dO);
-        f32x4 sc[2][2], dp[2][2];
+        f32x4 sc[2][NT], dp[2][NT];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < NT; ++kt) {
                 sc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dp[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
@@ -261,14 +271,14 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                 const bf16x8 qa = *reinterpret_cast<const bf16x8*>(tq + a_off[kk] + rt * 16 * L::RB);
                 const bf16x8 da = *reinterpret_cast<const bf16x8*>(td + a_off[kk] + rt * 16 * L::RB);
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
+                for (int kt = 0; kt < NT; ++kt) {
                     sc[rt][kt] = mfma(qa, kf[kt][kk], sc[rt][kt]);
                     dp[rt][kt] = mfma(da, vf[kt][kk], dp[rt][kt]);
                 }
             }
         }
         // P and dS for rows 16rt + 4g + i, keys kbase + 16kt + r.
-        float pv[2][2][4], dsv[2][2][4];
+        float pv[NT][2][4], dsv[NT][2][4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int4 tt = *reinterpret_cast<const int4*>(sg.t + 16 * rt + 4 * g);
@@ -278,7 +288,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
             const float nl[4] = {-ll.x * kLog2e, -ll.y * kLog2e, -ll.z * kLog2e, -ll.w * kLog2e};
             const float de[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < NT; ++kt) {
                 const int key = kbase + 16 * kt + r;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -288,9 +298,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                 }
             }
         }
-        bf16x8 pb[2], dsb[2];
+        bf16x8 pb[NT], dsb[NT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < NT; ++kt) {
             pb[kt] = pack8(pv[kt][0], pv[kt][1]);
             dsb[kt] = pack8(dsv[kt][0], dsv[kt][1]);
         }
@@ -306,7 +316,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
             const uint2 q1 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt] + 16 * L::RB));
             const bf16x8 qcol = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < NT; ++kt) {
                 dvt[kt][dt] = mfma(dcol, pb[kt], dvt[kt][dt]);
                 dkt[kt][dt] = mfma(qcol, dsb[kt], dkt[kt][dt]);
             }
@@ -347,7 +357,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     // Output: dvt[kt][dt][i] = dV[key kbase + 16kt + r][16dt + 4g + i].
     if (it.nitems == 1) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < NT; ++kt) {
             const int key = kbase + 16 * kt + r;
             if (key >= s.len) continue;
             const int64_t ko = k_off(s, hkv, key);
@@ -362,15 +372,16 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
             }
         }
     } else {
-        // Partial slot layout: [dk, dv][wave][kt][dt][lane] x 4 floats.
+        // Partial slot layout: [dk, dv][16-key tile of the block][dt][lane] x
+        // 4 floats; this wave's tiles are NT w + kt.
         const int slot = zh_base[ZH + 1 + it.zh] + pslot_pre[(int64_t)it.zh * (NB + 1) + u] + it.kitem;
         f32x4* pk = reinterpret_cast<f32x4*>(partials + (int64_t)slot * 2 * BS * D);
         f32x4* pv_ = pk + BS * D / 4;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
-                const int e = ((w * 2 + kt) * ND + dt) * 64 + lane;
+                const int e = ((w * NT + kt) * ND + dt) * 64 + lane;
                 pk[e] = dkt[kt][dt];
                 pv_[e] = dvt[kt][dt];
             }
@@ -379,8 +390,8 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 
 // Sums the fp32 partials of split lists in chunk order and writes zeros for
 // blocks no row attends to (blocks handled whole by one item are skipped).
-// Thread e4 owns one float4 of the slot layout [plane][wave][kt][dt][lane],
-// i.e. dK or dV of key 32 wave + 16 kt + (lane & 15), columns 16 dt + 4
+// Thread e4 owns one float4 of the slot layout [plane][tile][dt][lane], i.e.
+// dK or dV of key 16 tile + (lane & 15), columns 16 dt + 4
 // (lane >> 4) .. + 3.  Chunk loads are issued four at a time but added
 // strictly in chunk order.
 template <int D, int BS>
@@ -401,8 +412,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     const float4* part = reinterpret_cast<const float4*>(partials) + (int64_t)slot0 * 2 * E4;
     for (int e4 = threadIdx.x; e4 < 2 * E4; e4 += blockDim.x) {
         const int plane = e4 / E4, x = e4 % E4;
-        const int ln = x % 64, dt = (x / 64) % ND, wkt = x / (64 * ND);
-        const int key = u * BS + 16 * wkt + (ln & 15), d = 16 * dt + 4 * (ln >> 4);
+        const int ln = x % 64, dt = (x / 64) % ND, tile = x / (64 * ND);
+        const int key = u * BS + 16 * tile + (ln & 15), d = 16 * dt + 4 * (ln >> 4);
         if (key >= s.len) continue;
         const float4* src = part + e4;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -454,7 +465,8 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
     const unsigned nred = (parts & kDkdvReduce) ? (unsigned)((int64_t)hp.ZH * hp.dev.NBmax) : 0u;
     if (items) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
-                          hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 32 * 64), 0,
+                          hipLaunchKernelGGL((dkdv_kernel<D, BS, kDkdvKpw>), dim3(items),
+                                             dim3(BS / kDkdvKpw * 64), 0,
                                              st, hp.dev, (const uint16_t*)q, (const uint16_t*)k,
                                              (const uint16_t*)v, (const uint16_t*)dO, lse, delta,
                                              ws.offsets, ws.tokens, ws.item_pre, ws.pslot_pre,
