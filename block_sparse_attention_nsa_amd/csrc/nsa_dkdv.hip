@@ -253,9 +253,32 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         }
     const float c2 = p.scale_log2;
 
+    // One step on a staged tile, in phases the compiler may not interleave
+    // (so every operand read gets a register of its own and is in flight
+    // well before its use): (1) all reads of S / dP operands and of the row
+    // metadata, (2) S and dP, (3) all transposed reads of Q and dO, (4) P and
+    // dS, (5) dV^T and dK^T.
     auto compute = [&](const Stage<D>& sg) {
         const uint8_t* tq = reinterpret_cast<const uint8_t*>(sg.q);
         const uint8_t* td = reinterpret_cast<const uint8_t*>(sg.dO);
+        bf16x8 qa[KD][2], da[KD][2];
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                qa[kk][rt] = *reinterpret_cast<const bf16x8*>(tq + a_off[kk] + rt * 16 * L::RB);
+                da[kk][rt] = *reinterpret_cast<const bf16x8*>(td + a_off[kk] + rt * 16 * L::RB);
+            }
+        int4 tt[2];
+        float4 ll[2], dd[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            tt[rt] = *reinterpret_cast<const int4*>(sg.t + 16 * rt + 4 * g);
+            ll[rt] = *reinterpret_cast<const float4*>(sg.lse + 16 * rt + 4 * g);
+            dd[rt] = *reinterpret_cast<const float4*>(sg.dl + 16 * rt + 4 * g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
         f32x4 sc[2][NT], dp[2][NT];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -265,34 +288,46 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                 dp[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
+        for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(tq + a_off[kk] + rt * 16 * L::RB);
-                const bf16x8 da = *reinterpret_cast<const bf16x8*>(td + a_off[kk] + rt * 16 * L::RB);
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int kt = 0; kt < NT; ++kt) {
-                    sc[rt][kt] = mfma(qa, kf[kt][kk], sc[rt][kt]);
-                    dp[rt][kt] = mfma(da, vf[kt][kk], dp[rt][kt]);
+                    sc[rt][kt] = mfma(qa[kk][rt], kf[kt][kk], sc[rt][kt]);
+                    dp[rt][kt] = mfma(da[kk][rt], vf[kt][kk], dp[rt][kt]);
                 }
-            }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Transposed operands: the contraction rows are 4g + e and 16 + 4g +
+        // e, the rows the C layout of S gave this lane.
+        bf16x8 dcol[ND], qcol[ND];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const uint2 d0 = lds_read_tr(reinterpret_cast<const uint16_t*>(td + t_off[dt]));
+            const uint2 d1 = lds_read_tr(reinterpret_cast<const uint16_t*>(td + t_off[dt] + 16 * L::RB));
+            const uint2 q0 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt]));
+            const uint2 q1 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt] + 16 * L::RB));
+            dcol[dt] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+            qcol[dt] = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
         }
-        // P and dS for rows 16rt + 4g + i, keys kbase + 16kt + r.
+        __builtin_amdgcn_sched_barrier(0);
+
+        // P and dS for rows 16rt + 4g + i, keys kbase + 16kt + r.  The
+        // exponential is taken for every entry and masked by a select.
         float pv[NT][2][4], dsv[NT][2][4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            const int4 tt = *reinterpret_cast<const int4*>(sg.t + 16 * rt + 4 * g);
-            const float4 ll = *reinterpret_cast<const float4*>(sg.lse + 16 * rt + 4 * g);
-            const float4 dd = *reinterpret_cast<const float4*>(sg.dl + 16 * rt + 4 * g);
-            const int tv[4] = {tt.x, tt.y, tt.z, tt.w};
-            const float nl[4] = {-ll.x * kLog2e, -ll.y * kLog2e, -ll.z * kLog2e, -ll.w * kLog2e};
-            const float de[4] = {dd.x, dd.y, dd.z, dd.w};
+            const int tv[4] = {tt[rt].x, tt[rt].y, tt[rt].z, tt[rt].w};
+            const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
+                                 -ll[rt].w * kLog2e};
+            const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
 #pragma unroll
             for (int kt = 0; kt < NT; ++kt) {
                 const int key = kbase + 16 * kt + r;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float P = key <= tv[i] ? fast_exp2(fmaf(sc[rt][kt][i], c2, nl[i])) : 0.f;
+                    const float e = fast_exp2(fmaf(sc[rt][kt][i], c2, nl[i]));
+                    const float P = key <= tv[i] ? e : 0.f;
                     pv[kt][rt][i] = P;
                     dsv[kt][rt][i] = P * (dp[rt][kt][i] - de[i]);
                 }
@@ -304,23 +339,17 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
             pb[kt] = pack8(pv[kt][0], pv[kt][1]);
             dsb[kt] = pack8(dsv[kt][0], dsv[kt][1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+
         // dV^T[d][key] += sum_rows dO[row][d] P[row][key]; dK^T likewise with
-        // Q and dS.  The transposed operand's contraction rows are 4g + e and
-        // 16 + 4g + e, the rows the C layout of S gave this lane.
+        // Q and dS.
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-            const uint2 d0 = lds_read_tr(reinterpret_cast<const uint16_t*>(td + t_off[dt]));
-            const uint2 d1 = lds_read_tr(reinterpret_cast<const uint16_t*>(td + t_off[dt] + 16 * L::RB));
-            const bf16x8 dcol = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
-            const uint2 q0 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt]));
-            const uint2 q1 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt] + 16 * L::RB));
-            const bf16x8 qcol = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int kt = 0; kt < NT; ++kt) {
-                dvt[kt][dt] = mfma(dcol, pb[kt], dvt[kt][dt]);
-                dkt[kt][dt] = mfma(qcol, dsb[kt], dkt[kt][dt]);
+                dvt[kt][dt] = mfma(dcol[dt], pb[kt], dvt[kt][dt]);
+                dkt[kt][dt] = mfma(qcol[dt], dsb[kt], dkt[kt][dt]);
             }
-        }
     };
 
     // Loads a wave issues per step in (B): 2 per row load group (Q, dO), and
