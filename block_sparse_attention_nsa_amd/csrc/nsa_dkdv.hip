@@ -353,11 +353,19 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     };
 
     // Loads a wave issues per step in (B): 2 per row load group (Q, dO), and
-    // lse / Delta on wave 0.  The end-of-step wait lets the newest 2 NJ of
-    // them stay in flight; everything older (the rows of the next step, the
-    // token ids of the step after) is then complete.
+    // lse / Delta on wave 0.  The end-of-step wait lets these newest loads
+    // stay in flight; everything older (the rows of the next step, the token
+    // ids of the step after) is then complete.  A wave without a full share
+    // of row loads waits for all of them.
     constexpr int kInFlight = 2 * NJ;
     const bool full_share = w + NW * (NJ - 1) < NI;
+    auto end_wait = [&](bool ahead) {
+        if (full_share && ahead) {
+            if (w == 0) wait_vm_barrier<kInFlight + 2>(); else wait_vm_barrier<kInFlight>();
+        } else {
+            wait_vm_barrier<0>();
+        }
+    };
 
     // Prologue: token ids of steps 0..2, then the rows of steps 0 and 1.
     tok_dma(tk0);
@@ -366,7 +374,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     wait_vm_barrier<0>();
     row_dma(tk0, st0);
     row_dma(tk1, st1);
-    if (full_share) wait_vm_barrier<kInFlight>(); else wait_vm_barrier<0>();
+    end_wait(true);
 
     // Step i: (A) token ids of step i + 3 into slot (i + 3) % 3 (last read in
     // step i - 2), (B) rows of step i + 2 into stage (i + 2) % 3 (last read in
@@ -375,7 +383,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         if (i + 3 < nsteps) tok_dma(tk_fill);
         if (i + 2 < nsteps) row_dma(tk_next2, nxt2);
         compute(cur);
-        if (full_share && i + 2 < nsteps) wait_vm_barrier<kInFlight>(); else wait_vm_barrier<0>();
+        end_wait(i + 2 < nsteps);
     };
     for (int i = 0; i < nsteps; i += 3) {
         step(i, st0, st2, tk0, tk2);
