@@ -1,15 +1,15 @@
 // nsa_dkdv.hip -- key-major dK / dV for bf16 on gfx950 matrix cores
 // (v_mfma_f32_16x16x32_bf16).
 //
-// One workgroup = one key block u (BS keys, KPW of them per wave) and one
-// chunk of the block's inverted list of query rows (token, head).  The
-// rows are taken 32 at a time, newest token first, and copied from HBM
-// straight into a three-stage LDS ring by buffer loads that write LDS (no
-// register staging), two steps ahead of their use.  Every wave reads the
-// shared tile:
-//     S = Q K^T,  dP = dO V^T              (K, V of the wave's keys in VGPRs)
+// One workgroup = one key block u (BS keys, BS / 16 waves) and one chunk of
+// the block's inverted list of query rows (token, head).  The rows are taken
+// 32 at a time, newest token first, and copied from HBM straight into a
+// four-stage LDS ring by buffer loads that write LDS (no register staging),
+// two steps ahead of their use.  Per step and 32 keys:
+//     S = Q K^T,  dP = dO V^T              (K, V of the keys in VGPRs)
 //     P = exp(S*scale - lse) (causal),  dS = P (dP - Delta)
 //     dV^T += dO^T P,  dK^T += Q^T dS      (accumulated transposed)
+// the first two lines on one wave, the last on another (see dkdv_kernel).
 // A list longer than one chunk writes fp32 partials that dkdv_reduce sums in
 // chunk order, so the result does not depend on scheduling.
 //
@@ -28,14 +28,14 @@ namespace nsa {
 namespace {
 
 // One stage of the row ring: the Q and dO tiles of 32 rows (RowTile layout)
-// and their per-row token, lse and Delta.
-template <int D>
+// and their lse and Delta, one copy per accumulator wave (entries 32.. take
+// the zeros of unused lanes).
+template <int D, int NP>
 struct alignas(16) Stage {
     uint16_t q[32 * D];
     uint16_t dO[32 * D];
-    int t[32];
-    float lse[32];
-    float dl[32];
+    float lse[NP][64];
+    float dl[NP][64];
 };
 
 struct ItemRef {
@@ -106,18 +106,20 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-// Keys per wave: 16 keeps a wave within 256 registers (two or more waves per
-// SIMD hide each other's LDS and load latency) at twice the LDS operand reads
-// per matrix op of 32 keys per wave (one wave per SIMD).
-#ifndef NSA_DKDV_KPW
-#define NSA_DKDV_KPW 16
-#endif
-constexpr int kDkdvKpw = NSA_DKDV_KPW;
-static_assert(kDkdvKpw == 16 || kDkdvKpw == 32, "keys per wave");
-
-template <int D, int BS, int KPW>
-__global__ __launch_bounds__(BS / KPW * 64)
-__attribute__((amdgpu_waves_per_eu(KPW == 16 ? 2 : 1, KPW == 16 ? 8 : 1)))
+// Waves come in pairs; pair a owns keys u BS + 32 a .. + 31 of the block.
+//   S wave (w = a):        S = Q K^T, dP = dO V^T with its keys' K and V in
+//                          VGPRs; P and dS (bf16) go to its pair's LDS slot.
+//   accumulator (w = NP + a): one step behind, dV^T += dO^T P and
+//                          dK^T += Q^T dS from that slot and the staged rows
+//                          (read transposed); it also issues the row loads.
+// Splitting the two halves of the work keeps 32 keys per wave (each staged
+// tile is read by two waves of a pair per operand layout, not by four waves
+// of 16 keys) while neither wave needs more than 256 VGPRs, so two
+// workgroups share a CU and their waves hide each other's latency.
+// The slot is reused every step: the accumulator counts in `freed` when it
+// has read it, and the S wave waits for that count before writing again.
+template <int D, int BS>
+__global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                  const float* __restrict__ lse, const float* __restrict__ delta,
@@ -126,12 +128,19 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  const int* __restrict__ zh_base, int CR, float* __restrict__ partials,
                  uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     using L = RowTile<D>;
-    constexpr int NW = BS / KPW, NT = KPW / 16, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
-    constexpr int NJ = (NI + NW - 1) / NW;  // 1 KB row loads per tile for each wave (at most)
-    __shared__ Stage<D> st0, st1, st2;
-    __shared__ __attribute__((aligned(16))) int tk0[32], tk1[32], tk2[32];
+    constexpr int NP = BS / 32, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
+    constexpr int NJ = (NI + NP - 1) / NP;  // 1 KB row loads per tile for each accumulator (at most)
+    constexpr bool kEven = NP * NJ == NI;   // every accumulator has exactly NJ
+    __shared__ Stage<D, NP> st0, st1, st2, st3;
+    // Token ids of the rows of step x in tkr[a][x % 4], one copy per
+    // accumulator wave a (entries 32.. unused).
+    __shared__ __attribute__((aligned(16))) int tkr[NP][4][64];
+    __shared__ uint4 pbuf[NP][2][2][64];  // [pair][P, dS][key tile][lane]
+    __shared__ int freed[NP];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r = lane & 15;
+    const bool s_wave = w < NP;
+    const int a = s_wave ? w : w - NP;
     const int ZH = p.Z * p.Hkv, NB = p.NBmax, G = p.G;
     const int n_items = zh_base[ZH];
     if ((int)blockIdx.x >= n_items) return;
@@ -144,7 +153,129 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const int R = (off[u + 1] - off[u]) * G;
     const int f_begin = it.kitem * CR, f_end = min(R, f_begin + CR);
     const int nsteps = (f_end - f_begin + 31) / 32;
+    const int kbase = u * BS + 32 * a;
+    if (tid < NP) freed[tid] = 0;
 
+    f32x4 dkt[2][ND], dvt[2][ND];  // accumulators: dK^T / dV^T of keys kbase + 16 kt + r
+
+    if (s_wave) {
+        // K and V of the pair's 32 keys as MFMA B operands: kf[kt][kk] holds
+        // K[key 16kt + r][32kk + 8g .. + 7].
+        bf16x8 kf[2][KD], vf[2][KD];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key = kbase + 16 * kt + r;
+            const bool in = key < s.len;
+            const int64_t ko = k_off(s, hkv, in ? key : 0);
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk) {
+                kf[kt][kk] = in ? as_bf16x8(ldg16(k + ko + 32 * kk + 8 * g)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+                vf[kt][kk] = in ? as_bf16x8(ldg16(v + ko + 32 * kk + 8 * g)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+            }
+        }
+        uint32_t a_off[KD];
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
+        const float c2 = p.scale_log2;
+
+        // One step in phases the compiler may not interleave (every operand
+        // read gets its own register and is in flight before its use): all
+        // reads of the tile and its row metadata, S and dP, then P and dS.
+        auto s_step = [&](int i, const Stage<D, NP>& sg) {
+            if (i < nsteps) {
+                const uint8_t* tq = reinterpret_cast<const uint8_t*>(sg.q);
+                const uint8_t* td = reinterpret_cast<const uint8_t*>(sg.dO);
+                bf16x8 qa[KD][2], da[KD][2];
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) {
+                        qa[kk][rt] = *reinterpret_cast<const bf16x8*>(tq + a_off[kk] + rt * 16 * L::RB);
+                        da[kk][rt] = *reinterpret_cast<const bf16x8*>(td + a_off[kk] + rt * 16 * L::RB);
+                    }
+                int4 tt[2];
+                float4 ll[2], dd[2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    tt[rt] = *reinterpret_cast<const int4*>(&tkr[a][i & 3][16 * rt + 4 * g]);
+                    ll[rt] = *reinterpret_cast<const float4*>(&sg.lse[a][16 * rt + 4 * g]);
+                    dd[rt] = *reinterpret_cast<const float4*>(&sg.dl[a][16 * rt + 4 * g]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+
+                f32x4 sc[2][2], dp[2][2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        sc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        dp[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt) {
+                            sc[rt][kt] = mfma(qa[kk][rt], kf[kt][kk], sc[rt][kt]);
+                            dp[rt][kt] = mfma(da[kk][rt], vf[kt][kk], dp[rt][kt]);
+                        }
+                __builtin_amdgcn_sched_barrier(0);
+
+                // P and dS for rows 16rt + 4g + i, keys kbase + 16kt + r; the
+                // exponential is taken for every entry and masked by a select.
+                // Row x of the step is list row f_end - 32 (i + 1) + x; rows
+                // below the chunk take token -1 (no key passes the mask).
+                const int f0 = f_end - 32 * (i + 1) - f_begin;
+                float pv[2][2][4], dsv[2][2][4];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int x0 = f0 + 16 * rt + 4 * g;
+                    const int tv[4] = {x0 >= 0 ? tt[rt].x : -1, x0 + 1 >= 0 ? tt[rt].y : -1,
+                                       x0 + 2 >= 0 ? tt[rt].z : -1, x0 + 3 >= 0 ? tt[rt].w : -1};
+                    const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
+                                         -ll[rt].w * kLog2e};
+                    const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        const int key = kbase + 16 * kt + r;
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const float e = fast_exp2(fmaf(sc[rt][kt][i4], c2, nl[i4]));
+                            const float P = key <= tv[i4] ? e : 0.f;
+                            pv[kt][rt][i4] = P;
+                            dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
+                        }
+                    }
+                }
+                uint4 pk[2][2];
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    pk[0][kt] = __builtin_bit_cast(uint4, pack8(pv[kt][0], pv[kt][1]));
+                    pk[1][kt] = __builtin_bit_cast(uint4, pack8(dsv[kt][0], dsv[kt][1]));
+                }
+                // The accumulator has read the previous step's P / dS.
+                if (i > 0) spin_ge(&freed[a], i);
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) pbuf[a][x][kt][lane] = pk[x][kt];
+            }
+            wait_vm_barrier<0>();
+        };
+        // The accumulators' prologue has two barriers.
+        wait_vm_barrier<0>();
+        wait_vm_barrier<0>();
+        for (int i = 0; i <= nsteps; i += 4) {
+            s_step(i, st0);
+            if (i + 1 <= nsteps) s_step(i + 1, st1);
+            if (i + 2 <= nsteps) s_step(i + 2, st2);
+            if (i + 3 <= nsteps) s_step(i + 3, st3);
+        }
+        return;
+    }
+
+    // ---- accumulator wave -------------------------------------------------
     // Buffers of this (z, kv group): rows (h, t) of q / dO and lse / Delta.
     // Every valid row lies below the sizes; invalid rows use an offset past
     // them and load zeros.
@@ -164,7 +295,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const uint32_t q_r32 = (uint32_t)r32 * qsh_b, q_G = (uint32_t)G * qsh_b;
     const uint32_t l_r32 = (uint32_t)r32 * lsh_b, l_G = (uint32_t)G * lsh_b;
 
-    // Rows this lane loads: 1 KB load jj = w + NW * j of a tile covers the
+    // Rows this lane loads: 1 KB load jj = a + NP * j of a tile covers the
     // 16-byte positions 64 jj + lane, i.e. row (64 jj + lane) / QCH at some
     // LDS slot, which holds data chunk chunk(row, slot) of that row.
     Cursor cq[NJ];
@@ -172,38 +303,40 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     uint32_t cofs[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const int jj = min(w + NW * j, NI - 1);
+        const int jj = min(a + NP * j, NI - 1);
         const int pos = 64 * jj + lane;
         qrow[j] = pos / QCH;
         cofs[j] = 16u * (uint32_t)L::chunk(qrow[j], pos % QCH);
         cq[j] = cursor_at(f_end - 32 + qrow[j], G, qsh_b);
     }
-    // Wave 0, lanes < 32: row `lane` of each step, once for the token list
-    // (one step ahead of the rows) and once for lse / Delta.
+    // Lanes < 32: row `lane` of each step, once for the token list (one step
+    // ahead of the rows) and once for lse / Delta, into this accumulator's
+    // own copies (lanes 32.. load zeros into unused entries).
     const int mrow = lane & 31;
-    const bool meta = w == 0 && lane < 32;
+    const bool meta = lane < 32;
     Cursor ct = cursor_at(f_end - 32 + mrow, G, 0u);
     Cursor cm = cursor_at(f_end - 32 + mrow, G, lsh_b);
     const buf_rsrc rt = make_rsrc(list, (uint32_t)(4 * (R / G)));
 
-    // (A) token ids of a step into its ring slot: list[e] of every row.
-    auto tok_dma = [&](int* slot_t) {
-        if (meta) dma4(rt, slot_t, ct.f >= f_begin ? 4u * (uint32_t)ct.e : kOob);
+    // (A) token ids of step x into tkr[a][x % 4]: list[e] of every row.
+    auto tok_dma = [&](int x) {
+        dma4(rt, &tkr[a][x & 3][0], meta && ct.f >= f_begin ? 4u * (uint32_t)ct.e : kOob);
         retreat32(ct, G, q32, r32, 0u, 0u);
     };
-    // (B) the rows of a step into stage `sg`, with token ids from `slot_t`
-    // (written by an earlier tok_dma that has completed): Q and dO rows,
-    // then the row token (-1 for rows past the chunk), lse and Delta.
-    auto row_dma = [&](const int* slot_t, Stage<D>& sg) {
+    // (B) the rows of step x into stage `sg` with token ids from
+    // tkr[a][x % 4] (written by an earlier tok_dma that has completed): Q and
+    // dO rows, then lse and Delta.  `pre` runs once the token ids are read.
+    auto row_dma = [&](int x, Stage<D, NP>& sg, auto&& pre) {
+        const int* slot_t = &tkr[a][x & 3][0];
         int tj[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) tj[j] = slot_t[qrow[j]];
         const int tm = slot_t[mrow];
-        if (meta) sg.t[lane] = cm.f >= f_begin ? tm : -1;
+        pre();
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int jj = w + NW * j;
-            if (jj < NI) {
+            const int jj = a + NP * j;
+            if (kEven || jj < NI) {
                 const uint32_t vo = cq[j].f >= f_begin
                                         ? cq[j].hoff + (uint32_t)tj[j] * qst_b + cofs[j] : kOob;
                 dma16(rq, reinterpret_cast<uint8_t*>(sg.q) + 1024 * jj, vo);
@@ -211,214 +344,133 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
             }
             retreat32(cq[j], G, q32, r32, q_r32, q_G);
         }
-        if (meta) {
-            const uint32_t lo = cm.f >= f_begin ? cm.hoff + 4u * (uint32_t)tm : kOob;
-            dma4(rl, sg.lse, lo);
-            dma4(rdl, sg.dl, lo);
+        {
+            const uint32_t lo = meta && cm.f >= f_begin ? cm.hoff + 4u * (uint32_t)tm : kOob;
+            dma4(rl, &sg.lse[a][0], lo);
+            dma4(rdl, &sg.dl[a][0], lo);
         }
         retreat32(cm, G, q32, r32, l_r32, l_G);
     };
 
-    // K and V of this wave's KPW keys as MFMA B operands: kf[kt][kk] holds
-    // K[key 16kt + r][32kk + 8g .. + 7].
-    const int kbase = u * BS + KPW * w;
-    bf16x8 kf[NT][KD], vf[NT][KD];
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt) {
-        const int key = kbase + 16 * kt + r;
-        const bool in = key < s.len;
-        const int64_t ko = k_off(s, hkv, in ? key : 0);
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-            kf[kt][kk] = in ? as_bf16x8(ldg16(k + ko + 32 * kk + 8 * g)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-            vf[kt][kk] = in ? as_bf16x8(ldg16(v + ko + 32 * kk + 8 * g)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-        }
-    }
-
-    // LDS byte offsets inside a tile of this lane's operand reads (rows 16..
-    // of a tile sit 16 RB bytes further).
-    uint32_t a_off[KD], t_off[ND];
-#pragma unroll
-    for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
+    uint32_t t_off[ND];
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
-
-    f32x4 dkt[NT][ND], dvt[NT][ND];
 #pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
             dkt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
             dvt[kt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    const float c2 = p.scale_log2;
 
-    // One step on a staged tile, in phases the compiler may not interleave
-    // (so every operand read gets a register of its own and is in flight
-    // well before its use): (1) all reads of S / dP operands and of the row
-    // metadata, (2) S and dP, (3) all transposed reads of Q and dO, (4) P and
-    // dS, (5) dV^T and dK^T.
-    auto compute = [&](const Stage<D>& sg) {
+    // The products of one step on a staged tile and the pair's P / dS:
+    // dV^T[d][key] += sum_rows dO[row][d] P[row][key]; dK^T likewise with Q
+    // and dS.  The transposed operand's contraction rows are 4g + e and
+    // 16 + 4g + e, the rows the C layout of S gave the S wave's lane.
+    auto acc_step = [&](const Stage<D, NP>& sg) {
+        uint4 pk[2][2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) pk[x][kt] = pbuf[a][x][kt][lane];
+        signal(&freed[a], lane);
         const uint8_t* tq = reinterpret_cast<const uint8_t*>(sg.q);
         const uint8_t* td = reinterpret_cast<const uint8_t*>(sg.dO);
-        bf16x8 qa[KD][2], da[KD][2];
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                qa[kk][rt] = *reinterpret_cast<const bf16x8*>(tq + a_off[kk] + rt * 16 * L::RB);
-                da[kk][rt] = *reinterpret_cast<const bf16x8*>(td + a_off[kk] + rt * 16 * L::RB);
-            }
-        int4 tt[2];
-        float4 ll[2], dd[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            tt[rt] = *reinterpret_cast<const int4*>(sg.t + 16 * rt + 4 * g);
-            ll[rt] = *reinterpret_cast<const float4*>(sg.lse + 16 * rt + 4 * g);
-            dd[rt] = *reinterpret_cast<const float4*>(sg.dl + 16 * rt + 4 * g);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        f32x4 sc[2][NT], dp[2][NT];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int kt = 0; kt < NT; ++kt) {
-                sc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                dp[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int kt = 0; kt < NT; ++kt) {
-                    sc[rt][kt] = mfma(qa[kk][rt], kf[kt][kk], sc[rt][kt]);
-                    dp[rt][kt] = mfma(da[kk][rt], vf[kt][kk], dp[rt][kt]);
-                }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // Transposed operands: the contraction rows are 4g + e and 16 + 4g +
-        // e, the rows the C layout of S gave this lane.
         bf16x8 dcol[ND], qcol[ND];
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
             const uint2 d0 = lds_read_tr(reinterpret_cast<const uint16_t*>(td + t_off[dt]));
             const uint2 d1 = lds_read_tr(reinterpret_cast<const uint16_t*>(td + t_off[dt] + 16 * L::RB));
+            dcol[dt] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // The dO^T operands are all in flight; the Q^T reads go out while the
+        // dV^T products run.
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                dvt[kt][dt] = mfma(dcol[dt], __builtin_bit_cast(bf16x8, pk[0][kt]), dvt[kt][dt]);
             const uint2 q0 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt]));
             const uint2 q1 = lds_read_tr(reinterpret_cast<const uint16_t*>(tq + t_off[dt] + 16 * L::RB));
-            dcol[dt] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
             qcol[dt] = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
         }
         __builtin_amdgcn_sched_barrier(0);
-
-        // P and dS for rows 16rt + 4g + i, keys kbase + 16kt + r.  The
-        // exponential is taken for every entry and masked by a select.
-        float pv[NT][2][4], dsv[NT][2][4];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int tv[4] = {tt[rt].x, tt[rt].y, tt[rt].z, tt[rt].w};
-            const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
-                                 -ll[rt].w * kLog2e};
-            const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
-#pragma unroll
-            for (int kt = 0; kt < NT; ++kt) {
-                const int key = kbase + 16 * kt + r;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float e = fast_exp2(fmaf(sc[rt][kt][i], c2, nl[i]));
-                    const float P = key <= tv[i] ? e : 0.f;
-                    pv[kt][rt][i] = P;
-                    dsv[kt][rt][i] = P * (dp[rt][kt][i] - de[i]);
-                }
-            }
-        }
-        bf16x8 pb[NT], dsb[NT];
-#pragma unroll
-        for (int kt = 0; kt < NT; ++kt) {
-            pb[kt] = pack8(pv[kt][0], pv[kt][1]);
-            dsb[kt] = pack8(dsv[kt][0], dsv[kt][1]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        // dV^T[d][key] += sum_rows dO[row][d] P[row][key]; dK^T likewise with
-        // Q and dS.
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int kt = 0; kt < NT; ++kt) {
-                dvt[kt][dt] = mfma(dcol[dt], pb[kt], dvt[kt][dt]);
-                dkt[kt][dt] = mfma(qcol[dt], dsb[kt], dkt[kt][dt]);
-            }
+            for (int kt = 0; kt < 2; ++kt)
+                dkt[kt][dt] = mfma(qcol[dt], __builtin_bit_cast(bf16x8, pk[1][kt]), dkt[kt][dt]);
     };
 
-    // Loads a wave issues per step in (B): 2 per row load group (Q, dO), and
-    // lse / Delta on wave 0.  The end-of-step wait lets these newest loads
-    // stay in flight; everything older (the rows of the next step, the token
-    // ids of the step after) is then complete.  A wave without a full share
-    // of row loads waits for all of them.
-    constexpr int kInFlight = 2 * NJ;
-    const bool full_share = w + NW * (NJ - 1) < NI;
-    auto end_wait = [&](bool ahead) {
-        if (full_share && ahead) {
-            if (w == 0) wait_vm_barrier<kInFlight + 2>(); else wait_vm_barrier<kInFlight>();
-        } else {
-            wait_vm_barrier<0>();
-        }
+    // Loads an accumulator issues per step: the token ids (A), 2 per row
+    // load group (Q, dO) and lse / Delta (B), every step, also past the end
+    // of the list (they then load zeros into stages and slots nobody reads
+    // any more).  The end-of-step wait lets the newest (B) loads stay in
+    // flight; everything older (the rows of the next step, the token ids of
+    // the step after) is then complete.  An accumulator without a full
+    // share of row loads waits for all of them.
+    constexpr int kInFlight = 2 * NJ + 2;
+    const bool full_share = kEven || a + NP * (NJ - 1) < NI;
+    auto end_wait = [&]() {
+        if (kEven || full_share) wait_vm_barrier<kInFlight>(); else wait_vm_barrier<0>();
     };
 
     // Prologue: token ids of steps 0..2, then the rows of steps 0 and 1.
-    tok_dma(tk0);
-    tok_dma(tk1);
-    tok_dma(tk2);
+    tok_dma(0);
+    tok_dma(1);
+    tok_dma(2);
     wait_vm_barrier<0>();
-    row_dma(tk0, st0);
-    row_dma(tk1, st1);
-    end_wait(true);
+    row_dma(0, st0, [] {});
+    row_dma(1, st1, [] {});
+    end_wait();
 
-    // Step i: (A) token ids of step i + 3 into slot (i + 3) % 3 (last read in
-    // step i - 2), (B) rows of step i + 2 into stage (i + 2) % 3 (last read in
-    // step i - 1), compute stage i % 3, wait, barrier.
-    auto step = [&](int i, const Stage<D>& cur, Stage<D>& nxt2, int* tk_fill, const int* tk_next2) {
-        if (i + 3 < nsteps) tok_dma(tk_fill);
-        if (i + 2 < nsteps) row_dma(tk_next2, nxt2);
-        compute(cur);
-        end_wait(i + 2 < nsteps);
+    // Step i (0 <= i <= nsteps): read the token ids of step i + 2, then
+    // issue (A) those of step i + 3 into slot (i + 3) % 4 (last read in step
+    // i - 1) and (B) the rows of step i + 2 into stage (i + 2) % 4 (last read
+    // by the accumulators in step i - 1); the products of step i - 1 (stage
+    // (i - 1) % 4); wait, barrier.  The S waves work on step i (stage i % 4,
+    // token slot i % 4) meanwhile.
+    auto step = [&](int i, const Stage<D, NP>& prev, Stage<D, NP>& nxt2) {
+        row_dma(i + 2, nxt2, [&] { tok_dma(i + 3); });
+        if (i > 0) acc_step(prev);
+        end_wait();
     };
-    for (int i = 0; i < nsteps; i += 3) {
-        step(i, st0, st2, tk0, tk2);
-        if (i + 1 < nsteps) step(i + 1, st1, st0, tk1, tk0);
-        if (i + 2 < nsteps) step(i + 2, st2, st1, tk2, tk1);
+    for (int i = 0; i <= nsteps; i += 4) {
+        step(i, st3, st2);
+        if (i + 1 <= nsteps) step(i + 1, st0, st3);
+        if (i + 2 <= nsteps) step(i + 2, st1, st0);
+        if (i + 3 <= nsteps) step(i + 3, st2, st1);
     }
 
     // Output: dvt[kt][dt][i] = dV[key kbase + 16kt + r][16dt + 4g + i].
     if (it.nitems == 1) {
 #pragma unroll
-        for (int kt = 0; kt < NT; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
             if (key >= s.len) continue;
             const int64_t ko = k_off(s, hkv, key);
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
-                const f32x4 a = dkt[kt][dt], b = dvt[kt][dt];
+                const f32x4 x = dkt[kt][dt], y = dvt[kt][dt];
                 *reinterpret_cast<uint2*>(dk + ko + 16 * dt + 4 * g) =
-                    make_uint2(pack_bf16x2(a[0] * p.scale, a[1] * p.scale),
-                               pack_bf16x2(a[2] * p.scale, a[3] * p.scale));
+                    make_uint2(pack_bf16x2(x[0] * p.scale, x[1] * p.scale),
+                               pack_bf16x2(x[2] * p.scale, x[3] * p.scale));
                 *reinterpret_cast<uint2*>(dv + ko + 16 * dt + 4 * g) =
-                    make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+                    make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             }
         }
     } else {
         // Partial slot layout: [dk, dv][16-key tile of the block][dt][lane] x
-        // 4 floats; this wave's tiles are NT w + kt.
+        // 4 floats; this pair's tiles are 2 a + kt.
         const int slot = zh_base[ZH + 1 + it.zh] + pslot_pre[(int64_t)it.zh * (NB + 1) + u] + it.kitem;
         f32x4* pk = reinterpret_cast<f32x4*>(partials + (int64_t)slot * 2 * BS * D);
         f32x4* pv_ = pk + BS * D / 4;
 #pragma unroll
-        for (int kt = 0; kt < NT; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
-                const int e = ((w * NT + kt) * ND + dt) * 64 + lane;
+                const int e = ((a * 2 + kt) * ND + dt) * 64 + lane;
                 pk[e] = dkt[kt][dt];
                 pv_[e] = dvt[kt][dt];
             }
@@ -502,8 +554,7 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
     const unsigned nred = (parts & kDkdvReduce) ? (unsigned)((int64_t)hp.ZH * hp.dev.NBmax) : 0u;
     if (items) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
-                          hipLaunchKernelGGL((dkdv_kernel<D, BS, kDkdvKpw>), dim3(items),
-                                             dim3(BS / kDkdvKpw * 64), 0,
+                          hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 16 * 64), 0,
                                              st, hp.dev, (const uint16_t*)q, (const uint16_t*)k,
                                              (const uint16_t*)v, (const uint16_t*)dO, lse, delta,
                                              ws.offsets, ws.tokens, ws.item_pre, ws.pslot_pre,

@@ -262,29 +262,6 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // LDS address of a __shared__ int (for the counter instructions below).
-__device__ __forceinline__ uint32_t lds_addr(const int* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)p;
-}
-
-// Waits until the LDS counter reaches target.  Every wave of the workgroup
-// eventually adds its share (see q_ring), so the wait ends; the iteration cap
-// only bounds it should that ever fail.  The counter is read with a plain
-// ds_read_b32 in asm: to the compiler it is unrelated to the stages that
-// buffer-to-LDS loads are filling, so it adds no vector-memory wait.
-__device__ __forceinline__ void spin_ge(const int* ctr, int target) {
-    const uint32_t a = lds_addr(ctr);
-    for (int it = 0; it < (1 << 18); ++it) {
-        int v;
-        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
-    }
-}
-// One count from this wave (LDS operations of a wave are processed in order,
-// so its earlier LDS reads and writes are done first).
-__device__ __forceinline__ void signal(int* ctr, int lane) {
-    if (lane == 0) asm volatile("ds_add_u32 %0, %1" : : "v"(lds_addr(ctr)), "v"(1) : "memory");
-}
-
 // The workgroup's walk over its jobs with a ring of kQStages K/V stages and
 // no workgroup barrier per job: waves advance at their own pace, at most one
 // job apart (slack kQAhead - 1), synchronised by two counters per stage.
