@@ -529,7 +529,7 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
     int* n_u = reinterpret_cast<int*>(smem + QLds<D, JK>::dynamic_bytes(p.NBmax) - 16);
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), g = lane >> 4, r = lane & 15;
     const WgCoord wc = wg_coord(p, qg);
     const Seq s = seq_of(p, wc.z);
     if (wc.T0 >= s.len) return;
