@@ -421,6 +421,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
 #pragma unroll
                     for (int kk = 0; kk < KD; ++kk)
                         ka[kt][kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
+                // All K reads are issued before the products (each into its
+                // own registers), not one read per product.
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt) {
                     sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -596,6 +599,8 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
                     ka[kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
                     va[kk] = *reinterpret_cast<const bf16x8*>(vs + a_off[kk] + kt * 16 * L::RB);
                 }
+                // The step's K and V reads are all issued before its products.
+                __builtin_amdgcn_sched_barrier(0);
                 sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
