@@ -101,6 +101,9 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
     if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");
     hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
+    if (nsa::invert_lds_bytes(hp) > 163840)
+        return fail(NSA_ERR_UNSUPPORTED, "the block inversion needs %zu bytes of LDS for %lld blocks (max 163840)",
+                    nsa::invert_lds_bytes(hp), (long long)NBmax);
     if (p->dtype == NSA_BF16 && nsa::query_lds_bytes(hp) > 163840)
         return fail(NSA_ERR_UNSUPPORTED, "bf16 forward/dQ need %zu bytes of LDS for %lld blocks (max 163840)",
                     nsa::query_lds_bytes(hp), (long long)NBmax);

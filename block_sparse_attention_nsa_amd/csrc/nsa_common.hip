@@ -7,6 +7,8 @@
 //                 owner without global atomics.  Integer work, bit-exact: counts
 //                 use LDS atomics (order-free), the fill is a stable sequential pass.
 //   * plan:       global prefix of dK/dV work items and fp32 partial slots.
+#include <algorithm>
+
 #include "nsa_internal.h"
 
 namespace nsa {
@@ -131,6 +133,8 @@ __device__ __forceinline__ void stage_rows(const Problem& p, const Seq& s, const
                                            int t0, int t1, int* buf) {
     const int* src = idx_row(p, s, idx, hkv, t0);
     const int n = (t1 - t0) * p.S;
+    // Unrolled so that several loads of each thread are in flight at once.
+#pragma unroll 8
     for (int i = threadIdx.x; i < n; i += blockDim.x) buf[i] = src[i];
 }
 
@@ -203,21 +207,27 @@ __device__ void block_excl_scan(const int* vals, int n, int* out, int* scratch) 
     __syncthreads();
 }
 
-// In-place exclusive prefix sum of a global array by one 256-thread block,
-// 1024 entries per tile (coalesced int4 loads), tiles in order with a
-// running carry.  Returns the total to every thread.  scratch: 257 ints.
-__device__ int block_excl_scan_global(int* a, int64_t n, int* scratch) {
+// In-place exclusive prefix sum of a global array of n ints by one
+// 256-thread block, through LDS: coalesced copy in (entry i at i + i / 64,
+// so the 64-entry segment of each thread starts on its own bank), each
+// thread sums its segment, one scan of the 256 segment sums, each thread
+// rewrites its segment, coalesced copy out.  Returns the total to every
+// thread.  buf: n + n / 64 + 1 ints of LDS; scratch: 257 ints.
+__device__ int block_excl_scan_global(int* a, int n, int* buf, int* scratch) {
     const int tid = threadIdx.x, nt = blockDim.x;  // nt == 256
+#pragma unroll 16
+    for (int i = tid; i < n; i += nt) buf[i + (i >> 6)] = a[i];
+    __syncthreads();
+    const int nseg = (n + 63) >> 6;  // 64-entry segments, 256 per pass
     int carry = 0;
-    for (int64_t base = 0; base < n; base += 4 * nt) {
-        const int64_t i0 = base + 4 * tid;
-        int v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (i0 + e < n) ? a[i0 + e] : 0;
-        const int sum = v[0] + v[1] + v[2] + v[3];
+    for (int s0 = 0; s0 < nseg; s0 += nt) {
+        const int seg = s0 + tid;
+        const int lo = seg * 64, hi = min(lo + 64, n);
+        int* sb = buf + seg * 65;
+        int sum = 0;
+        for (int i = lo; i < hi; ++i) sum += sb[i - lo];
         scratch[tid] = sum;
         __syncthreads();
-        // Hillis-Steele inclusive scan of the 256 thread sums.
         for (int off = 1; off < nt; off <<= 1) {
             const int x = tid >= off ? scratch[tid - off] : 0;
             __syncthreads();
@@ -225,15 +235,17 @@ __device__ int block_excl_scan_global(int* a, int64_t n, int* scratch) {
             __syncthreads();
         }
         int run = carry + scratch[tid] - sum;
-        const int tile_total = scratch[nt - 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (i0 + e < n) a[i0 + e] = run;
-            run += v[e];
+        for (int i = lo; i < hi; ++i) {
+            const int x = sb[i - lo];
+            sb[i - lo] = run;
+            run += x;
         }
-        carry += tile_total;
+        carry += scratch[nt - 1];
         __syncthreads();
     }
+#pragma unroll 16
+    for (int i = tid; i < n; i += nt) a[i] = buf[i + (i >> 6)];
+    __syncthreads();
     return carry;
 }
 
@@ -250,10 +262,11 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     const int NB = p.NBmax;
     int* vals = sm;             // [NB]
     int* scratch = sm + NB;     // [257]
+    int* sbuf = sm + NB + 257;  // [NB C + NB C / 64 + 1]
     const int zh = blockIdx.x;
     int* cp = chunk_pos + (int64_t)zh * NB * C;
     int* off = offsets + (int64_t)zh * (NB + 1);
-    const int total = block_excl_scan_global(cp, (int64_t)NB * C, scratch);
+    const int total = block_excl_scan_global(cp, NB * C, sbuf, scratch);
     for (int u = threadIdx.x; u < NB; u += blockDim.x) vals[u] = cp[(int64_t)u * C];
     __syncthreads();
     for (int u = threadIdx.x; u <= NB; u += blockDim.x) off[u] = u < NB ? vals[u] : total;
@@ -336,6 +349,14 @@ __global__ __launch_bounds__(256) void plan_kernel(int ZH, const int* __restrict
     block_excl_scan(vals, ZH, zh_base + ZH + 1, scratch);
 }
 
+size_t invert_lds_bytes(const HostProblem& hp) {
+    const int64_t NB = hp.dev.NBmax, NBW = (NB + 31) / 32, n_cp = NB * hp.C;
+    const int64_t count = NB + kInvWaves * NBW + kRowStage;
+    const int64_t scan = NB + 257 + n_cp + n_cp / 64 + 1;
+    const int64_t fill = NB + NBW + kRowStage;
+    return sizeof(int) * (size_t)std::max(count, std::max(scan, fill));
+}
+
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st) {
     const Problem& p = hp.dev;
@@ -345,7 +366,8 @@ hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdW
     size_t lds_count = sizeof(int) * (p.NBmax + kInvWaves * NBW + kRowStage);
     hipLaunchKernelGGL(inv_count_kernel, grid, dim3(64 * kInvWaves), lds_count, st, p, hp.CT,
                        hp.C, block_idx, ws.chunk_pos);
-    size_t lds_scan = sizeof(int) * (p.NBmax + 257);
+    const int64_t n_cp = (int64_t)p.NBmax * hp.C;  // <= 2^14 + NBmax by the choice of CT
+    size_t lds_scan = sizeof(int) * (p.NBmax + 257 + n_cp + n_cp / 64 + 1);
     hipLaunchKernelGGL(inv_scan_kernel, dim3(hp.ZH), dim3(256), lds_scan, st, p, hp.C, hp.CR,
                        ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
                        ws.zh_base + 2 * (hp.ZH + 1));

@@ -482,7 +482,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 // Thread e4 owns one float4 of the slot layout [plane][tile][dt][lane], i.e.
 // dK or dV of key 16 tile + (lane & 15), columns 16 dt + 4
 // (lane >> 4) .. + 3.  Chunk loads are issued four at a time but added
-// strictly in chunk order.
+// strictly in chunk order.  kRedSplit workgroups share one block, each a
+// contiguous quarter of its float4s.
+constexpr int kRedSplit = 4;
 template <int D, int BS>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     Problem p, const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
@@ -490,7 +492,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     constexpr int ND = D / 16, E4 = BS * D / 4;  // float4 per plane of one block
     const int NB = p.NBmax, ZH = p.Z * p.Hkv;
-    const int zh = blockIdx.x / NB, u = blockIdx.x % NB;
+    const int bu = blockIdx.x / kRedSplit, sp = blockIdx.x % kRedSplit;
+    const int zh = bu / NB, u = bu % NB;
     const int z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
     if (u * BS >= s.len) return;
@@ -499,7 +502,9 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     if (n == 1) return;
     const int slot0 = n > 1 ? zh_base[ZH + 1 + zh] + pslot_pre[(int64_t)zh * (NB + 1) + u] : 0;
     const float4* part = reinterpret_cast<const float4*>(partials) + (int64_t)slot0 * 2 * E4;
-    for (int e4 = threadIdx.x; e4 < 2 * E4; e4 += blockDim.x) {
+    constexpr int kPer = (2 * E4 + kRedSplit - 1) / kRedSplit;
+    const int e_end = min(2 * E4, (sp + 1) * kPer);
+    for (int e4 = sp * kPer + threadIdx.x; e4 < e_end; e4 += blockDim.x) {
         const int plane = e4 / E4, x = e4 % E4;
         const int ln = x % 64, dt = (x / 64) % ND, tile = x / (64 * ND);
         const int key = u * BS + 16 * tile + (ln & 15), d = 16 * dt + 4 * (ln >> 4);
@@ -551,7 +556,7 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
                             int parts) {
     if (hp.ZH == 0) return hipSuccess;
     const unsigned items = (parts & kDkdvBlocks) ? (unsigned)hp.items_ub : 0u;
-    const unsigned nred = (parts & kDkdvReduce) ? (unsigned)((int64_t)hp.ZH * hp.dev.NBmax) : 0u;
+    const unsigned nred = (parts & kDkdvReduce) ? (unsigned)((int64_t)hp.ZH * hp.dev.NBmax * kRedSplit) : 0u;
     if (items) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
                           hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 16 * 64), 0,

@@ -71,5 +71,7 @@ hipError_t launch_dkdv_f32(const HostProblem& hp, const float* q, const float* k
 
 // Dynamic LDS the bf16 forward / dQ kernels need (0 if unsupported).
 size_t query_lds_bytes(const HostProblem& hp);
+// LDS of the largest inversion kernel (block counts, chunk-table scan, fill).
+size_t invert_lds_bytes(const HostProblem& hp);
 
 }  // namespace nsa
