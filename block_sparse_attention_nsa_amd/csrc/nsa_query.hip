@@ -431,6 +431,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                     for (int kk = 0; kk < KD; ++kk) sc[kt] = mfma(ka[kt][kk], qf[i][kk], sc[kt]);
                 }
             }
+            // The transposed V reads of the first 32 keys go out while the
+            // products run (they do not depend on the softmax).
+            bf16x8 vop0[ND];
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) {
+                const uint8_t* vb0 = vs + t_off[dt];
+                const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
+                const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
+                vop0[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            }
             // No mask when every token of the tile lists the block, the slice
             // ends before the tile's first token, and all rows exist.
             const bool full = ((bm & tmask[i]) == tmask[i]) &&
@@ -485,10 +495,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                 bf16x8 vop[ND];
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) {
-                    const uint8_t* vb0 = vs + t_off[dt] + 32 * ks_ * L::RB;
-                    const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
-                    const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
-                    vop[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    if (ks_ == 0) {
+                        vop[dt] = vop0[dt];
+                    } else {
+                        const uint8_t* vb0 = vs + t_off[dt] + 32 * ks_ * L::RB;
+                        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
+                        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
+                        vop[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+                    }
                 }
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(vop[dt], pb[ks_], acc[i][dt]);
