@@ -13,10 +13,13 @@
 // A list longer than one chunk writes fp32 partials that dkdv_reduce sums in
 // chunk order, so the result does not depend on scheduling.
 //
-// Scheduling: work items are dealt out so that consecutive items (the blocks
-// of one (batch, kv-head) group) run on one XCD; as all of them walk their
-// row lists from the newest token down, the groups that share rows read them
-// at about the same time and mostly from that XCD's L2.
+// Scheduling: with a multiple of 8 (batch, kv-head) groups of equal length,
+// work items are dealt out so that consecutive items (the blocks of one
+// group) run on one XCD; as all of them walk their row lists from the newest
+// token down, the blocks that share rows read them at about the same time
+// and mostly from that XCD's L2.  Otherwise (packed sequences, or fewer
+// groups than XCDs, where contiguous ranges would give some XCDs all the
+// long early-block lists) items are dealt round-robin over the XCDs.
 //
 // Method: page 1 of the reference text (NSA selection gradcheck gate) defines
 // the call and its gradients; the backward formulas are the exact gradient of
@@ -145,7 +148,8 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const int n_items = zh_base[ZH];
     if ((int)blockIdx.x >= n_items) return;
     ItemRef it;
-    find_item(xcd_remap(blockIdx.x, n_items), ZH, NB, zh_base, item_pre, it);
+    const int li = (!p.packed && ZH % 8 == 0) ? xcd_remap(blockIdx.x, n_items) : (int)blockIdx.x;
+    find_item(li, ZH, NB, zh_base, item_pre, it);
     const int z = it.zh / p.Hkv, hkv = it.zh % p.Hkv, u = it.u;
     const Seq s = seq_of(p, z);
     const int* off = offsets + (int64_t)it.zh * (NB + 1);

@@ -107,18 +107,21 @@ __device__ __forceinline__ uint64_t tile_tokens(const Problem& p, const QGeo& qg
 struct WgCoord {
     int z, hkv, T0;
 };
-// Dense inputs: the workgroups of one (z, hkv) run on one XCD (consecutive
-// logical indices) and share its K/V in that L2; every (z, hkv) has the same
-// work, so the XCDs stay balanced.  Packed inputs: sequences differ in length,
-// so workgroups are ordered latest token first across all (z, hkv) and dealt
-// round-robin over the XCDs, which balances them (K/V then come from HBM or
-// the memory-side cache more often).  Within either order the heaviest
-// (latest) token windows start first.
+// With a multiple of 8 (z, hkv) groups of equal length (dense inputs) the
+// workgroups of one group run on one XCD (consecutive logical indices) and
+// share its K/V in that L2, and every XCD gets the same work.  Otherwise
+// (packed inputs, whose sequences differ in length, or fewer groups than
+// XCDs, where one group's token windows would be cut across XCDs by
+// position and the XCDs holding the latest tokens would get most of the
+// work) workgroups are ordered latest token first across all groups and
+// dealt round-robin over the XCDs, which balances them (K/V then come from
+// HBM or the memory-side cache more often).  Within either order the
+// heaviest (latest) token windows start first.
 __device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
     WgCoord c;
     int zh, w;
-    if (p.packed) {
-        const int ZH = p.Z * p.Hkv;
+    const int ZH = p.Z * p.Hkv;
+    if (p.packed || ZH % 8 != 0) {
         zh = (int)blockIdx.x % ZH;
         w = (int)blockIdx.x / ZH;
     } else {
