@@ -107,21 +107,68 @@ __device__ __forceinline__ uint64_t tile_tokens(const Problem& p, const QGeo& qg
 struct WgCoord {
     int z, hkv, T0;
 };
+// Packed inputs with at most 64 sequences: workgroup b takes kv head
+// b % Hkv and the (b / Hkv)-th non-empty (window level, sequence) pair,
+// levels from the latest window down (level lw holds token windows starting
+// at (L - 1 - lw) TW), sequences in index order within a level; workgroups
+// past the last pair are empty and come last.  (Empty workgroups spread
+// through the launch order, one per window past a short sequence's end, were
+// measured to hold back the dispatch of the real ones: config 4 forward
+// 0.618 -> 0.460 ms.)  Each wave computes this alone: lane z holds sequence
+// z's first level s_z = L - ceil(len_z / TW), so P(lw) = sum_z max(0, lw -
+// s_z) pairs precede level lw and #{z : s_z <= lw} lie on it; 64 candidate
+// levels are tested per pass, one per lane.  Returns false when b is past
+// the last pair.
+__device__ bool packed_pair(const Problem& p, const QGeo& qg, int& zh, int& w) {
+    const int lane = threadIdx.x & 63, L = qg.wg_per_zh;
+    int s_z = L;
+    if (lane < p.Z) {
+        const int len = min(max(p.cu[lane + 1] - p.cu[lane], 0), p.Tmax);
+        s_z = L - (len + qg.TW - 1) / qg.TW;
+    }
+    const int hkv = (int)blockIdx.x % p.Hkv, n = (int)blockIdx.x / p.Hkv;
+    for (int c = 0; c < L; c += 64) {
+        const int lw = c + lane;
+        int before = 0, on = 0;
+        for (int z = 0; z < p.Z; ++z) {
+            const int sz = __builtin_amdgcn_readlane(s_z, z);
+            before += max(0, lw - sz);
+            on += sz <= lw ? 1 : 0;
+        }
+        const uint64_t hit = __ballot(lw < L && before <= n && n < before + on);
+        if (hit) {
+            const int src = __builtin_ctzll(hit), lev = c + src;
+            const int r = n - __builtin_amdgcn_readlane(before, src);
+            const uint64_t live = __ballot(lane < p.Z && s_z <= lev);
+            const int rank = __popcll(live & ((1ull << lane) - 1ull));
+            const uint64_t pick = __ballot(((live >> lane) & 1ull) && rank == r);
+            zh = __builtin_ctzll(pick) * p.Hkv + hkv;
+            w = lev;
+            return true;
+        }
+    }
+    return false;
+}
+
 // With a multiple of 8 (z, hkv) groups of equal length (dense inputs) the
 // workgroups of one group run on one XCD (consecutive logical indices) and
-// share its K/V in that L2, and every XCD gets the same work.  Otherwise
-// (packed inputs, whose sequences differ in length, or fewer groups than
-// XCDs, where one group's token windows would be cut across XCDs by
+// share its K/V in that L2, and every XCD gets the same work.  With fewer
+// groups than XCDs, one group's token windows would be cut across XCDs by
 // position and the XCDs holding the latest tokens would get most of the
-// work) workgroups are ordered latest token first across all groups and
-// dealt round-robin over the XCDs, which balances them (K/V then come from
-// HBM or the memory-side cache more often).  Within either order the
-// heaviest (latest) token windows start first.
+// work; then, and for packed inputs, workgroups are dealt round-robin over
+// the XCDs, latest token first (packed: as above, or, with more than 64
+// sequences, every (window, group) in turn, empty ones included).  K/V then
+// come from HBM or the memory-side cache more often.
 __device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
     WgCoord c;
     int zh, w;
     const int ZH = p.Z * p.Hkv;
-    if (p.packed || ZH % 8 != 0) {
+    if (p.packed && p.Z <= 64) {
+        if (!packed_pair(p, qg, zh, w)) {
+            zh = 0;
+            w = -1;  // past the last pair: T0 lies past every sequence
+        }
+    } else if (p.packed || ZH % 8 != 0) {
         zh = (int)blockIdx.x % ZH;
         w = (int)blockIdx.x / ZH;
     } else {
