@@ -148,7 +148,16 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const int n_items = zh_base[ZH];
     if ((int)blockIdx.x >= n_items) return;
     ItemRef it;
-    const int li = (!p.packed && ZH % 8 == 0) ? xcd_remap(blockIdx.x, n_items) : (int)blockIdx.x;
+    int li = (!p.packed && ZH % 8 == 0) ? xcd_remap(blockIdx.x, n_items) : (int)blockIdx.x;
+    if (!p.packed && ZH % 8 == 0 && n_items == ZH * NB) {
+        // One item per block (every list fits one chunk): the XCD's ZH / 8
+        // groups are interleaved block-major, so its launch order runs from
+        // the longest lists to the shortest once, not once per group.  (A
+        // bijection on the items either way.)
+        const int gx = ZH / 8, per = n_items / 8;
+        const int x = li / per, k = li % per;
+        li = (x * gx + k % gx) * NB + k / gx;
+    }
     find_item(li, ZH, NB, zh_base, item_pre, it);
     const int z = it.zh / p.Hkv, hkv = it.zh % p.Hkv, u = it.u;
     const Seq s = seq_of(p, z);
