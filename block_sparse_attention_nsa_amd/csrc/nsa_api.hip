@@ -96,7 +96,9 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.rows = (int64_t)p->B * p->Hq * p->T;
     hp.cap = Smin * idx_rows;
     const int64_t rows_ub = hp.cap * G;
-    int64_t cr = (rows_ub / 1024 + 31) / 32 * 32;
+    // Rows per dK/dV work item: about 1/2048 of the row bound (several items
+    // per workgroup slot, so the last round is short), within [1024, 16384].
+    int64_t cr = (rows_ub / 2048 + 31) / 32 * 32;
     hp.CR = (int)std::min<int64_t>(16384, std::max<int64_t>(1024, cr));
     hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
     if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");

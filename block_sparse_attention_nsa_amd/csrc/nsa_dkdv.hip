@@ -24,6 +24,8 @@
 // Method: page 1 of the reference text (NSA selection gradcheck gate) defines
 // the call and its gradients; the backward formulas are the exact gradient of
 // the masked softmax attention, as stated in include/nsa_sel.h.
+#include <algorithm>
+
 #include "nsa_internal.h"
 
 namespace nsa {
@@ -494,18 +496,21 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 // blocks no row attends to (blocks handled whole by one item are skipped).
 // Thread e4 owns one float4 of the slot layout [plane][tile][dt][lane], i.e.
 // dK or dV of key 16 tile + (lane & 15), columns 16 dt + 4
-// (lane >> 4) .. + 3.  Chunk loads are issued four at a time but added
-// strictly in chunk order.  kRedSplit workgroups share one block, each a
-// contiguous quarter of its float4s.
-constexpr int kRedSplit = 4;
+// (lane >> 4) .. + 3.  Chunk loads are issued eight at a time but added
+// strictly in chunk order.  rs workgroups share one block, each a contiguous
+// share of its float4s (the launch picks rs so that there are about 4096
+// workgroups, at least enough for 4 float4s per thread: with few blocks, up
+// to 16 per block, so a block listed by many rows does not hold back the
+// others; with many, fewer, since most blocks need no reduction and their
+// workgroups only exit).
 template <int D, int BS>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     Problem p, const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
-    const int* __restrict__ zh_base, const float* __restrict__ partials,
+    const int* __restrict__ zh_base, const float* __restrict__ partials, int rs,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     constexpr int ND = D / 16, E4 = BS * D / 4;  // float4 per plane of one block
     const int NB = p.NBmax, ZH = p.Z * p.Hkv;
-    const int bu = blockIdx.x / kRedSplit, sp = blockIdx.x % kRedSplit;
+    const int bu = blockIdx.x / rs, sp = blockIdx.x % rs;
     const int zh = bu / NB, u = bu % NB;
     const int z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
@@ -515,33 +520,50 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     if (n == 1) return;
     const int slot0 = n > 1 ? zh_base[ZH + 1 + zh] + pslot_pre[(int64_t)zh * (NB + 1) + u] : 0;
     const float4* part = reinterpret_cast<const float4*>(partials) + (int64_t)slot0 * 2 * E4;
-    constexpr int kPer = (2 * E4 + kRedSplit - 1) / kRedSplit;
-    const int e_end = min(2 * E4, (sp + 1) * kPer);
-    for (int e4 = sp * kPer + threadIdx.x; e4 < e_end; e4 += blockDim.x) {
-        const int plane = e4 / E4, x = e4 % E4;
-        const int ln = x % 64, dt = (x / 64) % ND, tile = x / (64 * ND);
-        const int key = u * BS + 16 * tile + (ln & 15), d = 16 * dt + 4 * (ln >> 4);
-        if (key >= s.len) continue;
-        const float4* src = part + e4;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int kk = 0;
-        for (; kk + 4 <= n; kk += 4) {
-            const float4 x0 = src[(int64_t)(kk + 0) * 2 * E4];
-            const float4 x1 = src[(int64_t)(kk + 1) * 2 * E4];
-            const float4 x2 = src[(int64_t)(kk + 2) * 2 * E4];
-            const float4 x3 = src[(int64_t)(kk + 3) * 2 * E4];
-            acc.x += x0.x; acc.y += x0.y; acc.z += x0.z; acc.w += x0.w;
-            acc.x += x1.x; acc.y += x1.y; acc.z += x1.z; acc.w += x1.w;
-            acc.x += x2.x; acc.y += x2.y; acc.z += x2.z; acc.w += x2.w;
-            acc.x += x3.x; acc.y += x3.y; acc.z += x3.z; acc.w += x3.w;
+    // This workgroup's float4s: e0 + threadIdx.x + 256 q for q < kP (rs is
+    // at least 2 E4 / (256 kP)); each thread loads its kP of them for four
+    // chunks at a time and adds them in chunk order.
+    constexpr int kP = 4;
+    const int per = (2 * E4 + rs - 1) / rs;
+    const int e0 = sp * per, e_end = min(2 * E4, e0 + per);
+    int pos[kP], key[kP];
+    bool on[kP];
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+        pos[q] = e0 + (int)threadIdx.x + 256 * q;
+        const int x = pos[q] % E4;
+        const int ln = x % 64, tile = x / (64 * ND);
+        key[q] = u * BS + 16 * tile + (ln & 15);
+        on[q] = pos[q] < e_end && key[q] < s.len;
+    }
+    float4 acc[kP];
+#pragma unroll
+    for (int q = 0; q < kP; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int kk = 0; kk < n; kk += 4) {
+        float4 x[kP][4];
+#pragma unroll
+        for (int q = 0; q < kP; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                x[q][j] = on[q] && kk + j < n ? part[pos[q] + (int64_t)(kk + j) * 2 * E4]
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (kk + j >= n) break;
+#pragma unroll
+            for (int q = 0; q < kP; ++q) {
+                acc[q].x += x[q][j].x; acc[q].y += x[q][j].y; acc[q].z += x[q][j].z; acc[q].w += x[q][j].w;
+            }
         }
-        for (; kk < n; ++kk) {
-            const float4 y = src[(int64_t)kk * 2 * E4];
-            acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
-        }
+    }
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+        if (!on[q]) continue;
+        const int plane = pos[q] / E4, x = pos[q] % E4;
+        const int dt = (x / 64) % ND, d = 16 * dt + 4 * ((x % 64) >> 4);
         const float m = plane == 0 ? p.scale : 1.f;
-        const uint2 pk = make_uint2(pack_bf16x2(acc.x * m, acc.y * m), pack_bf16x2(acc.z * m, acc.w * m));
-        uint16_t* dst = (plane == 0 ? dk : dv) + k_off(s, hkv, key) + d;
+        const uint2 pk = make_uint2(pack_bf16x2(acc[q].x * m, acc[q].y * m), pack_bf16x2(acc[q].z * m, acc[q].w * m));
+        uint16_t* dst = (plane == 0 ? dk : dv) + k_off(s, hkv, key[q]) + d;
         *reinterpret_cast<uint2*>(dst) = pk;
     }
 }
@@ -569,7 +591,10 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
                             int parts) {
     if (hp.ZH == 0) return hipSuccess;
     const unsigned items = (parts & kDkdvBlocks) ? (unsigned)hp.items_ub : 0u;
-    const unsigned nred = (parts & kDkdvReduce) ? (unsigned)((int64_t)hp.ZH * hp.dev.NBmax * kRedSplit) : 0u;
+    const int64_t n_blocks = (int64_t)hp.ZH * hp.dev.NBmax;
+    const int64_t rs_min = ((int64_t)hp.dev.bs * hp.dev.D / 2 + 1023) / 1024;  // 2 E4 / (256 * 4)
+    const int rs = (int)std::max<int64_t>(rs_min, std::min<int64_t>(16, 4096 / std::max<int64_t>(1, n_blocks)));
+    const unsigned nred = (parts & kDkdvReduce) ? (unsigned)(n_blocks * rs) : 0u;
     if (items) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
                           hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 16 * 64), 0,
@@ -583,7 +608,7 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
                           hipLaunchKernelGGL((dkdv_reduce_kernel<D, BS>), dim3(nred), dim3(256), 0,
                                              st, hp.dev, ws.item_pre, ws.pslot_pre, ws.zh_base,
-                                             ws.partials, (uint16_t*)dk, (uint16_t*)dv));
+                                             ws.partials, rs, (uint16_t*)dk, (uint16_t*)dv));
     }
     return hipGetLastError();
 }
