@@ -390,12 +390,69 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
     wait_vm<0>();
 }
 
+// The same walk with a workgroup barrier after every job, for selections
+// that cover whole causal prefixes (every tile busy on every job, so the
+// counters above only add waiting): job j is computed from stage j % 4 while
+// the loads of job j + 3 go to stage (j + 3) % 4, last read by job j - 1
+// (freed by the barrier that ended it); the end-of-job wait leaves the
+// loads of jobs j + 2 and j + 3 in flight.
+template <int D, int BS, int NW, class Compute>
+__device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const uint16_t* kb,
+                                            const uint16_t* vb, int kst2, int len,
+                                            const uint16_t* ulist, int nU, int t_last,
+                                            Compute&& compute) {
+    constexpr int JK = JobKeys<BS>::JK;
+    using LD = KVLoad<D, NW, JK>;
+    static_assert(kQStages == 4, "the unrolled walk below is written for 4 stages");
+    __shared__ KVStage<D, JK> s0, s1, s2, s3;
+    const bool full = ld.full_share();
+    auto ring_wait = [&]() {
+        if constexpr (LD::kEven) {
+            wait_vm_barrier<2 * LD::kPerWave>();
+        } else {
+            if (full) wait_vm_barrier<2 * LD::kPerWave>(); else wait_vm_barrier<0>();
+        }
+    };
+    Job jc = first_job<BS>(ulist, nU);
+    Job j1 = next_job_q<BS>(jc, ulist, nU, t_last);
+    Job j2 = next_job_q<BS>(j1, ulist, nU, t_last);
+    Job j3 = next_job_q<BS>(j2, ulist, nU, t_last);
+    ld.issue(kb, vb, kst2, jc.j0, len, jc.ok, s0);
+    ld.issue(kb, vb, kst2, j1.j0, len, j1.ok, s1);
+    ld.issue(kb, vb, kst2, j2.j0, len, j2.ok, s2);
+    if constexpr (LD::kEven) {
+        wait_vm_barrier<2 * LD::kPerWave>();
+    } else {
+        if (full) wait_vm_barrier<2 * LD::kPerWave>(); else wait_vm_barrier<0>();
+    }
+    auto step = [&](const KVStage<D, JK>& cs, KVStage<D, JK>& is) {
+        ld.issue(kb, vb, kst2, j3.j0, len, j3.ok, is);
+        compute(jc, cs);
+        ring_wait();
+        jc = j1;
+        j1 = j2;
+        j2 = j3;
+        j3 = next_job_q<BS>(j3, ulist, nU, t_last);
+    };
+    while (jc.ok) {
+        step(s0, s3);
+        if (!jc.ok) break;
+        step(s1, s0);
+        if (!jc.ok) break;
+        step(s2, s1);
+        if (!jc.ok) break;
+        step(s3, s2);
+    }
+    // Loads of job slots past the end finish before the wave leaves.
+    wait_vm_barrier<0>();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int D, int BS, int RT, int NW>
+template <int D, int BS, int RT, int NW, bool SYNC>
 __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                                                         const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
@@ -560,7 +617,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         }
     };
 
-    q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
+    if constexpr (SYNC) {
+        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, compute);
+    } else {
+        q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
+    }
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -584,7 +645,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, int BS, int RT, int NW>
+template <int D, int BS, int RT, int NW, bool SYNC>
 __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     Problem p, QGeo qg, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
@@ -713,7 +774,11 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
         }
     };
 
-    q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
+    if constexpr (SYNC) {
+        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, compute);
+    } else {
+        q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
+    }
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
@@ -790,6 +855,13 @@ size_t query_dynamic_lds(const HostProblem& hp) {
         else return hipErrorInvalidValue;                                                  \
     } while (0)
 
+// The barrier-per-job walk when the selection can cover a token's whole
+// causal prefix (S block_size >= max length): then every tile works on
+// nearly every job.
+static bool q_sync(const HostProblem& hp) {
+    return (int64_t)hp.dev.S * hp.dev.bs >= (int64_t)hp.dev.Tmax;
+}
+
 hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                            const int* block_idx, void* o, float* lse, hipStream_t st) {
     const QGeo qg = q_geo(hp, kRT_F, kNW_F);
@@ -797,9 +869,15 @@ hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, 
     if (grid == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
-                   hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT_F, kNW_F>), dim3(grid), dim3(kNW_F * 64), lds,
-                                      st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
-                                      (const uint16_t*)v, block_idx, (uint16_t*)o, lse));
+                   if (q_sync(hp)) {
+                       hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT_F, kNW_F, true>), dim3(grid), dim3(kNW_F * 64),
+                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)v, block_idx, (uint16_t*)o, lse);
+                   } else {
+                       hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT_F, kNW_F, false>), dim3(grid), dim3(kNW_F * 64),
+                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)v, block_idx, (uint16_t*)o, lse);
+                   });
     return hipGetLastError();
 }
 
@@ -811,10 +889,17 @@ hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, c
     if (grid == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
-                   hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT_Q, kNW_Q>), dim3(grid), dim3(kNW_Q * 64), lds,
-                                      st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
-                                      (const uint16_t*)v, (const uint16_t*)dO, lse, delta, block_idx,
-                                      (uint16_t*)dq));
+                   if (q_sync(hp)) {
+                       hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT_Q, kNW_Q, true>), dim3(grid), dim3(kNW_Q * 64),
+                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)v, (const uint16_t*)dO, lse, delta, block_idx,
+                                          (uint16_t*)dq);
+                   } else {
+                       hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT_Q, kNW_Q, false>), dim3(grid), dim3(kNW_Q * 64),
+                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)v, (const uint16_t*)dO, lse, delta, block_idx,
+                                          (uint16_t*)dq);
+                   });
     return hipGetLastError();
 }
 
