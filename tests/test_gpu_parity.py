@@ -101,6 +101,38 @@ def test_packed_different_totals_same_count():
         _full_parity(w)
 
 
+
+def test_bf16_packed_many_and_empty_sequences():
+    """Packed bf16 with empty sequences among short ones, both with at most 64
+    sequences (the order of non-empty windows is computed per wave from the
+    lengths) and with more (every window of every sequence in turn)."""
+    rng = np.random.default_rng(12)
+    for n_seq in (12, 70):
+        lens = [int(x) for x in rng.integers(0, 97, size=n_seq)]
+        lens[0] = 0
+        lens[n_seq // 2] = 0
+        lens[-1] = 160
+        w = workloads.make_thd(lens, 4, 2, 64, 4, 32, "bf16", "own_first_random", seed=13,
+                               name=f"thd-{n_seq}-seqs")
+        _full_parity(w)
+
+
+@pytest.mark.parametrize("case", [
+    dict(name="prefix-G4-D128-bs64", B=1, Hq=8, Hkv=2, T=300, D=128, S=5, bs=64),
+    dict(name="prefix-G2-D64-bs128", B=2, Hq=4, Hkv=2, T=250, D=64, S=2, bs=128),
+])
+def test_bf16_whole_prefix_selection(case):
+    """Selections that can cover a token's whole causal prefix (S * block_size
+    >= T: forward and dQ take the walk with a barrier per job), with irregular
+    lists."""
+    rng = np.random.default_rng(14)
+    c = dict(case)
+    name = c.pop("name")
+    idx = _weird_block_idx(rng, c["B"], c["Hkv"], c["T"], c["bs"], c["S"])
+    w = workloads.make_dense(c["B"], c["Hq"], c["Hkv"], c["T"], c["D"], c["S"], c["bs"], "bf16",
+                             seed=15, name=name, block_idx=idx)
+    _full_parity(w)
+
 # ---- full-size configurations: sampled outputs + invariants ---------------
 
 def _sampled_parity(w, out, rng, n_rows=48, blocks=None):
