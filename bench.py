@@ -221,8 +221,8 @@ def main():
     dom = max(("fwd", "dq", "dkdv"), key=lambda n: stage_ms[n])
     achieved = STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N / (stage_ms[dom] * 1e-3) / 1e12
     from block_sparse_attention_nsa_amd.traffic import source_hash
-    src = source_hash()
     kern = STAGE_KERNEL[dom]
+    src = source_hash(kern)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(kern, args.workload, src), "kernel": kern,

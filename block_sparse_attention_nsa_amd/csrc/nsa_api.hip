@@ -213,8 +213,7 @@ nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProble
 
 nsa_status run_prepare(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
     const nsa::BwdWorkspace ws = carve(hp, a.ws);
-    NSA_HIP(nsa::launch_delta(hp, a.o, a.dO, ws.delta, st), "delta launch");
-    NSA_HIP(nsa::launch_invert(hp, a.idx, ws, st), "inversion launch");
+    NSA_HIP(nsa::launch_prepare(hp, a.o, a.dO, a.idx, ws, st), "Delta / inversion launch");
     if (hp.dtype == NSA_BF16) NSA_HIP(nsa::launch_plan(hp, ws, st), "planner launch");
     return NSA_OK;
 }

@@ -15,14 +15,15 @@ namespace nsa {
 
 // ---- Delta ----------------------------------------------------------------
 
-// bf16 rows: D/8 lanes per row, 16-byte loads, fp32 products and sums.
+// bf16 rows: D/8 lanes per row, 16-byte loads, fp32 products and sums; one
+// 256-thread block covers rows [blk * 256 / (D/8), ...).
 template <int D>
-__global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, const uint16_t* __restrict__ o,
-                                                         const uint16_t* __restrict__ dO,
-                                                         float* __restrict__ delta, int64_t nrows) {
+__device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t* __restrict__ o,
+                                                const uint16_t* __restrict__ dO,
+                                                float* __restrict__ delta, int64_t nrows, int64_t blk) {
     constexpr int TPR = D / 8;
     constexpr int RPB = 256 / TPR;
-    int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    int64_t r = blk * RPB + threadIdx.x / TPR;
     int part = threadIdx.x % TPR;
     float acc = 0.f;
     if (r < nrows) {
@@ -46,6 +47,16 @@ __global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, const uint16
         }
         delta[out] = acc;
     }
+}
+
+template <int D>
+constexpr int delta_rows_per_block() { return 256 / (D / 8); }
+
+template <int D>
+__global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dO,
+                                                         float* __restrict__ delta, int64_t nrows) {
+    delta_rows_bf16<D>(p, o, dO, delta, nrows, blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void delta_f32_kernel(Problem p, const float* __restrict__ o,
@@ -106,22 +117,33 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
 // so every list is ascending (a stable counting sort; bit-exact).
 //
 // A row's entry u counts when 0 <= u < NBz and u*bs <= t, once however often
-// the row repeats it: the wave marks u in an LDS bitmap with an atomic OR
-// that returns the old word, so exactly one lane sees the bit clear.
-
-// Marks this lane's entry (if valid) in the wave's bitmap; true for the one
-// lane that set the bit first.
-__device__ __forceinline__ bool mark_first(uint32_t* seen, int u, bool valid) {
-    if (!valid) return false;
-    const uint32_t bit = 1u << (u & 31);
-    return !(atomicOr(&seen[u >> 5], bit) & bit);
-}
-__device__ __forceinline__ void unmark(uint32_t* seen, int u, bool valid) {
-    if (valid) atomicAnd(&seen[u >> 5], ~(1u << (u & 31)));
-}
-
+// the row repeats it.  Each wave keeps a 16-bit array `last` over the blocks:
+// every valid entry of the row first writes its position in the row to
+// last[u] (lanes of one write that hit the same u leave exactly one of their
+// positions), then the entry whose position survived stands for u.  Every u
+// of the row is written before it is read, so `last` needs no clearing
+// between rows; plain LDS writes and reads replace atomics, and distinct
+// blocks never contend for one word.
 __device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t) {
     return u >= 0 && u < NBz && u * bs <= t;
+}
+
+// Calls f(u) once per distinct valid entry u of row (S entries, token t),
+// from the lane holding the representative entry.  Rows of up to 65535
+// entries (positions fit 16 bits).
+template <typename F>
+__device__ __forceinline__ void for_each_distinct(const int* row, int S, int NBz, int bs, int t,
+                                                  int lane, volatile uint16_t* last, F&& f) {
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int si = s0 + lane;
+        const int u = si < S ? row[si] : -1;
+        if (entry_ok(u, NBz, bs, t)) last[u] = (uint16_t)si;
+    }
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int si = s0 + lane;
+        const int u = si < S ? row[si] : -1;
+        if (entry_ok(u, NBz, bs, t) && last[u] == (uint16_t)si) f(u);
+    }
 }
 
 constexpr int kInvWaves = 4;
@@ -138,20 +160,21 @@ __device__ __forceinline__ void stage_rows(const Problem& p, const Seq& s, const
     for (int i = threadIdx.x; i < n; i += blockDim.x) buf[i] = src[i];
 }
 
-__global__ __launch_bounds__(64 * kInvWaves) void inv_count_kernel(Problem p, int CT, int C,
-                                                                   const int* __restrict__ idx,
-                                                                   int* __restrict__ chunk_pos) {
+// Block-idx entries per block for chunk c of (z, hkv) zh: 4 waves take the
+// chunk's tokens round-robin and count each row's distinct valid entries in
+// an LDS histogram (integer atomics: the counts do not depend on order).
+__device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, const int* __restrict__ idx,
+                                            int* __restrict__ chunk_pos, int c, int zh) {
     extern __shared__ int sm[];
     int* hist = sm;                                          // [NBmax]
-    const int NBW = (p.NBmax + 31) / 32;
+    const int NBH = (p.NBmax + 1) / 2;                       // ints per 16-bit array
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t* seen = reinterpret_cast<uint32_t*>(sm + p.NBmax) + w * NBW;
-    int* rows = sm + p.NBmax + kInvWaves * NBW;              // [kRowStage]
-    const int c = blockIdx.x, zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
+    volatile uint16_t* last = reinterpret_cast<volatile uint16_t*>(sm + p.NBmax + w * NBH);
+    int* rows = sm + p.NBmax + kInvWaves * NBH;              // [kRowStage]
+    const int z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
     const int NBz = (s.len + p.bs - 1) / p.bs;
     for (int u = threadIdx.x; u < p.NBmax; u += blockDim.x) hist[u] = 0;
-    for (int i = lane; i < NBW; i += 64) seen[i] = 0u;
     const int t_end = min(c * CT + CT, s.len);
     const int per = max(1, kRowStage / p.S);
     for (int tb = c * CT; tb < t_end; tb += per) {
@@ -159,46 +182,76 @@ __global__ __launch_bounds__(64 * kInvWaves) void inv_count_kernel(Problem p, in
         __syncthreads();
         stage_rows(p, s, idx, hkv, tb, te, rows);
         __syncthreads();
-        for (int t = tb + w; t < te; t += kInvWaves) {
-            const int* row = rows + (t - tb) * p.S;
-            for (int s0 = 0; s0 < p.S; s0 += 64) {
-                const int si = s0 + lane;
-                const int u = si < p.S ? row[si] : -1;
-                if (mark_first(seen, u, entry_ok(u, NBz, p.bs, t))) atomicAdd(&hist[u], 1);
-            }
-            for (int s0 = 0; s0 < p.S; s0 += 64) {
-                const int si = s0 + lane;
-                const int u = si < p.S ? row[si] : -1;
-                unmark(seen, u, entry_ok(u, NBz, p.bs, t));
-            }
-        }
+        for (int t = tb + w; t < te; t += kInvWaves)
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last,
+                              [&](int u) { atomicAdd(&hist[u], 1); });
     }
     __syncthreads();
     int* out = chunk_pos + (int64_t)zh * p.NBmax * C;
     for (int u = threadIdx.x; u < p.NBmax; u += blockDim.x) out[(int64_t)u * C + c] = hist[u];
 }
 
+__global__ __launch_bounds__(64 * kInvWaves) void inv_count_kernel(Problem p, int CT, int C,
+                                                                   const int* __restrict__ idx,
+                                                                   int* __restrict__ chunk_pos) {
+    count_chunk(p, CT, C, idx, chunk_pos, blockIdx.x, blockIdx.y);
+}
+
+// The backward's first launch for bf16: the count blocks (C per (z, hkv),
+// first in the grid, latency-bound) and the Delta blocks (bandwidth-bound)
+// run side by side instead of one kernel after the other.
+template <int D>
+__global__ __launch_bounds__(256) void count_delta_kernel(Problem p, int CT, int C, int ZH,
+                                                          const int* __restrict__ idx,
+                                                          int* __restrict__ chunk_pos,
+                                                          const uint16_t* __restrict__ o,
+                                                          const uint16_t* __restrict__ dO,
+                                                          float* __restrict__ delta, int64_t nrows) {
+    static_assert(64 * kInvWaves == 256, "count and Delta blocks share one block size");
+    const int64_t n_count = (int64_t)C * ZH;
+    if ((int64_t)blockIdx.x < n_count)
+        count_chunk(p, CT, C, idx, chunk_pos, blockIdx.x % C, blockIdx.x / C);
+    else
+        delta_rows_bf16<D>(p, o, dO, delta, nrows, (int64_t)blockIdx.x - n_count);
+}
+
+// Exclusive prefix of one int per thread over a 256-thread block (x of
+// thread i lands in thread i + 1's result); *total gets the sum.  Shuffle
+// scan inside each wave, then the four wave sums through scratch[0..4).
+// Ends with a barrier, so scratch may be reused at once.
+__device__ __forceinline__ int block_scan256(int x, int* scratch, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(v, off, 64);
+        if (lane >= off) v += y;
+    }
+    if (lane == 63) scratch[w] = v;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int sw = scratch[i];
+        base += i < w ? sw : 0;
+        tot += sw;
+    }
+    *total = tot;
+    __syncthreads();
+    return base + v - x;
+}
+
 // Exclusive prefix sum of vals[0..n) (LDS) by one 256-thread block into
-// out[0..n] (out[n] = total).  scratch: 256 ints of LDS.
+// out[0..n] (out[n] = total).  scratch: 4 ints of LDS.
 __device__ void block_excl_scan(const int* vals, int n, int* out, int* scratch) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int per = (n + nt - 1) / nt;
     const int a = min(tid * per, n), b = min(a + per, n);
     int sum = 0;
     for (int i = a; i < b; ++i) sum += vals[i];
-    scratch[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < nt; ++i) {
-            int x = scratch[i];
-            scratch[i] = run;
-            run += x;
-        }
-        out[n] = run;
-    }
-    __syncthreads();
-    int run = scratch[tid];
+    int total;
+    int run = block_scan256(sum, scratch, &total);
+    if (tid == 0) out[n] = total;
     for (int i = a; i < b; ++i) {
         int x = vals[i];
         out[i] = run;
@@ -212,7 +265,7 @@ __device__ void block_excl_scan(const int* vals, int n, int* out, int* scratch) 
 // so the 64-entry segment of each thread starts on its own bank), each
 // thread sums its segment, one scan of the 256 segment sums, each thread
 // rewrites its segment, coalesced copy out.  Returns the total to every
-// thread.  buf: n + n / 64 + 1 ints of LDS; scratch: 257 ints.
+// thread.  buf: n + n / 64 + 1 ints of LDS; scratch: 4 ints.
 __device__ int block_excl_scan_global(int* a, int n, int* buf, int* scratch) {
     const int tid = threadIdx.x, nt = blockDim.x;  // nt == 256
 #pragma unroll 16
@@ -226,23 +279,16 @@ __device__ int block_excl_scan_global(int* a, int n, int* buf, int* scratch) {
         int* sb = buf + seg * 65;
         int sum = 0;
         for (int i = lo; i < hi; ++i) sum += sb[i - lo];
-        scratch[tid] = sum;
-        __syncthreads();
-        for (int off = 1; off < nt; off <<= 1) {
-            const int x = tid >= off ? scratch[tid - off] : 0;
-            __syncthreads();
-            scratch[tid] += x;
-            __syncthreads();
-        }
-        int run = carry + scratch[tid] - sum;
+        int pass_total;
+        int run = carry + block_scan256(sum, scratch, &pass_total);
         for (int i = lo; i < hi; ++i) {
             const int x = sb[i - lo];
             sb[i - lo] = run;
             run += x;
         }
-        carry += scratch[nt - 1];
-        __syncthreads();
+        carry += pass_total;
     }
+    __syncthreads();
 #pragma unroll 16
     for (int i = tid; i < n; i += nt) a[i] = buf[i + (i >> 6)];
     __syncthreads();
@@ -267,7 +313,10 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     int* cp = chunk_pos + (int64_t)zh * NB * C;
     int* off = offsets + (int64_t)zh * (NB + 1);
     const int total = block_excl_scan_global(cp, NB * C, sbuf, scratch);
-    for (int u = threadIdx.x; u < NB; u += blockDim.x) vals[u] = cp[(int64_t)u * C];
+    for (int u = threadIdx.x; u < NB; u += blockDim.x) {
+        const int i = u * C;  // the scanned table is still in sbuf
+        vals[u] = sbuf[i + (i >> 6)];
+    }
     __syncthreads();
     for (int u = threadIdx.x; u <= NB; u += blockDim.x) off[u] = u < NB ? vals[u] : total;
     __syncthreads();
@@ -296,17 +345,16 @@ __global__ __launch_bounds__(64) void inv_fill_kernel(Problem p, int CT, int C,
                                                       const int* __restrict__ chunk_pos,
                                                       int* __restrict__ tokens) {
     extern __shared__ int sm[];
-    const int NBW = (p.NBmax + 31) / 32;
+    const int NBH = (p.NBmax + 1) / 2;
     int* cursor = sm;                                                    // [NBmax]
-    uint32_t* seen = reinterpret_cast<uint32_t*>(sm + p.NBmax);          // [NBW]
-    int* rows = sm + p.NBmax + NBW;                                      // [kRowStage]
+    volatile uint16_t* last = reinterpret_cast<volatile uint16_t*>(sm + p.NBmax);  // [NBmax]
+    int* rows = sm + p.NBmax + NBH;                                      // [kRowStage]
     const int c = blockIdx.x, zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
     const int lane = threadIdx.x;
     const Seq s = seq_of(p, z);
     const int NBz = (s.len + p.bs - 1) / p.bs;
     const int* cp = chunk_pos + (int64_t)zh * p.NBmax * C;
     for (int u = lane; u < p.NBmax; u += 64) cursor[u] = cp[(int64_t)u * C + c];
-    for (int i = lane; i < NBW; i += 64) seen[i] = 0u;
     int* out = tokens + region_base(p, s, hkv);
     const int t_end = min(c * CT + CT, s.len);
     const int per = max(1, kRowStage / p.S);
@@ -315,23 +363,12 @@ __global__ __launch_bounds__(64) void inv_fill_kernel(Problem p, int CT, int C,
         __syncthreads();
         stage_rows(p, s, idx, hkv, tb, te, rows);
         __syncthreads();
-        for (int t = tb; t < te; ++t) {
-            const int* row = rows + (t - tb) * p.S;
-            for (int s0 = 0; s0 < p.S; s0 += 64) {
-                const int si = s0 + lane;
-                const int u = si < p.S ? row[si] : -1;
-                if (mark_first(seen, u, entry_ok(u, NBz, p.bs, t))) {
-                    const int pos = cursor[u];
-                    cursor[u] = pos + 1;
-                    out[pos] = t;
-                }
-            }
-            for (int s0 = 0; s0 < p.S; s0 += 64) {
-                const int si = s0 + lane;
-                const int u = si < p.S ? row[si] : -1;
-                unmark(seen, u, entry_ok(u, NBz, p.bs, t));
-            }
-        }
+        for (int t = tb; t < te; ++t)
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last, [&](int u) {
+                const int pos = cursor[u];
+                cursor[u] = pos + 1;
+                out[pos] = t;
+            });
     }
 }
 
@@ -350,31 +387,68 @@ __global__ __launch_bounds__(256) void plan_kernel(int ZH, const int* __restrict
 }
 
 size_t invert_lds_bytes(const HostProblem& hp) {
-    const int64_t NB = hp.dev.NBmax, NBW = (NB + 31) / 32, n_cp = NB * hp.C;
-    const int64_t count = NB + kInvWaves * NBW + kRowStage;
+    const int64_t NB = hp.dev.NBmax, NBH = (NB + 1) / 2, n_cp = NB * hp.C;
+    const int64_t count = NB + kInvWaves * NBH + kRowStage;
     const int64_t scan = NB + 257 + n_cp + n_cp / 64 + 1;
-    const int64_t fill = NB + NBW + kRowStage;
+    const int64_t fill = NB + NBH + kRowStage;
     return sizeof(int) * (size_t)std::max(count, std::max(scan, fill));
 }
 
-hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
-                         hipStream_t st) {
+namespace {
+size_t count_lds_bytes(const Problem& p) {
+    return sizeof(int) * (p.NBmax + kInvWaves * ((p.NBmax + 1) / 2) + kRowStage);
+}
+
+// Scan and stable fill (after the counts are in chunk_pos).
+hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
+                            hipStream_t st) {
     const Problem& p = hp.dev;
-    if (hp.ZH == 0 || hp.C == 0) return hipSuccess;
-    dim3 grid(hp.C, hp.ZH);
-    const int NBW = (p.NBmax + 31) / 32;
-    size_t lds_count = sizeof(int) * (p.NBmax + kInvWaves * NBW + kRowStage);
-    hipLaunchKernelGGL(inv_count_kernel, grid, dim3(64 * kInvWaves), lds_count, st, p, hp.CT,
-                       hp.C, block_idx, ws.chunk_pos);
+    const int NBH = (p.NBmax + 1) / 2;
     const int64_t n_cp = (int64_t)p.NBmax * hp.C;  // <= 2^14 + NBmax by the choice of CT
     size_t lds_scan = sizeof(int) * (p.NBmax + 257 + n_cp + n_cp / 64 + 1);
     hipLaunchKernelGGL(inv_scan_kernel, dim3(hp.ZH), dim3(256), lds_scan, st, p, hp.C, hp.CR,
                        ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
                        ws.zh_base + 2 * (hp.ZH + 1));
-    size_t lds_fill = sizeof(int) * (p.NBmax + NBW + kRowStage);
-    hipLaunchKernelGGL(inv_fill_kernel, grid, dim3(64), lds_fill, st, p, hp.CT, hp.C, block_idx,
-                       ws.chunk_pos, ws.tokens);
+    size_t lds_fill = sizeof(int) * (p.NBmax + NBH + kRowStage);
+    hipLaunchKernelGGL(inv_fill_kernel, dim3(hp.C, hp.ZH), dim3(64), lds_fill, st, p, hp.CT, hp.C,
+                       block_idx, ws.chunk_pos, ws.tokens);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
+                         hipStream_t st) {
+    const Problem& p = hp.dev;
+    if (hp.ZH == 0 || hp.C == 0) return hipSuccess;
+    hipLaunchKernelGGL(inv_count_kernel, dim3(hp.C, hp.ZH), dim3(64 * kInvWaves), count_lds_bytes(p),
+                       st, p, hp.CT, hp.C, block_idx, ws.chunk_pos);
+    return launch_scan_fill(hp, block_idx, ws, st);
+}
+
+hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, const int* block_idx,
+                          const BwdWorkspace& ws, hipStream_t st) {
+    const Problem& p = hp.dev;
+    if (hp.dtype != 1 || hp.ZH == 0 || hp.C == 0 || hp.rows == 0) {
+        const hipError_t e = launch_delta(hp, o, dO, ws.delta, st);
+        if (e != hipSuccess) return e;
+        return launch_invert(hp, block_idx, ws, st);
+    }
+    const int64_t n_count = (int64_t)hp.C * hp.ZH;
+    auto go = [&](auto kernel, int rpb) {
+        const int64_t n_delta = (hp.rows + rpb - 1) / rpb;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(n_count + n_delta)), dim3(256), count_lds_bytes(p), st,
+                           p, hp.CT, hp.C, hp.ZH, block_idx, ws.chunk_pos, (const uint16_t*)o,
+                           (const uint16_t*)dO, ws.delta, hp.rows);
+    };
+    switch (p.D) {
+        case 32: go(count_delta_kernel<32>, delta_rows_per_block<32>()); break;
+        case 64: go(count_delta_kernel<64>, delta_rows_per_block<64>()); break;
+        case 128: go(count_delta_kernel<128>, delta_rows_per_block<128>()); break;
+        default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_scan_fill(hp, block_idx, ws, st);
 }
 
 hipError_t launch_plan(const HostProblem& hp, const BwdWorkspace& ws, hipStream_t st) {

@@ -44,6 +44,10 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
                         hipStream_t st);
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st);
+// Delta and the inversion, as the backward's prepare stage runs them (for
+// bf16 the Delta rows and the inversion counts share one launch).
+hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, const int* block_idx,
+                          const BwdWorkspace& ws, hipStream_t st);
 hipError_t launch_plan(const HostProblem& hp, const BwdWorkspace& ws, hipStream_t st);
 
 hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,

@@ -29,12 +29,25 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
 
-def source_hash() -> str:
-    """Hash of the HIP sources and the public header."""
+# The sources a kernel's memory traffic depends on: its own file, the shared
+# device headers, the launch parameters chosen in nsa_api.hip, and for the
+# dK/dV kernel the inversion and plan that lay out its row lists and items.
+_COMMON = ("nsa_device.h", "nsa_internal.h", "nsa_api.hip")
+KERNEL_SOURCES = {
+    "fwd_q_kernel": ("nsa_query.hip",) + _COMMON,
+    "dq_q_kernel": ("nsa_query.hip",) + _COMMON,
+    "dkdv_kernel": ("nsa_dkdv.hip", "nsa_common.hip") + _COMMON,
+}
+
+
+def source_hash(kernel: str = None) -> str:
+    """Hash of the HIP sources a kernel's traffic depends on (all HIP sources
+    and the public header when kernel is None or unknown)."""
     h = hashlib.sha256()
+    files = KERNEL_SOURCES.get(kernel)
     for d in (os.path.join(HERE, "csrc"), os.path.join(ROOT, "include")):
         for f in sorted(os.listdir(d)):
-            if f.endswith((".hip", ".h")):
+            if f.endswith((".hip", ".h")) and (files is None or f in files or d.endswith("include")):
                 with open(os.path.join(d, f), "rb") as fh:
                     h.update(fh.read())
     return h.hexdigest()[:16]
@@ -89,7 +102,7 @@ def main() -> None:
     rec = {
         "kernel": a.kernel,
         "workload": a.workload,
-        "source_hash": source_hash(),
+        "source_hash": source_hash(a.kernel),
         "fetch_bytes_per_launch": round(fetch),
         "write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
