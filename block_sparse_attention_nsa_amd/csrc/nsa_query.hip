@@ -509,6 +509,80 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
 
+    // Pieces of one tile's job.  K operands: all 16-key x 32-d slices of the
+    // job, each lane's 16 bytes (A layout).
+    using KOps = bf16x8[NKT][KD];
+    auto read_k = [&](const uint8_t* ks, KOps& ka) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int kk = 0; kk < KD; ++kk)
+                ka[kt][kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
+    };
+    // Transposed V operand of keys 32 ks_ .. 32 ks_ + 31 (the C layout of S
+    // gave this lane keys 32ks + 4g + e and 32ks + 16 + 4g + e).
+    auto read_v = [&](const uint8_t* vs, int ks_, bf16x8 (&vop)[ND]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const uint8_t* vb0 = vs + t_off[dt] + 32 * ks_ * L::RB;
+            const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
+            const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
+            vop[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
+        }
+    };
+    // Mask, online softmax (lazy rescale of tile i's O and l), P in bf16.
+    auto softmax = [&](int i, f32x4 (&sc)[NKT], const Job& cur, uint64_t bm,
+                       bf16x8 (&pb)[NKS]) __attribute__((always_inline)) {
+        // No mask when every token of the tile lists the block, the slice
+        // ends before the tile's first token, and all rows exist.
+        const bool full = ((bm & tmask[i]) == tmask[i]) &&
+                          (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
+                          tr[i].valid;
+        float mloc = kNegInfQ;
+        if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, sc[kt][e]);
+        } else {
+            const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
+            // Key 16 kt + 4 g + e is masked past lim; compared as
+            // 16 kt + e > lim - 4 g so the left side is a constant.
+            const int lim = (sel ? tr[i].t - cur.j0 : -1) - 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (16 * kt + e > lim) sc[kt][e] = kNegInfQ;
+                    mloc = fmaxf(mloc, sc[kt][e]);
+                }
+        }
+        const float mblk = col_max4(mloc);
+        const bool grow = mblk * c2 > m_run[i] * c2 + kLazyQ;
+        if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
+            const float m_new = grow ? mblk : m_run[i];
+            const float alpha = grow ? fast_exp2((m_run[i] - m_new) * c2) : 1.f;
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) acc[i][dt] *= alpha;
+            l_run[i] *= alpha;
+            m_run[i] = m_new;
+        }
+        const float mc = m_run[i] == kNegInfQ ? 0.f : m_run[i] * c2;
+        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks_ = 0; ks_ < NKS; ++ks_) {
+            float p0[4], p1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, -mc));
+                p1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, -mc));
+                lsum[e] += p0[e] + p1[e];
+            }
+            pb[ks_] = pack8(p0, p1);
+        }
+        l_run[i] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+
     // One job: for each tile whose tokens list the block, S^T = K Q^T (all
     // K operand reads in flight at once), the softmax, then O^T += V^T P^T
     // with the transposed V reads of each 32-key step issued together.  The
@@ -522,12 +596,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
             if (!__builtin_amdgcn_readfirstlane((int)((bm & tmask[i]) != 0ull))) continue;
             f32x4 sc[NKT];
             {
-                bf16x8 ka[NKT][KD];
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int kk = 0; kk < KD; ++kk)
-                        ka[kt][kk] = *reinterpret_cast<const bf16x8*>(ks + a_off[kk] + kt * 16 * L::RB);
+                KOps ka;
+                read_k(ks, ka);
                 // All K reads are issued before the products (each into its
                 // own registers), not one read per product.
                 __builtin_amdgcn_sched_barrier(0);
@@ -541,75 +611,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
             // The transposed V reads of the first 32 keys go out while the
             // products run (they do not depend on the softmax).
             bf16x8 vop0[ND];
-#pragma unroll
-            for (int dt = 0; dt < ND; ++dt) {
-                const uint8_t* vb0 = vs + t_off[dt];
-                const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
-                const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
-                vop0[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-            }
-            // No mask when every token of the tile lists the block, the slice
-            // ends before the tile's first token, and all rows exist.
-            const bool full = ((bm & tmask[i]) == tmask[i]) &&
-                              (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
-                              tr[i].valid;
-            float mloc = kNegInfQ;
-            if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, sc[kt][e]);
-            } else {
-                const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
-                const int lim = sel ? tr[i].t - cur.j0 : -1;
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
-                        mloc = fmaxf(mloc, sc[kt][e]);
-                    }
-            }
-            const float mblk = col_max4(mloc);
-            const bool grow = mblk * c2 > m_run[i] * c2 + kLazyQ;
-            if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
-                const float m_new = grow ? mblk : m_run[i];
-                const float alpha = grow ? fast_exp2((m_run[i] - m_new) * c2) : 1.f;
-#pragma unroll
-                for (int dt = 0; dt < ND; ++dt) acc[i][dt] *= alpha;
-                l_run[i] *= alpha;
-                m_run[i] = m_new;
-            }
-            const float mc = m_run[i] == kNegInfQ ? 0.f : m_run[i] * c2;
-            float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+            read_v(vs, 0, vop0);
             bf16x8 pb[NKS];
-#pragma unroll
-            for (int ks_ = 0; ks_ < NKS; ++ks_) {
-                float p0[4], p1[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, -mc));
-                    p1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, -mc));
-                    lsum[e] += p0[e] + p1[e];
-                }
-                pb[ks_] = pack8(p0, p1);
-            }
-            l_run[i] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-            // O^T += V^T P^T, 32 keys per step: keys 32ks + 4g + e and
-            // 32ks + 16 + 4g + e are the ones the C layout of S gave this lane.
+            softmax(i, sc, cur, bm, pb);
 #pragma unroll
             for (int ks_ = 0; ks_ < NKS; ++ks_) {
                 bf16x8 vop[ND];
+                if (ks_ == 0) {
 #pragma unroll
-                for (int dt = 0; dt < ND; ++dt) {
-                    if (ks_ == 0) {
-                        vop[dt] = vop0[dt];
-                    } else {
-                        const uint8_t* vb0 = vs + t_off[dt] + 32 * ks_ * L::RB;
-                        const uint2 v0 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0));
-                        const uint2 v1 = lds_read_tr(reinterpret_cast<const uint16_t*>(vb0 + 16 * L::RB));
-                        vop[dt] = __builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y));
-                    }
+                    for (int dt = 0; dt < ND; ++dt) vop[dt] = vop0[dt];
+                } else {
+                    read_v(vs, ks_, vop);
                 }
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(vop[dt], pb[ks_], acc[i][dt]);
@@ -617,8 +629,56 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         }
     };
 
+    // The same job for both tiles of the wave at once (whole-prefix
+    // selections, where every tile works on nearly every job): each K and V
+    // operand read from LDS feeds both tiles' products, which halves the
+    // LDS reads, and one tile's softmax overlaps the other's products.  A
+    // tile none of whose tokens lists the block is masked out entirely.
+    auto compute_pair = [&](const Job& cur, const KVStage<D, JK>& sg) {
+        static_assert(RT == 2, "two tiles per wave");
+        const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
+        const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
+        const uint64_t bm = umask[cur.u];
+        f32x4 sc0[NKT], sc1[NKT];
+        {
+            KOps ka;
+            read_k(ks, ka);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                sc0[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sc1[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KD; ++kk) {
+                    sc0[kt] = mfma(ka[kt][kk], qf[0][kk], sc0[kt]);
+                    sc1[kt] = mfma(ka[kt][kk], qf[1][kk], sc1[kt]);
+                }
+            }
+        }
+        bf16x8 vop0[ND];
+        read_v(vs, 0, vop0);
+        bf16x8 pb0[NKS], pb1[NKS];
+        softmax(0, sc0, cur, bm, pb0);
+        softmax(1, sc1, cur, bm, pb1);
+#pragma unroll
+        for (int ks_ = 0; ks_ < NKS; ++ks_) {
+            bf16x8 vop[ND];
+            if (ks_ == 0) {
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) vop[dt] = vop0[dt];
+            } else {
+                read_v(vs, ks_, vop);
+            }
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) {
+                acc[0][dt] = mfma(vop[dt], pb0[ks_], acc[0][dt]);
+                acc[1][dt] = mfma(vop[dt], pb1[ks_], acc[1][dt]);
+            }
+        }
+    };
+
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, compute);
+        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, compute_pair);
     } else {
         q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
     }
@@ -704,6 +764,45 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
 
+    // Pieces of one tile's job.  Mask of S^T (-inf outside the tile's
+    // selection and causal range), then dS = P (dP - Delta) in bf16.
+    auto dscore = [&](int i, f32x4 (&sc)[NKT], const f32x4 (&dp)[NKT], const Job& cur, uint64_t bm,
+                      bf16x8 (&dsb)[NKS]) __attribute__((always_inline)) {
+        const bool full = ((bm & tmask[i]) == tmask[i]) &&
+                          (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
+                          tr[i].valid;
+        if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
+            const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
+            // Key 16 kt + 4 g + e is masked past lim (constant left side).
+            const int lim = (sel ? tr[i].t - cur.j0 : -1) - 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (16 * kt + e > lim) sc[kt][e] = kNegInfQ;
+        }
+#pragma unroll
+        for (int ks_ = 0; ks_ < NKS; ++ks_) {
+            float d0[4], d1[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, nlse2[i])) * (dp[2 * ks_][e] - dl[i]);
+                d1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, nlse2[i])) * (dp[2 * ks_ + 1][e] - dl[i]);
+            }
+            dsb[ks_] = pack8(d0, d1);
+        }
+    };
+    // Transposed K operand of keys 32 ks_ .. 32 ks_ + 31 for dQ^T += K^T dS^T.
+    auto read_kt = [&](const uint8_t* ks, int ks_, bf16x8 (&kop)[ND]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const uint8_t* kb0 = ks + t_off[dt] + 32 * ks_ * L::RB;
+            const uint2 k0 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0));
+            const uint2 k1 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0 + 16 * L::RB));
+            kop[dt] = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+        }
+    };
+
     // One job: for each tile whose tokens list the block, S^T = K Q^T and
     // dP^T = V dO^T (all K and V operand reads in flight at once), dS, then
     // dQ^T += K^T dS^T with the transposed K reads of each 32-key step issued
@@ -734,40 +833,13 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
                     dp[kt] = mfma(va[kk], df[i][kk], dp[kt]);
                 }
             }
-            const bool full = ((bm & tmask[i]) == tmask[i]) &&
-                              (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
-                              tr[i].valid;
-            if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
-                const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
-                const int lim = sel ? tr[i].t - cur.j0 : -1;
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (16 * kt + 4 * g + e > lim) sc[kt][e] = kNegInfQ;
-            }
             bf16x8 dsb[NKS];
-#pragma unroll
-            for (int ks_ = 0; ks_ < NKS; ++ks_) {
-                float d0[4], d1[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    d0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, nlse2[i])) * (dp[2 * ks_][e] - dl[i]);
-                    d1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, nlse2[i])) * (dp[2 * ks_ + 1][e] - dl[i]);
-                }
-                dsb[ks_] = pack8(d0, d1);
-            }
+            dscore(i, sc, dp, cur, bm, dsb);
             // dQ^T += K^T dS^T, 32 keys per step.
 #pragma unroll
             for (int ks_ = 0; ks_ < NKS; ++ks_) {
                 bf16x8 kop[ND];
-#pragma unroll
-                for (int dt = 0; dt < ND; ++dt) {
-                    const uint8_t* kb0 = ks + t_off[dt] + 32 * ks_ * L::RB;
-                    const uint2 k0 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0));
-                    const uint2 k1 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0 + 16 * L::RB));
-                    kop[dt] = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
-                }
+                read_kt(ks, ks_, kop);
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(kop[dt], dsb[ks_], acc[i][dt]);
             }
