@@ -129,6 +129,7 @@ nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
     w.item_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
     w.pslot_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
     w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 2 * ZH));
+    w.ticket = (int*)take(sizeof(int));
     w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * hp.dev.bs * hp.dev.D);
     w.bytes = off;
     return w;
@@ -214,7 +215,6 @@ nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProble
 nsa_status run_prepare(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
     const nsa::BwdWorkspace ws = carve(hp, a.ws);
     NSA_HIP(nsa::launch_prepare(hp, a.o, a.dO, a.idx, ws, st), "Delta / inversion launch");
-    if (hp.dtype == NSA_BF16) NSA_HIP(nsa::launch_plan(hp, ws, st), "planner launch");
     return NSA_OK;
 }
 

@@ -164,7 +164,10 @@ __device__ __forceinline__ void stage_rows(const Problem& p, const Seq& s, const
 // chunk's tokens round-robin and count each row's distinct valid entries in
 // an LDS histogram (integer atomics: the counts do not depend on order).
 __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, const int* __restrict__ idx,
-                                            int* __restrict__ chunk_pos, int c, int zh) {
+                                            int* __restrict__ chunk_pos, int c, int zh,
+                                            int* __restrict__ ticket) {
+    // The scan that follows counts its finished workgroups from zero.
+    if (c == 0 && zh == 0 && threadIdx.x == 0) *ticket = 0;
     extern __shared__ int sm[];
     int* hist = sm;                                          // [NBmax]
     const int NBH = (p.NBmax + 1) / 2;                       // ints per 16-bit array
@@ -193,8 +196,9 @@ __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, con
 
 __global__ __launch_bounds__(64 * kInvWaves) void inv_count_kernel(Problem p, int CT, int C,
                                                                    const int* __restrict__ idx,
-                                                                   int* __restrict__ chunk_pos) {
-    count_chunk(p, CT, C, idx, chunk_pos, blockIdx.x, blockIdx.y);
+                                                                   int* __restrict__ chunk_pos,
+                                                                   int* __restrict__ ticket) {
+    count_chunk(p, CT, C, idx, chunk_pos, blockIdx.x, blockIdx.y, ticket);
 }
 
 // The backward's first launch for bf16: the count blocks (C per (z, hkv),
@@ -204,13 +208,14 @@ template <int D>
 __global__ __launch_bounds__(256) void count_delta_kernel(Problem p, int CT, int C, int ZH,
                                                           const int* __restrict__ idx,
                                                           int* __restrict__ chunk_pos,
+                                                          int* __restrict__ ticket,
                                                           const uint16_t* __restrict__ o,
                                                           const uint16_t* __restrict__ dO,
                                                           float* __restrict__ delta, int64_t nrows) {
     static_assert(64 * kInvWaves == 256, "count and Delta blocks share one block size");
     const int64_t n_count = (int64_t)C * ZH;
     if ((int64_t)blockIdx.x < n_count)
-        count_chunk(p, CT, C, idx, chunk_pos, blockIdx.x % C, blockIdx.x / C);
+        count_chunk(p, CT, C, idx, chunk_pos, blockIdx.x % C, blockIdx.x / C, ticket);
     else
         delta_rows_bf16<D>(p, o, dO, delta, nrows, (int64_t)blockIdx.x - n_count);
 }
@@ -296,19 +301,24 @@ __device__ int block_excl_scan_global(int* a, int n, int* buf, int* scratch) {
 }
 
 // Per (z, hkv): list cursors for every (block, chunk), CSR offsets, and the
-// number of dK/dV work items (ceil(rows / CR), rows = tokens * G) and fp32
-// partial slots (the items, when a list needs more than one) per list.
-__global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
+// number of dK/dV work items (ceil(rows / CR), rows = tokens * G; at least
+// one for a block inside the sequence when min1, so that its workgroup
+// writes the zeros of an empty list) and fp32 partial slots (the items, when
+// a list needs more than one) per list.
+__global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR, int min1,
                                                        int* __restrict__ chunk_pos,
                                                        int* __restrict__ offsets,
                                                        int* __restrict__ item_pre,
                                                        int* __restrict__ pslot_pre,
-                                                       int* __restrict__ zh_tot) {
+                                                       int* __restrict__ zh_base,
+                                                       int* __restrict__ ticket) {
+    int* zh_tot = zh_base + 2 * (gridDim.x + 1);
     extern __shared__ int sm[];
     const int NB = p.NBmax;
-    int* vals = sm;             // [NB]
-    int* scratch = sm + NB;     // [257]
-    int* sbuf = sm + NB + 257;  // [NB C + NB C / 64 + 1]
+    const int VN = max(NB, (int)gridDim.x);
+    int* vals = sm;             // [max(NB, ZH)]
+    int* scratch = sm + VN;     // [257]
+    int* sbuf = sm + VN + 257;  // [NB C + NB C / 64 + 1]
     const int zh = blockIdx.x;
     int* cp = chunk_pos + (int64_t)zh * NB * C;
     int* off = offsets + (int64_t)zh * (NB + 1);
@@ -320,9 +330,11 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     __syncthreads();
     for (int u = threadIdx.x; u <= NB; u += blockDim.x) off[u] = u < NB ? vals[u] : total;
     __syncthreads();
+    const int len = seq_of(p, zh / p.Hkv).len;
     for (int u = threadIdx.x; u < NB; u += blockDim.x) {
         const int rows = (off[u + 1] - off[u]) * p.G;
-        vals[u] = (rows + CR - 1) / CR;
+        const int items = (rows + CR - 1) / CR;
+        vals[u] = min1 && u * p.bs < len ? max(items, 1) : items;
     }
     __syncthreads();
     int* ipre = item_pre + (int64_t)zh * (NB + 1);
@@ -331,10 +343,29 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     __syncthreads();
     int* ppre = pslot_pre + (int64_t)zh * (NB + 1);
     block_excl_scan(vals, NB, ppre, scratch);
+    // The last workgroup to finish also writes the global prefixes over
+    // (z, hkv) of items and partial slots (the dK/dV work plan): each
+    // workgroup publishes its totals, then takes a ticket; the one holding
+    // the last ticket reads every total back from L2.
+    __shared__ int last;
     if (threadIdx.x == 0) {
         zh_tot[zh] = ipre[NB];
         zh_tot[gridDim.x + zh] = ppre[NB];
+        __threadfence();
+        last = atomicAdd(ticket, 1) == (int)gridDim.x - 1;
     }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    const int ZH = gridDim.x;
+    for (int i = threadIdx.x; i < ZH; i += blockDim.x)
+        vals[i] = __hip_atomic_load(&zh_tot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    block_excl_scan(vals, ZH, zh_base, scratch);
+    for (int i = threadIdx.x; i < ZH; i += blockDim.x)
+        vals[i] = __hip_atomic_load(&zh_tot[ZH + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    block_excl_scan(vals, ZH, zh_base + ZH + 1, scratch);
 }
 
 // Stable fill: one wave walks its chunk's tokens in ascending order and
@@ -372,24 +403,10 @@ __global__ __launch_bounds__(64) void inv_fill_kernel(Problem p, int CT, int C,
     }
 }
 
-// Global exclusive prefixes over (z, hkv) of work items and partial slots.
-__global__ __launch_bounds__(256) void plan_kernel(int ZH, const int* __restrict__ zh_tot,
-                                                   int* __restrict__ zh_base) {
-    extern __shared__ int sm[];
-    int* vals = sm;
-    int* scratch = sm + ZH;
-    for (int i = threadIdx.x; i < ZH; i += blockDim.x) vals[i] = zh_tot[i];
-    __syncthreads();
-    block_excl_scan(vals, ZH, zh_base, scratch);
-    for (int i = threadIdx.x; i < ZH; i += blockDim.x) vals[i] = zh_tot[ZH + i];
-    __syncthreads();
-    block_excl_scan(vals, ZH, zh_base + ZH + 1, scratch);
-}
-
 size_t invert_lds_bytes(const HostProblem& hp) {
     const int64_t NB = hp.dev.NBmax, NBH = (NB + 1) / 2, n_cp = NB * hp.C;
     const int64_t count = NB + kInvWaves * NBH + kRowStage;
-    const int64_t scan = NB + 257 + n_cp + n_cp / 64 + 1;
+    const int64_t scan = std::max<int64_t>(NB, hp.ZH) + 257 + n_cp + n_cp / 64 + 1;
     const int64_t fill = NB + NBH + kRowStage;
     return sizeof(int) * (size_t)std::max(count, std::max(scan, fill));
 }
@@ -405,10 +422,12 @@ hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const B
     const Problem& p = hp.dev;
     const int NBH = (p.NBmax + 1) / 2;
     const int64_t n_cp = (int64_t)p.NBmax * hp.C;  // <= 2^14 + NBmax by the choice of CT
-    size_t lds_scan = sizeof(int) * (p.NBmax + 257 + n_cp + n_cp / 64 + 1);
+    size_t lds_scan = sizeof(int) * (std::max(p.NBmax, hp.ZH) + 257 + n_cp + n_cp / 64 + 1);
+    // Without partial slots no list is split and the dK/dV kernel itself
+    // writes the zeros of empty lists (one item each), so no reduce runs.
     hipLaunchKernelGGL(inv_scan_kernel, dim3(hp.ZH), dim3(256), lds_scan, st, p, hp.C, hp.CR,
-                       ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
-                       ws.zh_base + 2 * (hp.ZH + 1));
+                       hp.pslots == 0 ? 1 : 0, ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
+                       ws.zh_base, ws.ticket);
     size_t lds_fill = sizeof(int) * (p.NBmax + NBH + kRowStage);
     hipLaunchKernelGGL(inv_fill_kernel, dim3(hp.C, hp.ZH), dim3(64), lds_fill, st, p, hp.CT, hp.C,
                        block_idx, ws.chunk_pos, ws.tokens);
@@ -421,7 +440,7 @@ hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdW
     const Problem& p = hp.dev;
     if (hp.ZH == 0 || hp.C == 0) return hipSuccess;
     hipLaunchKernelGGL(inv_count_kernel, dim3(hp.C, hp.ZH), dim3(64 * kInvWaves), count_lds_bytes(p),
-                       st, p, hp.CT, hp.C, block_idx, ws.chunk_pos);
+                       st, p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.ticket);
     return launch_scan_fill(hp, block_idx, ws, st);
 }
 
@@ -437,7 +456,7 @@ hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, 
     auto go = [&](auto kernel, int rpb) {
         const int64_t n_delta = (hp.rows + rpb - 1) / rpb;
         hipLaunchKernelGGL(kernel, dim3((unsigned)(n_count + n_delta)), dim3(256), count_lds_bytes(p), st,
-                           p, hp.CT, hp.C, hp.ZH, block_idx, ws.chunk_pos, (const uint16_t*)o,
+                           p, hp.CT, hp.C, hp.ZH, block_idx, ws.chunk_pos, ws.ticket, (const uint16_t*)o,
                            (const uint16_t*)dO, ws.delta, hp.rows);
     };
     switch (p.D) {
@@ -451,12 +470,5 @@ hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, 
     return launch_scan_fill(hp, block_idx, ws, st);
 }
 
-hipError_t launch_plan(const HostProblem& hp, const BwdWorkspace& ws, hipStream_t st) {
-    if (hp.ZH == 0) return hipSuccess;
-    size_t lds = sizeof(int) * (hp.ZH + 257);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), lds, st, hp.ZH,
-                       ws.zh_base + 2 * (hp.ZH + 1), ws.zh_base);
-    return hipGetLastError();
-}
 
 }  // namespace nsa

@@ -594,7 +594,9 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
     const int64_t n_blocks = (int64_t)hp.ZH * hp.dev.NBmax;
     const int64_t rs_min = ((int64_t)hp.dev.bs * hp.dev.D / 2 + 1023) / 1024;  // 2 E4 / (256 * 4)
     const int rs = (int)std::max<int64_t>(rs_min, std::min<int64_t>(16, 4096 / std::max<int64_t>(1, n_blocks)));
-    const unsigned nred = (parts & kDkdvReduce) ? (unsigned)(n_blocks * rs) : 0u;
+    // Without partial slots every list (empty ones included) is written whole
+    // by the block kernel: nothing to reduce.
+    const unsigned nred = (parts & kDkdvReduce) && hp.pslots > 0 ? (unsigned)(n_blocks * rs) : 0u;
     if (items) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
                           hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 16 * 64), 0,

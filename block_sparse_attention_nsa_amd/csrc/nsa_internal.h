@@ -32,7 +32,9 @@ struct BwdWorkspace {
     int* tokens;         // [cap]: inverted lists
     int* item_pre;       // [ZH][NBmax + 1]: exclusive prefix of work items per list
     int* pslot_pre;      // [ZH][NBmax + 1]: exclusive prefix of partial slots per list
-    int* zh_base;        // [2][ZH + 1]: global prefixes of items and partial slots
+    int* zh_base;        // [2][ZH + 1]: global prefixes of items and partial slots,
+                         // then [2][ZH]: per-(z, hkv) totals of both
+    int* ticket;         // [1]: scan workgroups done (the last one plans)
     float* partials;     // [pslots][bs][D][2]
     size_t bytes;
 };
@@ -44,11 +46,11 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
                         hipStream_t st);
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st);
-// Delta and the inversion, as the backward's prepare stage runs them (for
-// bf16 the Delta rows and the inversion counts share one launch).
+// Delta, the inversion and the dK/dV work plan, as the backward's prepare
+// stage runs them (for bf16 the Delta rows and the inversion counts share one
+// launch; the last scan workgroup writes the plan).
 hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, const int* block_idx,
                           const BwdWorkspace& ws, hipStream_t st);
-hipError_t launch_plan(const HostProblem& hp, const BwdWorkspace& ws, hipStream_t st);
 
 hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                            const int* block_idx, void* o, float* lse, hipStream_t st);
