@@ -5,8 +5,9 @@
 //                 (z, hkv, block u), the ascending tokens t >= u*bs listing u,
 //                 as CSR lists, so that dK/dV of block u can be accumulated by one
 //                 owner without global atomics.  Integer work, bit-exact: counts
-//                 use LDS atomics (order-free), the fill is a stable sequential pass.
-//   * plan:       global prefix of dK/dV work items and fp32 partial slots.
+//                 use LDS atomics (order-free), the fill is a stable pass.
+//   * plan:       global prefix of dK/dV work items and fp32 partial slots
+//                 (written by the scan's last workgroup).
 #include <algorithm>
 
 #include "nsa_internal.h"
@@ -112,9 +113,11 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
 // chunk, how many of its tokens list each block (LDS histogram), stored
 // block-major [zh][u][c].  scan: one flat exclusive prefix over that
 // block-major array gives, for chunk c, where its first entry of block u goes
-// (all earlier blocks, then earlier chunks of u).  fill: one wave per chunk
-// walks its tokens in ascending order and appends each to its blocks' lists,
-// so every list is ascending (a stable counting sort; bit-exact).
+// (all earlier blocks, then earlier chunks of u); its last workgroup also
+// writes the dK/dV work plan.  fill: the waves of a chunk's workgroup take
+// consecutive runs of its tokens, split each block's cursor by their counts,
+// and append their tokens in ascending order, so every list is ascending (a
+// stable counting sort; bit-exact).
 //
 // A row's entry u counts when 0 <= u < NBz and u*bs <= t, once however often
 // the row repeats it.  Each wave keeps a 16-bit array `last` over the blocks:
@@ -368,46 +371,89 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     block_excl_scan(vals, ZH, zh_base + ZH + 1, scratch);
 }
 
-// Stable fill: one wave walks its chunk's tokens in ascending order and
-// appends each to the lists of the blocks it validly lists (once each); the
-// rows are staged in LDS first.
-__global__ __launch_bounds__(64) void inv_fill_kernel(Problem p, int CT, int C,
-                                                      const int* __restrict__ idx,
-                                                      const int* __restrict__ chunk_pos,
-                                                      int* __restrict__ tokens) {
+// Stable fill of chunk c of (z, hkv) zh by NW waves.  The chunk's rows are
+// staged in LDS a batch of tokens at a time; the batch's tokens are cut into
+// NW consecutive runs, one per wave.  Each wave counts the distinct valid
+// entries of its run per block (hist[w][u], plain LDS increments: a row's
+// lanes hold distinct blocks and a wave takes its rows one after another),
+// the block cursors are then split over the waves in wave order (hist[w][u]
+// becomes the first position of wave w's entries of block u), and each wave
+// appends its tokens, ascending, at those positions.  So every list is
+// ascending in t, exactly as one wave walking the whole chunk would write it.
+__global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
+                                                       const int* __restrict__ idx,
+                                                       const int* __restrict__ chunk_pos,
+                                                       int* __restrict__ tokens) {
     extern __shared__ int sm[];
-    const int NBH = (p.NBmax + 1) / 2;
-    int* cursor = sm;                                                    // [NBmax]
-    volatile uint16_t* last = reinterpret_cast<volatile uint16_t*>(sm + p.NBmax);  // [NBmax]
-    int* rows = sm + p.NBmax + NBH;                                      // [kRowStage]
+    const int NB = p.NBmax, NBH = (NB + 1) / 2, NW = (int)blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int* cursor = sm;                                     // [NB]
+    int* hist = sm + NB;                                  // [NW][NB]
+    volatile uint16_t* last =
+        reinterpret_cast<volatile uint16_t*>(sm + NB + NW * NB + w * NBH);  // [NW][NB] u16
+    int* rows = sm + NB + NW * NB + NW * NBH;             // [kRowStage]
+    int* hw = hist + w * NB;
     const int c = blockIdx.x, zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
-    const int lane = threadIdx.x;
     const Seq s = seq_of(p, z);
+    if (c * CT >= s.len) return;  // chunk past a short sequence's end
     const int NBz = (s.len + p.bs - 1) / p.bs;
-    const int* cp = chunk_pos + (int64_t)zh * p.NBmax * C;
-    for (int u = lane; u < p.NBmax; u += 64) cursor[u] = cp[(int64_t)u * C + c];
+    const int* cp = chunk_pos + (int64_t)zh * NB * C;
+    for (int u = threadIdx.x; u < NB; u += blockDim.x) cursor[u] = cp[(int64_t)u * C + c];
     int* out = tokens + region_base(p, s, hkv);
     const int t_end = min(c * CT + CT, s.len);
     const int per = max(1, kRowStage / p.S);
     for (int tb = c * CT; tb < t_end; tb += per) {
         const int te = min(tb + per, t_end);
+        for (int u = lane; u < NB; u += 64) hw[u] = 0;
         __syncthreads();
         stage_rows(p, s, idx, hkv, tb, te, rows);
         __syncthreads();
-        for (int t = tb; t < te; ++t)
+        // This wave's run of the batch.
+        const int n = te - tb, q = n / NW, rm = n % NW;
+        const int r0 = tb + w * q + min(w, rm), r1 = r0 + q + (w < rm ? 1 : 0);
+        for (int t = r0; t < r1; ++t)
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last,
+                              [&](int u) { hw[u] += 1; });
+        __syncthreads();
+        for (int u = threadIdx.x; u < NB; u += blockDim.x) {
+            int run = cursor[u];
+            for (int v = 0; v < NW; ++v) {
+                const int x = hist[v * NB + u];
+                hist[v * NB + u] = run;
+                run += x;
+            }
+            cursor[u] = run;
+        }
+        __syncthreads();
+        for (int t = r0; t < r1; ++t)
             for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last, [&](int u) {
-                const int pos = cursor[u];
-                cursor[u] = pos + 1;
+                const int pos = hw[u];
+                hw[u] = pos + 1;
                 out[pos] = t;
             });
+        __syncthreads();
     }
+}
+
+// Waves of the fill: as many as LDS allows (at most 8), at least four tokens
+// each (measured: with 16-token chunks, 4 waves beat 2 and 8).
+int fill_waves(const HostProblem& hp) {
+    const int64_t NB = hp.dev.NBmax, NBH = (NB + 1) / 2;
+    int nw = 8;
+    while (nw > 1 && 4 * (NB + nw * (NB + NBH) + kRowStage) > 163840) --nw;
+    return std::max(1, std::min(nw, hp.CT / 4));
+}
+
+size_t fill_lds_bytes(const HostProblem& hp, int nw) {
+    const int64_t NB = hp.dev.NBmax, NBH = (NB + 1) / 2;
+    return sizeof(int) * (size_t)(NB + nw * (NB + NBH) + kRowStage);
 }
 
 size_t invert_lds_bytes(const HostProblem& hp) {
     const int64_t NB = hp.dev.NBmax, NBH = (NB + 1) / 2, n_cp = NB * hp.C;
     const int64_t count = NB + kInvWaves * NBH + kRowStage;
     const int64_t scan = std::max<int64_t>(NB, hp.ZH) + 257 + n_cp + n_cp / 64 + 1;
-    const int64_t fill = NB + NBH + kRowStage;
+    const int64_t fill = NB + (NB + NBH) + kRowStage;  // one wave: the least the fill needs
     return sizeof(int) * (size_t)std::max(count, std::max(scan, fill));
 }
 
@@ -420,7 +466,6 @@ size_t count_lds_bytes(const Problem& p) {
 hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                             hipStream_t st) {
     const Problem& p = hp.dev;
-    const int NBH = (p.NBmax + 1) / 2;
     const int64_t n_cp = (int64_t)p.NBmax * hp.C;  // <= 2^14 + NBmax by the choice of CT
     size_t lds_scan = sizeof(int) * (std::max(p.NBmax, hp.ZH) + 257 + n_cp + n_cp / 64 + 1);
     // Without partial slots no list is split and the dK/dV kernel itself
@@ -428,9 +473,9 @@ hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const B
     hipLaunchKernelGGL(inv_scan_kernel, dim3(hp.ZH), dim3(256), lds_scan, st, p, hp.C, hp.CR,
                        hp.pslots == 0 ? 1 : 0, ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
                        ws.zh_base, ws.ticket);
-    size_t lds_fill = sizeof(int) * (p.NBmax + NBH + kRowStage);
-    hipLaunchKernelGGL(inv_fill_kernel, dim3(hp.C, hp.ZH), dim3(64), lds_fill, st, p, hp.CT, hp.C,
-                       block_idx, ws.chunk_pos, ws.tokens);
+    const int nw = fill_waves(hp);
+    hipLaunchKernelGGL(inv_fill_kernel, dim3(hp.C, hp.ZH), dim3(64 * nw), fill_lds_bytes(hp, nw), st,
+                       p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.tokens);
     return hipGetLastError();
 }
 }  // namespace
