@@ -83,16 +83,47 @@ def _copy_value(disp) -> float:
     return vals[-1]
 
 
+def stats_table(path: str, header: str) -> str:
+    """A rocprofv3 kernel_stats.csv as a fixed-width text table (microseconds),
+    kernel names cut before their argument lists."""
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            cut = name.find("(")
+            name = (name[:cut] if cut > 0 else name).replace("void ", "")
+            rows.append((name[:58], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines = [header.rstrip("\n"),
+             f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for n, c, av, mn, mx, pc in rows:
+        lines.append(f"{n:58s} {c:6d} {av:9.1f} {mn:9.1f} {mx:9.1f} {pc:6.2f}")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--kernel", required=True, help="regex of the kernel name (e.g. dq_q_kernel)")
+    ap.add_argument("--stats", help="format this kernel_stats.csv into --out instead (with "
+                                    "--command and --workload in its header)")
+    ap.add_argument("--kernel", help="regex of the kernel name (e.g. dq_q_kernel)")
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--copy-mb", type=int, required=True)
-    ap.add_argument("--fetch", required=True, help="run_counter_collection.csv with FETCH_SIZE")
-    ap.add_argument("--write", required=True, help="run_counter_collection.csv with WRITE_SIZE")
+    ap.add_argument("--copy-mb", type=int)
+    ap.add_argument("--fetch", help="run_counter_collection.csv with FETCH_SIZE")
+    ap.add_argument("--write", help="run_counter_collection.csv with WRITE_SIZE")
     ap.add_argument("--out", required=True)
-    ap.add_argument("--command", default="", help="the profiling commands, recorded in the JSON")
+    ap.add_argument("--command", default="", help="the profiling commands, recorded in the output")
     a = ap.parse_args()
+    if a.stats:
+        head = (f"# rocprofv3 kernel statistics, workload {a.workload}\n"
+                f"# command: {a.command}\n"
+                f"# kernel sources hash: {source_hash()}\n")
+        text = stats_table(a.stats, head)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
+    if not (a.kernel and a.copy_mb and a.fetch and a.write):
+        ap.error("--kernel, --copy-mb, --fetch and --write are needed for a traffic record")
     fd, wd = _per_dispatch(a.fetch, "FETCH_SIZE"), _per_dispatch(a.write, "WRITE_SIZE")
     read_known, write_known = a.copy_mb * 2 ** 20, 2 * a.copy_mb * 2 ** 20
     f_scale = read_known / (_copy_value(fd) * 1024.0)
