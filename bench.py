@@ -212,6 +212,10 @@ def main():
         for j, n in enumerate(names):
             stage_ms[n] += evs[j].elapsed_time(evs[j + 1])
     stage_ms = {n: v / args.steps for n, v in stage_ms.items()}
+    # Whole-step times from the launch stream's events (first to last).
+    per_step = sorted(evs[0].elapsed_time(evs[len(names)]) for evs in events)
+    step_stats = {"median": round(float(np.median(per_step)), 4), "min": round(per_step[0], 4),
+                  "max": round(per_step[-1], 4)}
     ms_step = wall * 1e3 / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"] + stage_ms["dkdv_reduce"]
@@ -274,6 +278,7 @@ def main():
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
         "bwd_frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "step_ms_events": step_stats,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "git": git_sha(),

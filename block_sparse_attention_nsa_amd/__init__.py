@@ -26,6 +26,7 @@ __all__ = [
     "BwdStages",
     "nsa_sel_delta",
     "nsa_sel_invert",
+    "nsa_sel_check_block_idx",
     "bwd_workspace_bytes",
     "make_problem",
     "selection_attn",
@@ -220,6 +221,18 @@ def nsa_sel_invert(q, k, block_idx, block_size, cu_seqlens=None, max_seqlen=None
                             _ptr(ws), ws.numel(), _stream())
     _lib.check("nsa_sel_invert", st)
     return offsets, tokens
+
+
+def nsa_sel_check_block_idx(q, k, block_idx, block_size, cu_seqlens=None, max_seqlen=None):
+    """Entry counts of block_idx (nsa_sel_check_block_idx): a dict with the
+    numbers of padding, out-of-range, future and repeated entries."""
+    p = make_problem(q, k, block_idx, block_size, None, cu_seqlens, max_seqlen)
+    counts = torch.empty(4, dtype=torch.int64, device=block_idx.device)
+    st = _lib.load().nsa_sel_check_block_idx(p, _ptr(block_idx), _ptr(cu_seqlens), _ptr(counts),
+                                             _stream())
+    _lib.check("nsa_sel_check_block_idx", st)
+    c = counts.cpu().tolist()
+    return {"padding": c[0], "out_of_range": c[1], "future": c[2], "repeated": c[3]}
 
 
 class SelectionAttn(torch.autograd.Function):

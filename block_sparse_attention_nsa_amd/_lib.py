@@ -24,6 +24,7 @@ EXPORTS = (
     "nsa_sel_delta",
     "nsa_sel_invert",
     "nsa_sel_invert_tokens_capacity",
+    "nsa_sel_check_block_idx",
     "nsa_status_string",
     "nsa_last_error",
 )
@@ -90,6 +91,8 @@ def load():
     lib.nsa_sel_invert.restype = st
     lib.nsa_sel_invert_tokens_capacity.argtypes = [P]
     lib.nsa_sel_invert_tokens_capacity.restype = sz
+    lib.nsa_sel_check_block_idx.argtypes = [P, ip, ip, vp, vp]
+    lib.nsa_sel_check_block_idx.restype = st
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []

@@ -366,6 +366,22 @@ nsa_status nsa_sel_invert(const nsa_sel_problem* p, const int32_t* block_idx,
     return NSA_OK;
 }
 
+nsa_status nsa_sel_check_block_idx(const nsa_sel_problem* p, const int32_t* block_idx,
+                                   const int32_t* cu_seqlens, uint64_t* counts,
+                                   nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, cu_seqlens));
+    NSA_TRY(check_tensor(block_idx, sizes_of(hp).idx, 4, "block_idx"));
+    NSA_TRY(check_tensor(counts, 4, 8, "counts"));
+    hp.dev.cu = cu_seqlens;
+    NSA_HIP(nsa::launch_check_idx(hp, block_idx, reinterpret_cast<unsigned long long*>(counts),
+                                  reinterpret_cast<hipStream_t>(stream)),
+            "block_idx check launch");
+    return NSA_OK;
+}
+
 nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
                        const void* o, const float* lse, const void* dO,
                        const int32_t* block_idx, const int32_t* cu_seqlens, void* dq, void* dk,

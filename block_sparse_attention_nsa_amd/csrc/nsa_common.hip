@@ -480,6 +480,76 @@ hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const B
 }
 }  // namespace
 
+// ---- block_idx validation -------------------------------------------------
+//
+// counts[0..4) (added to zeros): padding entries (negative), out-of-range
+// entries (>= NB of the row's sequence), future entries (in range, u * bs >
+// t: they add no key), and repeats (each further occurrence of an in-range
+// block the row already lists).  One wave per row, four per workgroup; a
+// row's distinct in-range blocks are counted with the same 16-bit
+// last-writer array as the inversion; per-lane counts, one 64-bit atomic add
+// per wave and counter (integer, so the totals are exact).
+constexpr int kChkWaves = 4, kChkRows = 64;
+
+__global__ __launch_bounds__(64) void zero_counts_kernel(unsigned long long* __restrict__ counts) {
+    if (threadIdx.x < 4) counts[threadIdx.x] = 0ull;
+}
+
+__global__ __launch_bounds__(64 * kChkWaves) void check_idx_kernel(Problem p, const int* __restrict__ idx,
+                                                                   unsigned long long* __restrict__ counts) {
+    extern __shared__ uint16_t lastbuf[];  // [kChkWaves][NBmax]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    volatile uint16_t* last = lastbuf + w * p.NBmax;
+    const int zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
+    const Seq s = seq_of(p, z);
+    const int NBz = (s.len + p.bs - 1) / p.bs;
+    unsigned long long c[4] = {0ull, 0ull, 0ull, 0ull};
+    const int t0 = blockIdx.x * kChkRows, t1 = min(s.len, t0 + kChkRows);
+    for (int t = t0 + w; t < t1; t += kChkWaves) {
+        const int* row = idx_row(p, s, idx, hkv, t);
+        int inr = 0, dist = 0;
+        for (int s0 = 0; s0 < p.S; s0 += 64) {
+            const int si = s0 + lane;
+            if (si >= p.S) continue;
+            const int u = row[si];
+            if (u < 0) {
+                ++c[0];
+            } else if (u >= NBz) {
+                ++c[1];
+            } else {
+                ++inr;
+                if ((int64_t)u * p.bs > t) ++c[2];
+                last[u] = (uint16_t)si;
+            }
+        }
+        for (int s0 = 0; s0 < p.S; s0 += 64) {
+            const int si = s0 + lane;
+            if (si >= p.S) continue;
+            const int u = row[si];
+            if (u >= 0 && u < NBz && last[u] == (uint16_t)si) ++dist;
+        }
+        c[3] += (unsigned long long)(inr - dist);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        unsigned long long x = c[i];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+        if (lane == 0 && x) atomicAdd(&counts[i], x);
+    }
+}
+
+hipError_t launch_check_idx(const HostProblem& hp, const int* block_idx, unsigned long long* counts,
+                            hipStream_t st) {
+    const Problem& p = hp.dev;
+    hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, st, counts);
+    if (hp.ZH == 0 || p.Tmax == 0 || p.S == 0) return hipGetLastError();
+    const dim3 grid((unsigned)((p.Tmax + kChkRows - 1) / kChkRows), (unsigned)hp.ZH);
+    hipLaunchKernelGGL(check_idx_kernel, grid, dim3(64 * kChkWaves),
+                       sizeof(uint16_t) * kChkWaves * (size_t)p.NBmax, st, p, block_idx, counts);
+    return hipGetLastError();
+}
+
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st) {
     const Problem& p = hp.dev;

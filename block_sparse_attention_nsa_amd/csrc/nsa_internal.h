@@ -46,6 +46,10 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
                         hipStream_t st);
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st);
+// Counts of padding / out-of-range / future / repeated block_idx entries
+// (counts[4], zeroed first on the stream).
+hipError_t launch_check_idx(const HostProblem& hp, const int* block_idx, unsigned long long* counts,
+                            hipStream_t st);
 // Delta, the inversion and the dK/dV work plan, as the backward's prepare
 // stage runs them (for bf16 the Delta rows and the inversion counts share one
 // launch; the last scan workgroup writes the plan).

@@ -174,6 +174,20 @@ nsa_status nsa_sel_invert(const nsa_sel_problem* p, const int32_t* block_idx,
                           const int32_t* cu_seqlens, int32_t* offsets, int32_t* tokens,
                           void* workspace, size_t workspace_bytes, nsa_stream_t stream);
 
+/* Validation of a block_idx (optional; the other calls accept any entry).
+ * Writes four counts over all rows of the problem into counts[4] (device
+ * memory, uint64, overwritten): [0] padding entries (negative), [1] entries
+ * out of range (>= NB of the row's sequence), [2] future entries (in range
+ * but starting after the row's token: they add no key), [3] repeats (each
+ * further occurrence of an in-range block the row already lists; the
+ * computation attends such a block once).  These are the readings of page 1's
+ * block lists (padding where S exceeds a row's valid block count) that the
+ * kernels apply; nothing here changes how they treat an entry.  Needs no
+ * workspace; queued on `stream`. */
+nsa_status nsa_sel_check_block_idx(const nsa_sel_problem* p, const int32_t* block_idx,
+                                   const int32_t* cu_seqlens, uint64_t* counts,
+                                   nsa_stream_t stream);
+
 /* Entries the tokens array of nsa_sel_invert must hold: Smin * B * Hkv * T
  * (dense) or Smin * Hkv * T (packed). */
 size_t nsa_sel_invert_tokens_capacity(const nsa_sel_problem* p);

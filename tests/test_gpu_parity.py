@@ -83,6 +83,55 @@ def test_f32_irregular_lists_packed():
     _full_parity(w)
 
 
+def _idx_counts_brute(groups, bs):
+    """Padding, out-of-range, future and repeated entries of block lists,
+    counted row by row in plain Python: groups yields (rows [L, S], L)."""
+    c = [0, 0, 0, 0]
+    for rows, L in groups:
+        nb = -(-L // bs)
+        for t in range(L):
+            seen = set()
+            for u in rows[t].tolist():
+                if u < 0:
+                    c[0] += 1
+                elif u >= nb:
+                    c[1] += 1
+                else:
+                    c[2] += u * bs > t
+                    c[3] += u in seen
+                    seen.add(u)
+    return dict(zip(("padding", "out_of_range", "future", "repeated"), c))
+
+
+def test_check_block_idx_counts_exact():
+    """nsa_sel_check_block_idx against a brute-force count, dense and packed
+    (empty sequence included), on lists with -1 and other negatives anywhere,
+    repeats, out-of-range and future blocks; S > 64 covers several passes of
+    a row.  (f32 problems: they take any block size.)"""
+    rng = np.random.default_rng(21)
+    for B, Hkv, T, bs, S in ((2, 2, 300, 32, 6), (1, 1, 200, 16, 70)):
+        idx = _weird_block_idx(rng, B, Hkv, T, bs, S)
+        w = workloads.make_dense(B, 2 * Hkv, Hkv, T, 32, S, bs, "f32", seed=3, block_idx=idx)
+        d = to_dev(w)
+        got = nsa.nsa_sel_check_block_idx(d["q"], d["k"], d["idx"], bs)
+        want = _idx_counts_brute(((idx[b, h], T) for b in range(B) for h in range(Hkv)), bs)
+        say(f"[check dense B{B} T{T} S{S}] {got}")
+        assert got == want and all(v > 0 for v in want.values())
+    w = workloads.make_thd([90, 0, 130, 7], 4, 2, 32, 5, 16, "f32", "own_random", seed=4,
+                           name="chk-packed")
+    for z in range(4):
+        a, b = w.cu_seqlens[z], w.cu_seqlens[z + 1]
+        if b > a:
+            w.block_idx[:, a:b] = _weird_block_idx(rng, 1, 2, int(b - a), 16, 5)[0]
+    d = to_dev(w)
+    got = nsa.nsa_sel_check_block_idx(d["q"], d["k"], d["idx"], 16, d["cu"], w.max_seqlen)
+    groups = ((w.block_idx[h, w.cu_seqlens[z]:w.cu_seqlens[z + 1]],
+               int(w.cu_seqlens[z + 1] - w.cu_seqlens[z])) for z in range(4) for h in range(2))
+    want = _idx_counts_brute(groups, 16)
+    say(f"[check packed] {got}")
+    assert got == want
+
+
 def test_bf16_packed_small_d64():
     """Packed bf16 at D=64 (page 3's review: a packed backward built for the
     wrong head dimension wrote out of bounds) with ragged lengths."""
