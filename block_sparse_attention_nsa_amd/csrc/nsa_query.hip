@@ -113,8 +113,8 @@ struct WgCoord {
 // at (L - 1 - lw) TW), sequences in index order within a level; workgroups
 // past the last pair are empty and come last.  (Empty workgroups spread
 // through the launch order, one per window past a short sequence's end, were
-// measured to hold back the dispatch of the real ones: config 4 forward
-// 0.618 -> 0.460 ms.)  Each wave computes this alone: lane z holds sequence
+// measured to hold back the dispatch of the real ones: forward on 8 packed
+// sequences of 128-4096 tokens, 32/8 heads, D 128, 0.618 -> 0.460 ms.)  Each wave computes this alone: lane z holds sequence
 // z's first level s_z = L - ceil(len_z / TW), so P(lw) = sum_z max(0, lw -
 // s_z) pairs precede level lw and #{z : s_z <= lw} lie on it; 64 candidate
 // levels are tested per pass, one per lane.  Returns false when b is past

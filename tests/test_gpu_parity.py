@@ -367,7 +367,8 @@ def test_deterministic_bitwise():
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_staged_backward_equals_one_call(cfg):
     """prepare, dq, dkdv_blocks, dkdv_reduce in order equal nsa_sel_bwd bit for
-    bit (config 2 has lists long enough to be split into fp32 partials)."""
+    bit (the T 8192, G 16 workload has lists long enough to be split into fp32
+    partials)."""
     w = workloads.make_config(cfg)
     d = to_dev(w)
     cu = d.get("cu")
