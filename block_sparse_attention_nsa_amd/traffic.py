@@ -40,16 +40,27 @@ KERNEL_SOURCES = {
 }
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and blank-line/indent noise, so that a
+    comment edit does not invalidate a traffic record."""
+    lines = (ln.strip() for ln in _COMMENT.sub("", text).splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_hash(kernel: str = None) -> str:
-    """Hash of the HIP sources a kernel's traffic depends on (all HIP sources
-    and the public header when kernel is None or unknown)."""
+    """Hash of the code (comments stripped) of the HIP sources a kernel's
+    traffic depends on (all HIP sources and the public header when kernel is
+    None or unknown)."""
     h = hashlib.sha256()
     files = KERNEL_SOURCES.get(kernel)
     for d in (os.path.join(HERE, "csrc"), os.path.join(ROOT, "include")):
         for f in sorted(os.listdir(d)):
             if f.endswith((".hip", ".h")) and (files is None or f in files or d.endswith("include")):
-                with open(os.path.join(d, f), "rb") as fh:
-                    h.update(fh.read())
+                with open(os.path.join(d, f), encoding="utf-8", errors="replace") as fh:
+                    h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
