@@ -103,6 +103,8 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
     if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");
     hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
+    hp.pair_possible = p->dtype == NSA_BF16 && hp.pslots == 0 && p->block_size <= 64 &&
+                       (int64_t)p->S * p->block_size >= Tmax && ZH > 0 && NBmax > 0;
     if (nsa::invert_lds_bytes(hp) > 163840)
         return fail(NSA_ERR_UNSUPPORTED, "the block inversion needs %zu bytes of LDS for %lld blocks (max 163840)",
                     nsa::invert_lds_bytes(hp), (long long)NBmax);
@@ -128,7 +130,7 @@ nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
     w.tokens = (int*)take(sizeof(int) * hp.cap);
     w.item_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
     w.pslot_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
-    w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 2 * ZH));
+    w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 3 * ZH + 1));
     w.ticket = (int*)take(sizeof(int));
     w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * hp.dev.bs * hp.dev.D);
     w.bytes = off;

@@ -334,6 +334,13 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     for (int u = threadIdx.x; u <= NB; u += blockDim.x) off[u] = u < NB ? vals[u] : total;
     __syncthreads();
     const int len = seq_of(p, zh / p.Hkv).len;
+    // Whole causal prefixes: a row's listed blocks can only be blocks at or
+    // before its own, so every row lists all of them exactly when every block
+    // u inside the sequence is listed by all len - u bs tokens from u bs on.
+    int short_list = 0;
+    for (int u = threadIdx.x; u < NB; u += blockDim.x)
+        if (u * p.bs < len && off[u + 1] - off[u] != len - u * p.bs) short_list = 1;
+    const int zh_full = !__syncthreads_or(short_list);
     for (int u = threadIdx.x; u < NB; u += blockDim.x) {
         const int rows = (off[u + 1] - off[u]) * p.G;
         const int items = (rows + CR - 1) / CR;
@@ -354,6 +361,7 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     if (threadIdx.x == 0) {
         zh_tot[zh] = ipre[NB];
         zh_tot[gridDim.x + zh] = ppre[NB];
+        zh_tot[2 * gridDim.x + zh] = zh_full;
         __threadfence();
         last = atomicAdd(ticket, 1) == (int)gridDim.x - 1;
     }
@@ -369,6 +377,13 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
         vals[i] = __hip_atomic_load(&zh_tot[ZH + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     block_excl_scan(vals, ZH, zh_base + ZH + 1, scratch);
+    // Every (z, hkv) selects whole causal prefixes: the flag the dK/dV
+    // launches read (zh_base[2 (ZH + 1) + 3 ZH]).
+    int part = 0;
+    for (int i = threadIdx.x; i < ZH; i += blockDim.x)
+        if (!__hip_atomic_load(&zh_tot[2 * ZH + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) part = 1;
+    const int any_short = __syncthreads_or(part);
+    if (threadIdx.x == 0) zh_tot[3 * ZH] = !any_short;
 }
 
 // Stable fill of chunk c of (z, hkv) zh by NW waves.  The chunk's rows are

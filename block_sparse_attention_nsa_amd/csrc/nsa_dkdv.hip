@@ -123,15 +123,21 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // workgroups share a CU and their waves hide each other's latency.
 // The slot is reused every step: the accumulator counts in `freed` when it
 // has read it, and the S wave waits for that count before writing again.
-template <int D, int BS>
+// PAIRED: a launch over pairs of the problem's blocks (BS = 2 block_size
+// keys per workgroup) that runs only when the planner found whole causal
+// prefixes everywhere (then the list of block 2U holds every row that sees a
+// key of block 2U + 1 and the rows it adds see none of them: the causal mask
+// removes those).  pair_on: this is the per-block launch of a problem that
+// also has the paired one, so it runs only when the paired one does not.
+template <int D, int BS, bool PAIRED>
 __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                  const float* __restrict__ lse, const float* __restrict__ delta,
                  const int* __restrict__ offsets, const int* __restrict__ tokens,
                  const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
-                 const int* __restrict__ zh_base, int CR, float* __restrict__ partials,
-                 uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+                 const int* __restrict__ zh_base, int CR, int pair_on,
+                 float* __restrict__ partials, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     using L = RowTile<D>;
     constexpr int NP = BS / 32, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
     constexpr int NJ = (NI + NP - 1) / NP;  // 1 KB row loads per tile for each accumulator (at most)
@@ -147,25 +153,38 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const bool s_wave = w < NP;
     const int a = s_wave ? w : w - NP;
     const int ZH = p.Z * p.Hkv, NB = p.NBmax, G = p.G;
-    const int n_items = zh_base[ZH];
+    const int whole_prefix = pair_on ? zh_base[2 * (ZH + 1) + 3 * ZH] : 0;
+    if (PAIRED ? !whole_prefix : whole_prefix) return;
+    // Paired: NU pairs of blocks per (z, hkv), one item each.
+    const int NU = PAIRED ? (NB + 1) / 2 : NB;
+    const int n_items = PAIRED ? ZH * NU : zh_base[ZH];
     if ((int)blockIdx.x >= n_items) return;
     ItemRef it;
     int li = (!p.packed && ZH % 8 == 0) ? xcd_remap(blockIdx.x, n_items) : (int)blockIdx.x;
-    if (!p.packed && ZH % 8 == 0 && n_items == ZH * NB) {
+    if (!p.packed && ZH % 8 == 0 && n_items == ZH * NU) {
         // One item per block (every list fits one chunk): the XCD's ZH / 8
         // groups are interleaved block-major, so its launch order runs from
         // the longest lists to the shortest once, not once per group.  (A
         // bijection on the items either way.)
         const int gx = ZH / 8, per = n_items / 8;
         const int x = li / per, k = li % per;
-        li = (x * gx + k % gx) * NB + k / gx;
+        li = (x * gx + k % gx) * NU + k / gx;
     }
-    find_item(li, ZH, NB, zh_base, item_pre, it);
+    if constexpr (PAIRED) {
+        it.zh = li / NU;
+        it.u = li - it.zh * NU;
+        it.kitem = 0;
+        it.nitems = 1;
+    } else {
+        find_item(li, ZH, NB, zh_base, item_pre, it);
+    }
     const int z = it.zh / p.Hkv, hkv = it.zh % p.Hkv, u = it.u;
     const Seq s = seq_of(p, z);
+    if (PAIRED && u * BS >= s.len) return;  // pair past a short sequence's end
+    const int lu = PAIRED ? 2 * u : u;      // the list walked: block lu's
     const int* off = offsets + (int64_t)it.zh * (NB + 1);
-    const int* list = tokens + region_base(p, s, hkv) + off[u];
-    const int R = (off[u + 1] - off[u]) * G;
+    const int* list = tokens + region_base(p, s, hkv) + off[lu];
+    const int R = (off[lu + 1] - off[lu]) * G;
     const int f_begin = it.kitem * CR, f_end = min(R, f_begin + CR);
     const int nsteps = (f_end - f_begin + 31) / 32;
     const int kbase = u * BS + 32 * a;
@@ -598,13 +617,21 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
     // by the block kernel: nothing to reduce.
     const unsigned nred = (parts & kDkdvReduce) && hp.pslots > 0 ? (unsigned)(n_blocks * rs) : 0u;
     if (items) {
-        NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
-                          hipLaunchKernelGGL((dkdv_kernel<D, BS>), dim3(items), dim3(BS / 16 * 64), 0,
-                                             st, hp.dev, (const uint16_t*)q, (const uint16_t*)k,
-                                             (const uint16_t*)v, (const uint16_t*)dO, lse, delta,
-                                             ws.offsets, ws.tokens, ws.item_pre, ws.pslot_pre,
-                                             ws.zh_base, hp.CR, ws.partials, (uint16_t*)dk,
-                                             (uint16_t*)dv));
+        const int pair_on = hp.pair_possible ? 1 : 0;
+        auto go = [&](auto kernel, unsigned grid, int threads) {
+            hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, hp.dev, (const uint16_t*)q,
+                               (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse,
+                               delta, ws.offsets, ws.tokens, ws.item_pre, ws.pslot_pre, ws.zh_base,
+                               hp.CR, pair_on, ws.partials, (uint16_t*)dk, (uint16_t*)dv);
+        };
+        if (pair_on) {
+            // The paired launch first (it does the work for whole-prefix
+            // selections); the per-block launch then exits at once.
+            const unsigned pairs = (unsigned)((int64_t)hp.ZH * ((hp.dev.NBmax + 1) / 2));
+            NSA_DISPATCH_D_BS(hp.dev.D, 2 * hp.dev.bs,
+                              go(dkdv_kernel<D, BS, true>, pairs, BS / 16 * 64));
+        }
+        NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false>, items, BS / 16 * 64));
     }
     if (nred) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,

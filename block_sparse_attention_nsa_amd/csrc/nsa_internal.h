@@ -22,6 +22,11 @@ struct HostProblem {
     int64_t cap;    // token-list capacity: Smin * rows of block_idx
     int64_t items_ub;  // upper bound on dK/dV work items
     int64_t pslots;    // fp32 partial slots reserved for split lists
+    // dK/dV may run on pairs of blocks (2 block_size keys per workgroup, one
+    // row list) when every row selects its whole causal prefix; decided on
+    // the device, possible only without partial slots, for block_size <= 64,
+    // bf16, and S * block_size >= the longest sequence.
+    bool pair_possible;
 };
 
 // Backward workspace carve (all offsets 256-byte aligned).
@@ -33,7 +38,8 @@ struct BwdWorkspace {
     int* item_pre;       // [ZH][NBmax + 1]: exclusive prefix of work items per list
     int* pslot_pre;      // [ZH][NBmax + 1]: exclusive prefix of partial slots per list
     int* zh_base;        // [2][ZH + 1]: global prefixes of items and partial slots,
-                         // then [2][ZH]: per-(z, hkv) totals of both
+                         // then [2][ZH]: per-(z, hkv) totals of both, [ZH]: per-(z,
+                         // hkv) whole-prefix flags, [1]: all of them set
     int* ticket;         // [1]: scan workgroups done (the last one plans)
     float* partials;     // [pslots][bs][D][2]
     size_t bytes;

@@ -182,6 +182,36 @@ def test_bf16_whole_prefix_selection(case):
                              seed=15, name=name, block_idx=idx)
     _full_parity(w)
 
+@pytest.mark.parametrize("case", [
+    dict(name="full-G4-D128-bs64", B=2, Hq=8, Hkv=2, T=250, D=128, bs=64),
+    dict(name="full-G3-D64-bs32-odd", B=1, Hq=6, Hkv=2, T=330, D=64, bs=32),
+    dict(name="full-G2-D128-bs64-odd", B=1, Hq=4, Hkv=2, T=400, D=128, bs=64),
+    dict(name="full-G16-D32-bs64-one", B=1, Hq=16, Hkv=1, T=60, D=32, bs=64),
+])
+def test_bf16_full_prefix_pairs(case):
+    """Every row lists every block up to its own (dense causal, -1 beyond) and
+    every list fits one work item (T * G <= 1024 here): the dK/dV stage runs
+    on pairs of blocks.  Ragged T, an odd number of blocks (the last pair
+    holds one block), a single block, and the same problem with one entry
+    removed (not a whole prefix any more: the per-block launch runs)."""
+    c = dict(case)
+    name = c.pop("name")
+    B, Hkv, T, bs = c["B"], c["Hkv"], c["T"], c["bs"]
+    NB = -(-T // bs)
+    S = NB
+    t = np.arange(T)
+    idx = np.where(np.arange(S)[None, :] <= (t // bs)[:, None], np.arange(S)[None, :], -1)
+    idx = np.broadcast_to(idx, (B, Hkv, T, S)).astype(np.int32).copy()
+    w = workloads.make_dense(B, c["Hq"], Hkv, T, c["D"], S, bs, "bf16", seed=16, name=name,
+                             block_idx=idx)
+    _full_parity(w)
+    idx2 = idx.copy()
+    idx2[0, 0, T - 1, 0] = -1  # the last token no longer lists block 0
+    w2 = workloads.make_dense(B, c["Hq"], Hkv, T, c["D"], S, bs, "bf16", seed=16,
+                              name=name + "-holed", block_idx=idx2)
+    _full_parity(w2)
+
+
 # ---- full-size configurations: sampled outputs + invariants ---------------
 
 def _sampled_parity(w, out, rng, n_rows=48, blocks=None):
