@@ -79,10 +79,20 @@ def _per_dispatch(path: str, counter: str):
 
 
 def _kernel_mean(disp, pattern: str) -> float:
-    vals = [v for _, n, v in disp if re.search(pattern, n)]
-    if not vals:
+    """KiB per launch of the stage the pattern names.  A stage may launch
+    more than one instantiation per step (dK/dV on whole-prefix selections:
+    the paired kernel and the per-block one, which then exits at once), so
+    this is the total over all matching dispatches divided by the number of
+    steps (the dispatch count of each instantiation)."""
+    per_name = {}
+    for _, n, v in disp:
+        if re.search(pattern, n):
+            c, t = per_name.get(n, (0, 0.0))
+            per_name[n] = (c + 1, t + v)
+    if not per_name:
         raise SystemExit(f"no dispatch of {pattern!r} in the counter file")
-    return sum(vals) / len(vals)
+    steps = max(c for c, _ in per_name.values())
+    return sum(t for _, t in per_name.values()) / steps
 
 
 def _copy_value(disp) -> float:
