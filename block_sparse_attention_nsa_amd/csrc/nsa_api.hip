@@ -132,6 +132,7 @@ nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
     w.pslot_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
     w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 3 * ZH + 1));
     w.ticket = (int*)take(sizeof(int));
+    w.iota = (int*)take(hp.pair_possible ? sizeof(int) * hp.dev.Tmax : 0);
     w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * hp.dev.bs * hp.dev.D);
     w.bytes = off;
     return w;

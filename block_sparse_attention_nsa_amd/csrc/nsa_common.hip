@@ -395,10 +395,23 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
 // becomes the first position of wave w's entries of block u), and each wave
 // appends its tokens, ascending, at those positions.  So every list is
 // ascending in t, exactly as one wave walking the whole chunk would write it.
+// whole: the whole-prefix flag the scan wrote (null when the lists are
+// always wanted).  When it is set the backward needs no lists (every list of
+// block u is the tokens u bs .. len - 1, read from iota[u bs ..] instead):
+// the workgroups of (z, hkv) 0 write iota[t] = t for their chunk and return.
 __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
                                                        const int* __restrict__ idx,
                                                        const int* __restrict__ chunk_pos,
-                                                       int* __restrict__ tokens) {
+                                                       int* __restrict__ tokens,
+                                                       const int* __restrict__ whole,
+                                                       int* __restrict__ iota) {
+    if (whole && *whole) {
+        if (blockIdx.y == 0)
+            for (int t = blockIdx.x * CT + (int)threadIdx.x; t < min(p.Tmax, (int)(blockIdx.x + 1) * CT);
+                 t += blockDim.x)
+                iota[t] = t;
+        return;
+    }
     extern __shared__ int sm[];
     const int NB = p.NBmax, NBH = (NB + 1) / 2, NW = (int)blockDim.x >> 6;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -479,7 +492,7 @@ size_t count_lds_bytes(const Problem& p) {
 
 // Scan and stable fill (after the counts are in chunk_pos).
 hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
-                            hipStream_t st) {
+                            hipStream_t st, bool lists_optional) {
     const Problem& p = hp.dev;
     const int64_t n_cp = (int64_t)p.NBmax * hp.C;  // <= 2^14 + NBmax by the choice of CT
     size_t lds_scan = sizeof(int) * (std::max(p.NBmax, hp.ZH) + 257 + n_cp + n_cp / 64 + 1);
@@ -489,8 +502,10 @@ hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const B
                        hp.pslots == 0 ? 1 : 0, ws.chunk_pos, ws.offsets, ws.item_pre, ws.pslot_pre,
                        ws.zh_base, ws.ticket);
     const int nw = fill_waves(hp);
+    const bool skip = lists_optional && hp.pair_possible;
     hipLaunchKernelGGL(inv_fill_kernel, dim3(hp.C, hp.ZH), dim3(64 * nw), fill_lds_bytes(hp, nw), st,
-                       p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.tokens);
+                       p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.tokens,
+                       skip ? ws.zh_base + 2 * (hp.ZH + 1) + 3 * hp.ZH : nullptr, ws.iota);
     return hipGetLastError();
 }
 }  // namespace
@@ -571,7 +586,7 @@ hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdW
     if (hp.ZH == 0 || hp.C == 0) return hipSuccess;
     hipLaunchKernelGGL(inv_count_kernel, dim3(hp.C, hp.ZH), dim3(64 * kInvWaves), count_lds_bytes(p),
                        st, p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.ticket);
-    return launch_scan_fill(hp, block_idx, ws, st);
+    return launch_scan_fill(hp, block_idx, ws, st, false);
 }
 
 hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, const int* block_idx,
@@ -597,7 +612,9 @@ hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, 
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_scan_fill(hp, block_idx, ws, st);
+    // The backward reads lists only through the dK/dV launches, which take
+    // them from iota when the selection is a whole prefix everywhere.
+    return launch_scan_fill(hp, block_idx, ws, st, true);
 }
 
 

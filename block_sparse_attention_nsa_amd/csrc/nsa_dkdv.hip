@@ -136,7 +136,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  const float* __restrict__ lse, const float* __restrict__ delta,
                  const int* __restrict__ offsets, const int* __restrict__ tokens,
                  const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
-                 const int* __restrict__ zh_base, int CR, int pair_on,
+                 const int* __restrict__ zh_base, const int* __restrict__ iota, int CR, int pair_on,
                  float* __restrict__ partials, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
     using L = RowTile<D>;
     constexpr int NP = BS / 32, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
@@ -183,7 +183,8 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     if (PAIRED && u * BS >= s.len) return;  // pair past a short sequence's end
     const int lu = PAIRED ? 2 * u : u;      // the list walked: block lu's
     const int* off = offsets + (int64_t)it.zh * (NB + 1);
-    const int* list = tokens + region_base(p, s, hkv) + off[lu];
+    // Paired (whole prefixes): block lu's list is the tokens lu bs .. len - 1.
+    const int* list = PAIRED ? iota + lu * p.bs : tokens + region_base(p, s, hkv) + off[lu];
     const int R = (off[lu + 1] - off[lu]) * G;
     const int f_begin = it.kitem * CR, f_end = min(R, f_begin + CR);
     const int nsteps = (f_end - f_begin + 31) / 32;
@@ -622,7 +623,7 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, hp.dev, (const uint16_t*)q,
                                (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse,
                                delta, ws.offsets, ws.tokens, ws.item_pre, ws.pslot_pre, ws.zh_base,
-                               hp.CR, pair_on, ws.partials, (uint16_t*)dk, (uint16_t*)dv);
+                               ws.iota, hp.CR, pair_on, ws.partials, (uint16_t*)dk, (uint16_t*)dv);
         };
         if (pair_on) {
             // The paired launch first (it does the work for whole-prefix

@@ -41,6 +41,8 @@ struct BwdWorkspace {
                          // then [2][ZH]: per-(z, hkv) totals of both, [ZH]: per-(z,
                          // hkv) whole-prefix flags, [1]: all of them set
     int* ticket;         // [1]: scan workgroups done (the last one plans)
+    int* iota;           // [Tmax] (pair_possible): iota[t] = t, the lists of a
+                         // whole-prefix selection
     float* partials;     // [pslots][bs][D][2]
     size_t bytes;
 };
