@@ -16,7 +16,11 @@ Where the method's source pages are silent the oracle takes these readings:
     listed twice counts once); negative or >= NB entries are skipped;
   * causality applies to every listed block (key j <= query t), so a listed
     future block adds nothing; an empty row gives o = 0, lse = -inf, dq = 0;
-  * scale defaults to 1/sqrt(D); lse is natural-log and includes the scale.
+  * scale defaults to 1/sqrt(D); lse is natural-log and includes the scale;
+  * an optional attention sink (page 3 names a dSink backward step, nothing
+    more): a per-head logit, no scale, in every row's softmax denominator
+    with no value; lse includes it, dq/dk/dv keep their formulas with that
+    lse, and dsink[h] = -sum over head h's rows of exp(sink[h] - lse) Delta.
 """
 from __future__ import annotations
 
@@ -55,7 +59,7 @@ def _load():
     ip = ctypes.POINTER(ctypes.c_int32)
     lp = ctypes.POINTER(ctypes.c_int64)
     i, d, i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
-    shape = [i, i, i, i, i, i, i, d]
+    shape = [i, i, i, i, i, i, i, d, dp]
     lib.nsa_oracle_fwd_rows.argtypes = shape + [dp, dp, dp, ip, i64, lp, dp, dp]
     lib.nsa_oracle_bwd_rows.argtypes = shape + [dp, dp, dp, dp, ip, i64, lp, dp, dp, dp]
     lib.nsa_oracle_dkdv_keys.argtypes = shape + [dp, dp, dp, dp, ip, dp, dp, i64, lp, dp, dp]
@@ -84,7 +88,9 @@ def _ptr(a: np.ndarray, ct):
     return a.ctypes.data_as(ctypes.POINTER(ct))
 
 
-def _shape(q, k, idx, block_size, scale):
+def _shape(q, k, idx, block_size, scale, sink=None):
+    """The C shape arguments; sink (per-head logits) is passed as a pointer
+    to a float64 copy that the returned tuple keeps alive."""
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     S = idx.shape[-1]
@@ -92,14 +98,26 @@ def _shape(q, k, idx, block_size, scale):
         scale = D ** -0.5
     if k.shape != (B, Hkv, T, D) or idx.shape != (B, Hkv, T, S) or Hq % Hkv:
         raise ValueError("inconsistent shapes")
-    return (B, Hq, Hkv, T, D, S, int(block_size), float(scale))
+    sk = None if sink is None else _f64(sink).reshape(-1)
+    if sk is not None and sk.shape != (Hq,):
+        raise ValueError("sink must hold one logit per query head")
+    ptr = None if sk is None else _ptr(sk, ctypes.c_double)
+    return _Shape((B, Hq, Hkv, T, D, S, int(block_size), float(scale), ptr), sk)
 
 
-def fwd_rows(q, k, v, block_idx, block_size, rows=None, scale=None):
+class _Shape(tuple):
+    """Shape arguments plus the sink array they point into."""
+    def __new__(cls, args, keep):
+        t = super().__new__(cls, args)
+        t.keep = keep
+        return t
+
+
+def fwd_rows(q, k, v, block_idx, block_size, rows=None, scale=None, sink=None):
     """Forward of the listed flat rows ((b*Hq + h)*T + t); all rows if None.
     Returns (o [n, D], lse [n])."""
     q, k, v, idx = _f64(q), _f64(k), _f64(v), _i32(block_idx)
-    sh = _shape(q, k, idx, block_size, scale)
+    sh = _shape(q, k, idx, block_size, scale, sink)
     n = q.shape[0] * q.shape[1] * q.shape[2] if rows is None else len(rows)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     o = np.zeros((n, sh[4]))
@@ -113,10 +131,11 @@ def fwd_rows(q, k, v, block_idx, block_size, rows=None, scale=None):
     return o, lse
 
 
-def bwd_rows(q, k, v, dO, block_idx, block_size, rows=None, scale=None, want_dq=True):
+def bwd_rows(q, k, v, dO, block_idx, block_size, rows=None, scale=None, want_dq=True,
+             sink=None):
     """lse, Delta and dq of the listed rows.  Returns (lse [n], delta [n], dq [n, D])."""
     q, k, v, dO, idx = _f64(q), _f64(k), _f64(v), _f64(dO), _i32(block_idx)
-    sh = _shape(q, k, idx, block_size, scale)
+    sh = _shape(q, k, idx, block_size, scale, sink)
     n = q.shape[0] * q.shape[1] * q.shape[2] if rows is None else len(rows)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     lse, delta = np.zeros(n), np.zeros(n)
@@ -152,21 +171,36 @@ def dkdv_keys(q, k, v, dO, block_idx, block_size, row_lse, row_delta, keys=None,
     return dk, dv
 
 
-def fwd(q, k, v, block_idx, block_size, scale=None):
-    """Dense forward: o like q, lse [B, Hq, T]."""
+def fwd(q, k, v, block_idx, block_size, scale=None, sink=None):
+    """Dense forward: o like q, lse [B, Hq, T] (sink: optional [Hq] logits)."""
     B, Hq, T, D = np.shape(q)
-    o, lse = fwd_rows(q, k, v, block_idx, block_size, None, scale)
+    o, lse = fwd_rows(q, k, v, block_idx, block_size, None, scale, sink)
     return o.reshape(B, Hq, T, D), lse.reshape(B, Hq, T)
 
 
-def bwd(q, k, v, dO, block_idx, block_size, scale=None):
-    """Dense backward: (dq, dk, dv, lse, delta)."""
+def bwd(q, k, v, dO, block_idx, block_size, scale=None, sink=None):
+    """Dense backward: (dq, dk, dv, lse, delta); lse includes the sink if any."""
     B, Hq, T, D = np.shape(q)
     Hkv = np.shape(k)[1]
-    lse, delta, dq = bwd_rows(q, k, v, dO, block_idx, block_size, None, scale)
+    lse, delta, dq = bwd_rows(q, k, v, dO, block_idx, block_size, None, scale, sink=sink)
     dk, dv = dkdv_keys(q, k, v, dO, block_idx, block_size, lse, delta, None, scale)
     return (dq.reshape(B, Hq, T, D), dk.reshape(B, Hkv, T, D), dv.reshape(B, Hkv, T, D),
             lse.reshape(B, Hq, T), delta.reshape(B, Hq, T))
+
+
+def dsink(sink, lse, delta, head_axis: int):
+    """Gradient of the per-head sink logits: dsink[h] = -sum over the rows of
+    head h of exp(sink[h] - lse) * Delta (o moves by -P_sink * o when the sink
+    logit grows, so <dO, do> = -P_sink <dO, o> = -P_sink Delta).  lse/delta:
+    the backward's row arrays; head_axis: their query-head axis (1 for dense
+    [B, Hq, T], 0 for packed [Hq, Ttot])."""
+    sk = _f64(sink).reshape(-1)
+    lse, delta = _f64(lse), _f64(delta)
+    shp = [1] * lse.ndim
+    shp[head_axis] = -1
+    p_sink = np.exp(sk.reshape(shp) - lse)
+    axes = tuple(a for a in range(lse.ndim) if a != head_axis)
+    return -(p_sink * delta).sum(axis=axes)
 
 
 def invert(block_idx, block_size) -> Tuple[np.ndarray, np.ndarray]:
@@ -201,7 +235,7 @@ def _seq(x_thd: np.ndarray, a: int, b: int) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x_thd)[a:b].transpose(1, 0, 2))[None]
 
 
-def fwd_thd(q, k, v, block_idx, cu_seqlens, block_size, scale=None):
+def fwd_thd(q, k, v, block_idx, cu_seqlens, block_size, scale=None, sink=None):
     """Packed forward: q [Ttot,Hq,D], k/v [Ttot,Hkv,D], block_idx [Hkv,Ttot,S].
     Returns (o [Ttot,Hq,D], lse [Hq,Ttot])."""
     Ttot, Hq, D = np.shape(q)
@@ -212,13 +246,13 @@ def fwd_thd(q, k, v, block_idx, cu_seqlens, block_size, scale=None):
         if b == a:
             continue
         oz, lz = fwd(_seq(q, a, b), _seq(k, a, b), _seq(v, a, b),
-                     np.asarray(block_idx)[:, a:b][None], block_size, scale)
+                     np.asarray(block_idx)[:, a:b][None], block_size, scale, sink)
         o[a:b] = oz[0].transpose(1, 0, 2)
         lse[:, a:b] = lz[0]
     return o, lse
 
 
-def bwd_thd(q, k, v, dO, block_idx, cu_seqlens, block_size, scale=None):
+def bwd_thd(q, k, v, dO, block_idx, cu_seqlens, block_size, scale=None, sink=None):
     """Packed backward: (dq, dk, dv) in the packed layouts, plus lse, delta [Hq,Ttot]."""
     Ttot, Hq, D = np.shape(q)
     Hkv = np.shape(k)[1]
@@ -229,7 +263,7 @@ def bwd_thd(q, k, v, dO, block_idx, cu_seqlens, block_size, scale=None):
         if b == a:
             continue
         r = bwd(_seq(q, a, b), _seq(k, a, b), _seq(v, a, b), _seq(dO, a, b),
-                np.asarray(block_idx)[:, a:b][None], block_size, scale)
+                np.asarray(block_idx)[:, a:b][None], block_size, scale, sink)
         dq[a:b] = r[0][0].transpose(1, 0, 2)
         dk[a:b] = r[1][0].transpose(1, 0, 2)
         dv[a:b] = r[2][0].transpose(1, 0, 2)

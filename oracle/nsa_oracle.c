@@ -24,6 +24,15 @@
  *   dv_j =       sum_{rows r with j in A(r)} P_{r,j} dO_r
  * with hkv = floor(h / G) and an empty A giving o = 0, lse = -inf, dq = 0.
  *
+ * Optional attention sink (page 3 names a dSink step of the backward chain
+ * without defining it; the reading taken): a per-head logit sink[h], no
+ * scale applied, that joins every row's softmax denominator with no value
+ * vector, lse = log(sum_{j in A} exp(s_j) + exp(sink[h])).  P_j, o, Delta,
+ * dS and the dq/dk/dv sums keep the formulas above with this lse (an empty
+ * A then gives lse = sink[h]); the sink's own gradient, summed over the
+ * rows of head h, is -sum_rows exp(sink[h] - lse) Delta (computed in
+ * oracle/__init__.py).  sink == NULL means no sink.
+ *
  * Layout (dense, contiguous, row-major): q, o, dO, dq [B][Hq][T][D];
  * k, v, dk, dv [B][Hkv][T][D]; block_idx [B][Hkv][T][S] int32; lse, delta
  * [B][Hq][T].  Packed variable-length batches are handled by the Python side
@@ -44,6 +53,7 @@
 typedef struct {
     int B, Hq, Hkv, T, D, S, bs;
     double scale;
+    const double* sink; /* [Hq] or NULL */
 } shape_t;
 
 static int n_blocks(const shape_t* sh) { return (sh->T + sh->bs - 1) / sh->bs; }
@@ -85,17 +95,19 @@ static int selected_keys(const shape_t* sh, const int32_t* row, int t, int* keys
     return n;
 }
 
-/* Softmax of one row over its selected keys.  Writes P (n values) and
- * returns lse (-inf when the row has no key). */
-static double row_softmax(const shape_t* sh, const double* q_r, const double* K, const int* keys,
-                          int n, double* P) {
-    if (n == 0) return -INFINITY;
-    double m = -INFINITY;
+/* Softmax of one row of head h over its selected keys (and the head's sink
+ * logit, if any).  Writes P (n values) and returns lse (-inf when the row
+ * has no key and there is no sink). */
+static double row_softmax(const shape_t* sh, int h, const double* q_r, const double* K,
+                          const int* keys, int n, double* P) {
+    const double sk = sh->sink ? sh->sink[h] : -INFINITY;
+    if (n == 0) return sk;
+    double m = sk;
     for (int a = 0; a < n; ++a) {
         P[a] = sh->scale * dot(q_r, K + (int64_t)keys[a] * sh->D, sh->D);
         if (P[a] > m) m = P[a];
     }
-    double sum = 0.0;
+    double sum = sh->sink ? exp(sk - m) : 0.0;
     for (int a = 0; a < n; ++a) sum += exp(P[a] - m);
     double lse = m + log(sum);
     for (int a = 0; a < n; ++a) P[a] = exp(P[a] - lse);
@@ -110,7 +122,7 @@ static void fwd_row(const shape_t* sh, const double* q, const double* k, const d
     const double* K = krow(sh, k, b, hkv, 0);
     const double* V = krow(sh, v, b, hkv, 0);
     int n = selected_keys(sh, idx_row(sh, idx, b, hkv, t), t, keys);
-    double lse = row_softmax(sh, qrow(sh, q, b, h, t), K, keys, n, P);
+    double lse = row_softmax(sh, h, qrow(sh, q, b, h, t), K, keys, n, P);
     for (int d = 0; d < D; ++d) o_out[d] = 0.0;
     for (int a = 0; a < n; ++a) {
         const double* vj = V + (int64_t)keys[a] * D;
@@ -128,7 +140,7 @@ static void bwd_row(const shape_t* sh, const double* q, const double* k, const d
     const double* V = krow(sh, v, b, hkv, 0);
     const double* do_r = qrow(sh, dO, b, h, t);
     int n = selected_keys(sh, idx_row(sh, idx, b, hkv, t), t, keys);
-    double lse = row_softmax(sh, qrow(sh, q, b, h, t), K, keys, n, P);
+    double lse = row_softmax(sh, h, qrow(sh, q, b, h, t), K, keys, n, P);
     double delta = 0.0;
     for (int a = 0; a < n; ++a) {
         dP[a] = dot(do_r, V + (int64_t)keys[a] * D, D);
@@ -179,8 +191,8 @@ static int shape_ok(const shape_t* sh) {
     return 1;
 }
 
-#define SHAPE_ARGS int B, int Hq, int Hkv, int T, int D, int S, int bs, double scale
-#define MAKE_SHAPE shape_t sh = {B, Hq, Hkv, T, D, S, bs, scale}
+#define SHAPE_ARGS int B, int Hq, int Hkv, int T, int D, int S, int bs, double scale, const double* sink
+#define MAKE_SHAPE shape_t sh = {B, Hq, Hkv, T, D, S, bs, scale, sink}
 
 int nsa_oracle_num_threads(void) {
 #ifdef _OPENMP
@@ -269,7 +281,7 @@ int nsa_oracle_dkdv_keys(SHAPE_ARGS, const double* q, const double* k, const dou
 /* Full forward: o [B][Hq][T][D], lse [B][Hq][T]. */
 int nsa_oracle_fwd(SHAPE_ARGS, const double* q, const double* k, const double* v,
                    const int32_t* idx, double* o, double* lse) {
-    return nsa_oracle_fwd_rows(B, Hq, Hkv, T, D, S, bs, scale, q, k, v, idx,
+    return nsa_oracle_fwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, q, k, v, idx,
                                (int64_t)B * Hq * T, NULL, o, lse);
 }
 
@@ -278,10 +290,10 @@ int nsa_oracle_fwd(SHAPE_ARGS, const double* q, const double* k, const double* v
 int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v,
                    const double* dO, const int32_t* idx, double* dq, double* dk, double* dv,
                    double* lse, double* delta) {
-    int rc = nsa_oracle_bwd_rows(B, Hq, Hkv, T, D, S, bs, scale, q, k, v, dO, idx,
+    int rc = nsa_oracle_bwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, q, k, v, dO, idx,
                                  (int64_t)B * Hq * T, NULL, lse, delta, dq);
     if (rc) return rc;
-    return nsa_oracle_dkdv_keys(B, Hq, Hkv, T, D, S, bs, scale, q, k, v, dO, idx, lse, delta,
+    return nsa_oracle_dkdv_keys(B, Hq, Hkv, T, D, S, bs, scale, sink, q, k, v, dO, idx, lse, delta,
                                 (int64_t)B * Hkv * T, NULL, dk, dv);
 }
 
@@ -294,7 +306,7 @@ int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v
  * too small. */
 int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* idx,
                           int32_t* counts, int32_t* tokens, int64_t cap) {
-    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0};
+    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL};
     int NB = n_blocks(&sh);
     int64_t n = 0;
     for (int b = 0; b < B; ++b)
@@ -314,7 +326,7 @@ int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* i
 
 /* Number of useful (query-head row, key) pairs: sum over rows of |A|. */
 int64_t nsa_oracle_count_pairs(int B, int Hq, int Hkv, int T, int S, int bs, const int32_t* idx) {
-    shape_t sh = {B, Hq, Hkv, T, 1, S, bs, 1.0};
+    shape_t sh = {B, Hq, Hkv, T, 1, S, bs, 1.0, NULL};
     if (!shape_ok(&sh)) return -1;
     int G = Hq / Hkv;
     int* keys = (int*)malloc(sizeof(int) * (size_t)S * bs);

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_pins as pins
+import test_oracle_sink as sink_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "nsa_oracle.c")
 
@@ -32,6 +33,8 @@ MUTANTS = {
     "no scale in scores": ("P[a] = sh->scale * dot(q_r,", "P[a] = dot(q_r,"),
     "o uses k": ("const double* V = krow(sh, v, b, hkv, 0);\n    int n = selected_keys",
                  "const double* V = krow(sh, k, b, hkv, 0);\n    int n = selected_keys"),
+    "sink left out of the sum": ("double sum = sh->sink ? exp(sk - m) : 0.0;", "double sum = 0.0;"),
+    "sink ignored on empty rows": ("if (n == 0) return sk;", "if (n == 0) return -INFINITY;"),
 }
 
 
@@ -59,6 +62,9 @@ CHECKS = [
     lambda: pins.test_gqa_equals_sum_over_heads(),
     lambda: pins.test_closed_forms(),
     lambda: pins.test_rows_sum_to_one_and_invariants(),
+    lambda: sink_pins.test_sink_finite_differences(pins.TINY[0]),
+    lambda: sink_pins.test_sink_dense_autograd(21, 2, 4, 2, 40, 8, 4, 5),
+    lambda: sink_pins.test_sink_closed_forms_and_empty_rows(),
 ]
 
 
