@@ -101,16 +101,28 @@ def _lse_shape(q, cu_seqlens):
     return tuple(q.shape[:3]) if cu_seqlens is None else (q.shape[1], q.shape[0])
 
 
+def _check_sink(sink, p: _lib.Problem):
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() != p.Hq:
+        raise ValueError("sink must be a contiguous float32 tensor of Hq logits")
+
+
 def nsa_sel_fwd(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None,
-                out=None, lse=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """o, lse = forward (nsa_sel_fwd)."""
+                out=None, lse=None, sink=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """o, lse = forward (nsa_sel_fwd; nsa_sel_fwd_sink with per-head sink logits)."""
     p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty(_lse_shape(q, cu_seqlens), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = _lib.load().nsa_sel_fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(cu_seqlens),
-                                 _ptr(o), _ptr(lse_t), _stream())
-    _lib.check("nsa_sel_fwd", st)
+    lib = _lib.load()
+    if sink is None:
+        st = lib.nsa_sel_fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(cu_seqlens),
+                             _ptr(o), _ptr(lse_t), _stream())
+        _lib.check("nsa_sel_fwd", st)
+    else:
+        _check_sink(sink, p)
+        st = lib.nsa_sel_fwd_sink(p, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(cu_seqlens),
+                                  _ptr(sink), _ptr(o), _ptr(lse_t), _stream())
+        _lib.check("nsa_sel_fwd_sink", st)
     return o, lse_t
 
 
@@ -123,8 +135,10 @@ def bwd_workspace_bytes(p: _lib.Problem) -> int:
 
 
 def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqlens=None,
-                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None):
-    """dq, dk, dv = backward (nsa_sel_bwd)."""
+                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None, sink=None):
+    """dq, dk, dv = backward (nsa_sel_bwd); with sink logits (lse from the
+    sink forward) also dsink, from nsa_sel_bwd_dsink on the same workspace:
+    dq, dk, dv, dsink."""
     p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     for name, t in (("o", o), ("dO", dO)):
@@ -143,7 +157,14 @@ def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqle
                                  _ptr(block_idx), _ptr(cu_seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(ws), ws.numel(), _stream())
     _lib.check("nsa_sel_bwd", st)
-    return dq, dk, dv
+    if sink is None:
+        return dq, dk, dv
+    _check_sink(sink, p)
+    dsink = torch.empty_like(sink)
+    st = _lib.load().nsa_sel_bwd_dsink(p, _ptr(lse), _ptr(sink), _ptr(cu_seqlens), _ptr(dsink),
+                                       _ptr(ws), ws.numel(), _stream())
+    _lib.check("nsa_sel_bwd_dsink", st)
+    return dq, dk, dv, dsink
 
 
 class BwdStages:
@@ -239,21 +260,25 @@ class SelectionAttn(torch.autograd.Function):
     """o = selection attention; backward through nsa_sel_bwd."""
 
     @staticmethod
-    def forward(ctx, q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen):
-        o, lse = nsa_sel_fwd(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen)
-        ctx.save_for_backward(q, k, v, o, lse, block_idx, cu_seqlens)
+    def forward(ctx, q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen, sink=None):
+        o, lse = nsa_sel_fwd(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen,
+                             sink=sink)
+        ctx.save_for_backward(q, k, v, o, lse, block_idx, cu_seqlens, sink)
         ctx.cfg = (block_size, scale, max_seqlen)
         return o
 
     @staticmethod
     def backward(ctx, dO):
-        q, k, v, o, lse, block_idx, cu_seqlens = ctx.saved_tensors
+        q, k, v, o, lse, block_idx, cu_seqlens, sink = ctx.saved_tensors
         block_size, scale, max_seqlen = ctx.cfg
-        dq, dk, dv = nsa_sel_bwd(q, k, v, o, lse, dO.contiguous(), block_idx, block_size, scale,
-                                 cu_seqlens, max_seqlen)
-        return dq, dk, dv, None, None, None, None, None
+        g = nsa_sel_bwd(q, k, v, o, lse, dO.contiguous(), block_idx, block_size, scale,
+                        cu_seqlens, max_seqlen, sink=sink)
+        dsink = g[3] if sink is not None else None
+        return g[0], g[1], g[2], None, None, None, None, None, dsink
 
 
-def selection_attn(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None):
-    """Differentiable NSA selection attention (page 1's selection_attn call)."""
-    return SelectionAttn.apply(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+def selection_attn(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None,
+                   sink=None):
+    """Differentiable NSA selection attention (page 1's selection_attn call);
+    sink: optional per-head sink logits [Hq] float32 (differentiable)."""
+    return SelectionAttn.apply(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen, sink)

@@ -25,6 +25,8 @@ EXPORTS = (
     "nsa_sel_invert",
     "nsa_sel_invert_tokens_capacity",
     "nsa_sel_check_block_idx",
+    "nsa_sel_fwd_sink",
+    "nsa_sel_bwd_dsink",
     "nsa_status_string",
     "nsa_last_error",
 )
@@ -93,6 +95,10 @@ def load():
     lib.nsa_sel_invert_tokens_capacity.restype = sz
     lib.nsa_sel_check_block_idx.argtypes = [P, ip, ip, vp, vp]
     lib.nsa_sel_check_block_idx.restype = st
+    lib.nsa_sel_fwd_sink.argtypes = [P, vp, vp, vp, ip, ip, fp, vp, fp, vp]
+    lib.nsa_sel_fwd_sink.restype = st
+    lib.nsa_sel_bwd_dsink.argtypes = [P, fp, fp, ip, fp, vp, sz, vp]
+    lib.nsa_sel_bwd_dsink.restype = st
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []

@@ -84,6 +84,7 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     d.B = p->B; d.T = p->T; d.Hq = p->Hq; d.Hkv = p->Hkv; d.G = G; d.D = p->D; d.S = p->S;
     d.bs = p->block_size; d.Z = Z; d.packed = packed ? 1 : 0; d.Tmax = Tmax; d.NBmax = (int)NBmax;
     d.Smin = (int)Smin; d.scale = p->scale; d.scale_log2 = p->scale * nsa::kLog2e; d.cu = nullptr;
+    d.sink = nullptr;
     hp.dtype = p->dtype;
     hp.ZH = (int)ZH;
     // Inversion chunks of CT tokens: small (16) for short sequences, growing
@@ -275,10 +276,18 @@ const char* nsa_last_error(void) { return g_last_error.c_str(); }
 nsa_status nsa_sel_fwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
                        const int32_t* block_idx, const int32_t* cu_seqlens, void* o, float* lse,
                        nsa_stream_t stream) {
+    return nsa_sel_fwd_sink(p, q, k, v, block_idx, cu_seqlens, nullptr, o, lse, stream);
+}
+
+nsa_status nsa_sel_fwd_sink(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                            const int32_t* block_idx, const int32_t* cu_seqlens, const float* sink,
+                            void* o, float* lse, nsa_stream_t stream) {
     g_last_error.clear();
     nsa::HostProblem hp;
     NSA_TRY(make_problem(p, hp));
     NSA_TRY(check_cu(hp, cu_seqlens));
+    if (sink) NSA_TRY(check_tensor(sink, hp.dev.Hq, 4, "sink"));
+    hp.dev.sink = sink;
     const Sizes sz = sizes_of(hp);
     const size_t a = elem_align(hp);
     NSA_TRY(check_tensor(q, sz.q, a, "q"));
@@ -366,6 +375,28 @@ nsa_status nsa_sel_invert(const nsa_sel_problem* p, const int32_t* block_idx,
     NSA_HIP(hipMemcpyAsync(offsets, ws.offsets, sizeof(int) * n_off, hipMemcpyDeviceToDevice, st), "offsets copy");
     if (hp.cap)
         NSA_HIP(hipMemcpyAsync(tokens, ws.tokens, sizeof(int) * hp.cap, hipMemcpyDeviceToDevice, st), "tokens copy");
+    return NSA_OK;
+}
+
+nsa_status nsa_sel_bwd_dsink(const nsa_sel_problem* p, const float* lse, const float* sink,
+                             const int32_t* cu_seqlens, float* dsink, void* workspace,
+                             size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    NSA_TRY(make_problem(p, hp));
+    NSA_TRY(check_cu(hp, cu_seqlens));
+    NSA_TRY(check_tensor(lse, sizes_of(hp).lse, 4, "lse"));
+    if (!sink) return fail(NSA_ERR_INVALID_ARG, "sink is NULL");
+    NSA_TRY(check_tensor(sink, hp.dev.Hq, 4, "sink"));
+    NSA_TRY(check_tensor(dsink, hp.dev.Hq, 4, "dsink"));
+    const nsa::BwdWorkspace need = carve(hp, nullptr);
+    if (need.bytes && (!workspace || workspace_bytes < need.bytes))
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need.bytes);
+    if (workspace && misaligned(workspace, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    hp.dev.cu = cu_seqlens;
+    const nsa::BwdWorkspace ws = carve(hp, workspace);
+    NSA_HIP(nsa::launch_dsink(hp, lse, ws.delta, sink, dsink, reinterpret_cast<hipStream_t>(stream)),
+            "dsink launch");
     return NSA_OK;
 }
 

@@ -32,6 +32,7 @@ struct Problem {
     float scale;  // softmax scale
     float scale_log2;  // scale * log2(e): scores in the base-2 domain
     const int* cu;
+    const float* sink;  // [Hq] per-head sink logits (natural log), or null
 };
 
 // Where sequence z lives.  Offsets are in elements; "rows" of block_idx and
@@ -296,6 +297,29 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// A finished softmax row with an attention-sink logit sk (natural log) in
+// its denominator: m2 is the row's running max in base-2 units and l the sum
+// of 2^(x - m2) over its keys (l = 0: no key).  Gives the factor that
+// normalises the output accumulated relative to 2^m2 and the row's lse:
+// with M = max(m2, sk log2 e), L = l 2^(m2 - M) + 2^(sk log2 e - M),
+// inv = 2^(m2 - M) / L and lse = (M + log2 L) ln 2 (a row with no key gets
+// o = 0, lse = sk; a sink of -inf changes nothing).
+__device__ __forceinline__ void finish_row_sink(float sk, float m2, float l, float& inv, float& lse) {
+    const float ninf = -__builtin_huge_valf();
+    const float mk = l > 0.f ? m2 : ninf;
+    const float s2 = sk * kLog2e;
+    const float M = fmaxf(mk, s2);
+    if (M == ninf) {
+        inv = 0.f;
+        lse = ninf;
+        return;
+    }
+    const float a = mk == ninf ? 0.f : fast_exp2(mk - M);
+    const float L = l * a + (s2 == ninf ? 0.f : fast_exp2(s2 - M));
+    inv = a / L;
+    lse = (M + fast_log2(L)) * kLn2;
+}
 
 // Workgroup index remapped so that consecutive logical indices stay on one
 // XCD (the dispatcher deals workgroups round-robin over the 8 XCDs, each

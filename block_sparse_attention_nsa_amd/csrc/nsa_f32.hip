@@ -80,9 +80,15 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
         }
     }
     float* orow = o + q_off(s, h, t);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float inv, lse_r;
+    if (p.sink) {
+        finish_row_sink(p.sink[h], m, l, inv, lse_r);
+    } else {
+        inv = l > 0.f ? 1.f / l : 0.f;
+        lse_r = l > 0.f ? (m + log2f(l)) * kLn2 : -__builtin_huge_valf();
+    }
     for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
-    lse[l_off(p, s, h, t)] = l > 0.f ? (m + log2f(l)) * kLn2 : -__builtin_huge_valf();
+    lse[l_off(p, s, h, t)] = lse_r;
 }
 
 template <int D>

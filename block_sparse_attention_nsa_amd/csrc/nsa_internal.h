@@ -54,6 +54,10 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
                         hipStream_t st);
 hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
                          hipStream_t st);
+// dsink[h] = -sum over head h's rows of exp(sink[h] - lse) * Delta (fixed
+// order: one workgroup per head).
+hipError_t launch_dsink(const HostProblem& hp, const float* lse, const float* delta,
+                        const float* sink, float* dsink, hipStream_t st);
 // Counts of padding / out-of-range / future / repeated block_idx entries
 // (counts[4], zeroed first on the stream).
 hipError_t launch_check_idx(const HostProblem& hp, const int* block_idx, unsigned long long* counts,

@@ -686,7 +686,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         const float l_tot = col_sum4(l_run[i]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float lse_r = l_tot > 0.f ? (m_run[i] * c2 + fast_log2(l_tot)) * kLn2 : kNegInfQ;
+        if (p.sink) finish_row_sink(p.sink[tr[i].h], m_run[i] * c2, l_tot, inv, lse_r);
         if (tr[i].valid) {
             uint16_t* orow = o + s.q_base + (int)(tr[i].h * s.q_sh + tr[i].t * s.q_st) + 4 * g;
 #pragma unroll
@@ -695,9 +697,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                                             pack_bf16x2(acc[i][dt][2] * inv, acc[i][dt][3] * inv));
                 *reinterpret_cast<uint2*>(orow + 16 * dt) = pk;
             }
-            if (g == 0)
-                lse[l_off(p, s, tr[i].h, tr[i].t)] =
-                    l_tot > 0.f ? (m_run[i] * c2 + fast_log2(l_tot)) * kLn2 : kNegInfQ;
+            if (g == 0) lse[l_off(p, s, tr[i].h, tr[i].t)] = lse_r;
         }
     }
 }

@@ -174,7 +174,27 @@ nsa_status nsa_sel_invert(const nsa_sel_problem* p, const int32_t* block_idx,
                           const int32_t* cu_seqlens, int32_t* offsets, int32_t* tokens,
                           void* workspace, size_t workspace_bytes, nsa_stream_t stream);
 
-/* Validation of a block_idx (optional; the other calls accept any entry).
+/* Attention sink (page 3's backward chain has a dSink step; the reading
+ * taken): sink [Hq] float (device) holds one logit per query head, in natural
+ * log units with no scale applied, that joins every row's softmax
+ * denominator and carries no value:
+ *   lse = log(sum_{j in A} exp(scale <q, k_j>) + exp(sink[h])),
+ *   o   = sum_{j in A} exp(scale <q, k_j> - lse) v_j
+ * (an empty A gives o = 0, lse = sink[h]).  nsa_sel_fwd_sink is nsa_sel_fwd
+ * with the sink (sink == NULL: no sink).  The backward needs nothing new for
+ * dq, dk, dv: nsa_sel_bwd (or its stages) given this lse computes them.
+ * nsa_sel_bwd_dsink, called after the backward's prepare stage on the same
+ * workspace (it reads Delta there), writes dsink [Hq] float:
+ *   dsink[h] = -sum over the rows of head h of exp(sink[h] - lse) * Delta
+ * in a fixed order (deterministic).  sink must not be NULL there. */
+nsa_status nsa_sel_fwd_sink(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
+                            const int32_t* block_idx, const int32_t* cu_seqlens, const float* sink,
+                            void* o, float* lse, nsa_stream_t stream);
+nsa_status nsa_sel_bwd_dsink(const nsa_sel_problem* p, const float* lse, const float* sink,
+                             const int32_t* cu_seqlens, float* dsink, void* workspace,
+                             size_t workspace_bytes, nsa_stream_t stream);
+
+/* Validation of a block_idx (optional; the other calls accept any entry)./* Validation of a block_idx (optional; the other calls accept any entry).
  * Writes four counts over all rows of the problem into counts[4] (device
  * memory, uint64, overwritten): [0] padding entries (negative), [1] entries
  * out of range (>= NB of the row's sequence), [2] future entries (in range
