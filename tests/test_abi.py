@@ -107,6 +107,26 @@ def test_workspace_checked_before_launch():
     assert "multiple" in _lib.last_error()
 
 
+def test_sink_and_check_calls_validate_before_any_hip_call():
+    """The sink forward, dsink and block_idx check reject bad arguments on the
+    host (no GPU here: a launch would fail differently)."""
+    lib = _lib.load()
+    p = _prob(dtype=1, D=64, block_size=32, Hq=6, Hkv=2, T=1024, B=2, S=8)
+    st = lib.nsa_sel_fwd_sink(p, FAKE, FAKE, FAKE, FAKE, None, FAKE + 2, FAKE, FAKE, None)
+    assert st == _lib.NSA_ERR_INVALID_ARG and "sink is not 4-byte aligned" in _lib.last_error()
+    need = lib.nsa_sel_bwd_workspace_bytes(p)
+    st = lib.nsa_sel_bwd_dsink(p, FAKE, None, None, FAKE, FAKE, need, None)
+    assert st == _lib.NSA_ERR_INVALID_ARG and "sink is NULL" in _lib.last_error()
+    st = lib.nsa_sel_bwd_dsink(p, FAKE, FAKE, None, FAKE, FAKE, need - 1, None)
+    assert st == _lib.NSA_ERR_WORKSPACE
+    st = lib.nsa_sel_bwd_dsink(p, FAKE, FAKE, None, None, FAKE, need, None)
+    assert st == _lib.NSA_ERR_INVALID_ARG and "dsink is NULL" in _lib.last_error()
+    st = lib.nsa_sel_check_block_idx(p, FAKE, None, FAKE + 4, None)
+    assert st == _lib.NSA_ERR_INVALID_ARG and "counts is not 8-byte aligned" in _lib.last_error()
+    st = lib.nsa_sel_check_block_idx(_prob(Hq=3, Hkv=2), FAKE, None, FAKE, None)
+    assert st == _lib.NSA_ERR_INVALID_ARG and "multiple" in _lib.last_error()
+
+
 def test_status_strings():
     for s in range(5):
         assert _lib.status_string(s)
