@@ -17,6 +17,7 @@ Where the method's source pages are silent the oracle takes these readings:
   * causality applies to every listed block (key j <= query t), so a listed
     future block adds nothing; an empty row gives o = 0, lse = -inf, dq = 0;
   * scale defaults to 1/sqrt(D); lse is natural-log and includes the scale;
+  * an optional sliding window W (keys t - W < j <= t), a mask on keys only;
   * an optional attention sink (page 3 names a dSink backward step, nothing
     more): a per-head logit, no scale, in every row's softmax denominator
     with no value; lse includes it, dq/dk/dv keep their formulas with that
@@ -59,7 +60,7 @@ def _load():
     ip = ctypes.POINTER(ctypes.c_int32)
     lp = ctypes.POINTER(ctypes.c_int64)
     i, d, i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
-    shape = [i, i, i, i, i, i, i, d, dp]
+    shape = [i, i, i, i, i, i, i, d, dp, i]
     lib.nsa_oracle_fwd_rows.argtypes = shape + [dp, dp, dp, ip, i64, lp, dp, dp]
     lib.nsa_oracle_bwd_rows.argtypes = shape + [dp, dp, dp, dp, ip, i64, lp, dp, dp, dp]
     lib.nsa_oracle_dkdv_keys.argtypes = shape + [dp, dp, dp, dp, ip, dp, dp, i64, lp, dp, dp]
@@ -88,7 +89,7 @@ def _ptr(a: np.ndarray, ct):
     return a.ctypes.data_as(ctypes.POINTER(ct))
 
 
-def _shape(q, k, idx, block_size, scale, sink=None):
+def _shape(q, k, idx, block_size, scale, sink=None, window=0):
     """The C shape arguments; sink (per-head logits) is passed as a pointer
     to a float64 copy that the returned tuple keeps alive."""
     B, Hq, T, D = q.shape
@@ -102,7 +103,9 @@ def _shape(q, k, idx, block_size, scale, sink=None):
     if sk is not None and sk.shape != (Hq,):
         raise ValueError("sink must hold one logit per query head")
     ptr = None if sk is None else _ptr(sk, ctypes.c_double)
-    return _Shape((B, Hq, Hkv, T, D, S, int(block_size), float(scale), ptr), sk)
+    if window is None or window < 0:
+        raise ValueError("window must be >= 0 (0: none)")
+    return _Shape((B, Hq, Hkv, T, D, S, int(block_size), float(scale), ptr, int(window)), sk)
 
 
 class _Shape(tuple):
@@ -113,11 +116,11 @@ class _Shape(tuple):
         return t
 
 
-def fwd_rows(q, k, v, block_idx, block_size, rows=None, scale=None, sink=None):
+def fwd_rows(q, k, v, block_idx, block_size, rows=None, scale=None, sink=None, window=0):
     """Forward of the listed flat rows ((b*Hq + h)*T + t); all rows if None.
     Returns (o [n, D], lse [n])."""
     q, k, v, idx = _f64(q), _f64(k), _f64(v), _i32(block_idx)
-    sh = _shape(q, k, idx, block_size, scale, sink)
+    sh = _shape(q, k, idx, block_size, scale, sink, window)
     n = q.shape[0] * q.shape[1] * q.shape[2] if rows is None else len(rows)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     o = np.zeros((n, sh[4]))
@@ -132,10 +135,10 @@ def fwd_rows(q, k, v, block_idx, block_size, rows=None, scale=None, sink=None):
 
 
 def bwd_rows(q, k, v, dO, block_idx, block_size, rows=None, scale=None, want_dq=True,
-             sink=None):
+             sink=None, window=0):
     """lse, Delta and dq of the listed rows.  Returns (lse [n], delta [n], dq [n, D])."""
     q, k, v, dO, idx = _f64(q), _f64(k), _f64(v), _f64(dO), _i32(block_idx)
-    sh = _shape(q, k, idx, block_size, scale, sink)
+    sh = _shape(q, k, idx, block_size, scale, sink, window)
     n = q.shape[0] * q.shape[1] * q.shape[2] if rows is None else len(rows)
     r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
     lse, delta = np.zeros(n), np.zeros(n)
@@ -151,11 +154,12 @@ def bwd_rows(q, k, v, dO, block_idx, block_size, rows=None, scale=None, want_dq=
     return lse, delta, dq
 
 
-def dkdv_keys(q, k, v, dO, block_idx, block_size, row_lse, row_delta, keys=None, scale=None):
+def dkdv_keys(q, k, v, dO, block_idx, block_size, row_lse, row_delta, keys=None, scale=None,
+              window=0):
     """dk, dv of the listed flat keys ((b*Hkv + hkv)*T + j); all keys if None.
     row_lse/row_delta: every row, shaped or flat [B*Hq*T]."""
     q, k, v, dO, idx = _f64(q), _f64(k), _f64(v), _f64(dO), _i32(block_idx)
-    sh = _shape(q, k, idx, block_size, scale)
+    sh = _shape(q, k, idx, block_size, scale, None, window)
     lse, delta = _f64(row_lse).reshape(-1), _f64(row_delta).reshape(-1)
     n = k.shape[0] * k.shape[1] * k.shape[2] if keys is None else len(keys)
     kk = None if keys is None else np.ascontiguousarray(keys, dtype=np.int64)
@@ -171,19 +175,21 @@ def dkdv_keys(q, k, v, dO, block_idx, block_size, row_lse, row_delta, keys=None,
     return dk, dv
 
 
-def fwd(q, k, v, block_idx, block_size, scale=None, sink=None):
-    """Dense forward: o like q, lse [B, Hq, T] (sink: optional [Hq] logits)."""
+def fwd(q, k, v, block_idx, block_size, scale=None, sink=None, window=0):
+    """Dense forward: o like q, lse [B, Hq, T] (sink: optional [Hq] logits;
+    window: sliding-window width, 0 for none)."""
     B, Hq, T, D = np.shape(q)
-    o, lse = fwd_rows(q, k, v, block_idx, block_size, None, scale, sink)
+    o, lse = fwd_rows(q, k, v, block_idx, block_size, None, scale, sink, window)
     return o.reshape(B, Hq, T, D), lse.reshape(B, Hq, T)
 
 
-def bwd(q, k, v, dO, block_idx, block_size, scale=None, sink=None):
+def bwd(q, k, v, dO, block_idx, block_size, scale=None, sink=None, window=0):
     """Dense backward: (dq, dk, dv, lse, delta); lse includes the sink if any."""
     B, Hq, T, D = np.shape(q)
     Hkv = np.shape(k)[1]
-    lse, delta, dq = bwd_rows(q, k, v, dO, block_idx, block_size, None, scale, sink=sink)
-    dk, dv = dkdv_keys(q, k, v, dO, block_idx, block_size, lse, delta, None, scale)
+    lse, delta, dq = bwd_rows(q, k, v, dO, block_idx, block_size, None, scale, sink=sink,
+                              window=window)
+    dk, dv = dkdv_keys(q, k, v, dO, block_idx, block_size, lse, delta, None, scale, window)
     return (dq.reshape(B, Hq, T, D), dk.reshape(B, Hkv, T, D), dv.reshape(B, Hkv, T, D),
             lse.reshape(B, Hq, T), delta.reshape(B, Hq, T))
 
@@ -235,7 +241,7 @@ def _seq(x_thd: np.ndarray, a: int, b: int) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x_thd)[a:b].transpose(1, 0, 2))[None]
 
 
-def fwd_thd(q, k, v, block_idx, cu_seqlens, block_size, scale=None, sink=None):
+def fwd_thd(q, k, v, block_idx, cu_seqlens, block_size, scale=None, sink=None, window=0):
     """Packed forward: q [Ttot,Hq,D], k/v [Ttot,Hkv,D], block_idx [Hkv,Ttot,S].
     Returns (o [Ttot,Hq,D], lse [Hq,Ttot])."""
     Ttot, Hq, D = np.shape(q)
@@ -246,13 +252,13 @@ def fwd_thd(q, k, v, block_idx, cu_seqlens, block_size, scale=None, sink=None):
         if b == a:
             continue
         oz, lz = fwd(_seq(q, a, b), _seq(k, a, b), _seq(v, a, b),
-                     np.asarray(block_idx)[:, a:b][None], block_size, scale, sink)
+                     np.asarray(block_idx)[:, a:b][None], block_size, scale, sink, window)
         o[a:b] = oz[0].transpose(1, 0, 2)
         lse[:, a:b] = lz[0]
     return o, lse
 
 
-def bwd_thd(q, k, v, dO, block_idx, cu_seqlens, block_size, scale=None, sink=None):
+def bwd_thd(q, k, v, dO, block_idx, cu_seqlens, block_size, scale=None, sink=None, window=0):
     """Packed backward: (dq, dk, dv) in the packed layouts, plus lse, delta [Hq,Ttot]."""
     Ttot, Hq, D = np.shape(q)
     Hkv = np.shape(k)[1]
@@ -263,7 +269,7 @@ def bwd_thd(q, k, v, dO, block_idx, cu_seqlens, block_size, scale=None, sink=Non
         if b == a:
             continue
         r = bwd(_seq(q, a, b), _seq(k, a, b), _seq(v, a, b), _seq(dO, a, b),
-                np.asarray(block_idx)[:, a:b][None], block_size, scale, sink)
+                np.asarray(block_idx)[:, a:b][None], block_size, scale, sink, window)
         dq[a:b] = r[0][0].transpose(1, 0, 2)
         dk[a:b] = r[1][0].transpose(1, 0, 2)
         dv[a:b] = r[2][0].transpose(1, 0, 2)

@@ -33,6 +33,12 @@
  * rows of head h, is -sum_rows exp(sink[h] - lse) Delta (computed in
  * oracle/__init__.py).  sink == NULL means no sink.
  *
+ * Optional sliding window (the pages list sliding-window masks among the
+ * backward's flavours; the reading taken): window W >= 1 further limits A to
+ * the keys j with t - W < j <= t (W = 0: no limit).  It is a mask on the
+ * keys only: block lists, and so the block -> query inversion, are
+ * unchanged.
+ *
  * Layout (dense, contiguous, row-major): q, o, dO, dq [B][Hq][T][D];
  * k, v, dk, dv [B][Hkv][T][D]; block_idx [B][Hkv][T][S] int32; lse, delta
  * [B][Hq][T].  Packed variable-length batches are handled by the Python side
@@ -54,6 +60,7 @@ typedef struct {
     int B, Hq, Hkv, T, D, S, bs;
     double scale;
     const double* sink; /* [Hq] or NULL */
+    int window;         /* 0: none */
 } shape_t;
 
 static int n_blocks(const shape_t* sh) { return (sh->T + sh->bs - 1) / sh->bs; }
@@ -90,7 +97,7 @@ static int selected_keys(const shape_t* sh, const int32_t* row, int t, int* keys
     for (int u = 0; u < NB; ++u) {
         if (!row_lists_block(row, sh->S, u)) continue;
         for (int j = u * sh->bs; j < (u + 1) * sh->bs && j < sh->T && j <= t; ++j)
-            keys[n++] = j;
+            if (sh->window <= 0 || j > t - sh->window) keys[n++] = j;
     }
     return n;
 }
@@ -169,6 +176,7 @@ static void dkdv_key(const shape_t* sh, const double* q, const double* k, const 
     const double* vj = krow(sh, v, b, hkv, j);
     for (int d = 0; d < D; ++d) dk_out[d] = dv_out[d] = 0.0;
     for (int t = j; t < sh->T; ++t) {
+        if (sh->window > 0 && t >= j + sh->window) break;  /* key j left row t's window */
         if (!row_lists_block(idx_row(sh, idx, b, hkv, t), sh->S, u)) continue;
         for (int g = 0; g < G; ++g) {
             int h = hkv * G + g;
@@ -191,8 +199,9 @@ static int shape_ok(const shape_t* sh) {
     return 1;
 }
 
-#define SHAPE_ARGS int B, int Hq, int Hkv, int T, int D, int S, int bs, double scale, const double* sink
-#define MAKE_SHAPE shape_t sh = {B, Hq, Hkv, T, D, S, bs, scale, sink}
+#define SHAPE_ARGS \
+    int B, int Hq, int Hkv, int T, int D, int S, int bs, double scale, const double* sink, int window
+#define MAKE_SHAPE shape_t sh = {B, Hq, Hkv, T, D, S, bs, scale, sink, window}
 
 int nsa_oracle_num_threads(void) {
 #ifdef _OPENMP
@@ -281,7 +290,7 @@ int nsa_oracle_dkdv_keys(SHAPE_ARGS, const double* q, const double* k, const dou
 /* Full forward: o [B][Hq][T][D], lse [B][Hq][T]. */
 int nsa_oracle_fwd(SHAPE_ARGS, const double* q, const double* k, const double* v,
                    const int32_t* idx, double* o, double* lse) {
-    return nsa_oracle_fwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, q, k, v, idx,
+    return nsa_oracle_fwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, window, q, k, v, idx,
                                (int64_t)B * Hq * T, NULL, o, lse);
 }
 
@@ -290,10 +299,10 @@ int nsa_oracle_fwd(SHAPE_ARGS, const double* q, const double* k, const double* v
 int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v,
                    const double* dO, const int32_t* idx, double* dq, double* dk, double* dv,
                    double* lse, double* delta) {
-    int rc = nsa_oracle_bwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, q, k, v, dO, idx,
+    int rc = nsa_oracle_bwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, window, q, k, v, dO, idx,
                                  (int64_t)B * Hq * T, NULL, lse, delta, dq);
     if (rc) return rc;
-    return nsa_oracle_dkdv_keys(B, Hq, Hkv, T, D, S, bs, scale, sink, q, k, v, dO, idx, lse, delta,
+    return nsa_oracle_dkdv_keys(B, Hq, Hkv, T, D, S, bs, scale, sink, window, q, k, v, dO, idx, lse, delta,
                                 (int64_t)B * Hkv * T, NULL, dk, dv);
 }
 
@@ -306,7 +315,7 @@ int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v
  * too small. */
 int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* idx,
                           int32_t* counts, int32_t* tokens, int64_t cap) {
-    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL};
+    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL, 0};
     int NB = n_blocks(&sh);
     int64_t n = 0;
     for (int b = 0; b < B; ++b)
@@ -326,7 +335,7 @@ int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* i
 
 /* Number of useful (query-head row, key) pairs: sum over rows of |A|. */
 int64_t nsa_oracle_count_pairs(int B, int Hq, int Hkv, int T, int S, int bs, const int32_t* idx) {
-    shape_t sh = {B, Hq, Hkv, T, 1, S, bs, 1.0, NULL};
+    shape_t sh = {B, Hq, Hkv, T, 1, S, bs, 1.0, NULL, 0};
     if (!shape_ok(&sh)) return -1;
     int G = Hq / Hkv;
     int* keys = (int*)malloc(sizeof(int) * (size_t)S * bs);

@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_pins as pins
 import test_oracle_sink as sink_pins
+import test_oracle_window as window_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "nsa_oracle.c")
 
@@ -35,6 +36,8 @@ MUTANTS = {
                  "const double* V = krow(sh, k, b, hkv, 0);\n    int n = selected_keys"),
     "sink left out of the sum": ("double sum = sh->sink ? exp(sk - m) : 0.0;", "double sum = 0.0;"),
     "sink ignored on empty rows": ("if (n == 0) return sk;", "if (n == 0) return -INFINITY;"),
+    "window off by one": ("j > t - sh->window) keys[n++] = j;", "j >= t - sh->window) keys[n++] = j;"),
+    "dkdv ignores the window": ("if (sh->window > 0 && t >= j + sh->window) break;", ";"),
 }
 
 
@@ -65,6 +68,8 @@ CHECKS = [
     lambda: sink_pins.test_sink_finite_differences(pins.TINY[0]),
     lambda: sink_pins.test_sink_dense_autograd(21, 2, 4, 2, 40, 8, 4, 5),
     lambda: sink_pins.test_sink_closed_forms_and_empty_rows(),
+    lambda: window_pins.test_window_finite_differences(window_pins.WTINY[0]),
+    lambda: window_pins.test_window_dense_autograd(41, 2, 4, 2, 40, 8, 4, 5, 7),
 ]
 
 
