@@ -46,7 +46,7 @@ def _stream():
 
 def make_problem(q: torch.Tensor, k: torch.Tensor, block_idx: torch.Tensor, block_size: int,
                  scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
-                 max_seqlen: Optional[int] = None) -> _lib.Problem:
+                 max_seqlen: Optional[int] = None, window: int = 0) -> _lib.Problem:
     """The nsa_sel_problem describing these tensors."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"q dtype {q.dtype} is not float32 or bfloat16")
@@ -74,6 +74,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, block_idx: torch.Tensor, bloc
     p.block_size = int(block_size)
     p.dtype = _DTYPES[q.dtype]
     p.scale = float(q.shape[-1] ** -0.5 if scale is None else scale)
+    p.window = int(window)
     return p
 
 
@@ -107,9 +108,10 @@ def _check_sink(sink, p: _lib.Problem):
 
 
 def nsa_sel_fwd(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None,
-                out=None, lse=None, sink=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """o, lse = forward (nsa_sel_fwd; nsa_sel_fwd_sink with per-head sink logits)."""
-    p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+                out=None, lse=None, sink=None, window=0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """o, lse = forward (nsa_sel_fwd; nsa_sel_fwd_sink with per-head sink
+    logits); window > 0: sliding window of that many keys."""
+    p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty(_lse_shape(q, cu_seqlens), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -135,11 +137,11 @@ def bwd_workspace_bytes(p: _lib.Problem) -> int:
 
 
 def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqlens=None,
-                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None, sink=None):
+                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None, sink=None, window=0):
     """dq, dk, dv = backward (nsa_sel_bwd); with sink logits (lse from the
     sink forward) also dsink, from nsa_sel_bwd_dsink on the same workspace:
     dq, dk, dv, dsink."""
-    p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+    p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     for name, t in (("o", o), ("dO", dO)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
@@ -173,8 +175,8 @@ class BwdStages:
     that order equals nsa_sel_bwd.  Buffers are allocated once here."""
 
     def __init__(self, q, k, v, block_idx, block_size, scale=None, cu_seqlens=None,
-                 max_seqlen=None):
-        self.p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+                 max_seqlen=None, window=0):
+        self.p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
         _check_tensors(q, k, v, block_idx, cu_seqlens, self.p)
         self.q, self.k, self.v, self.idx, self.cu = q, k, v, block_idx, cu_seqlens
         self.ws = torch.empty(max(bwd_workspace_bytes(self.p), 1), dtype=torch.uint8,
@@ -260,25 +262,28 @@ class SelectionAttn(torch.autograd.Function):
     """o = selection attention; backward through nsa_sel_bwd."""
 
     @staticmethod
-    def forward(ctx, q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen, sink=None):
+    def forward(ctx, q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen, sink=None,
+                window=0):
         o, lse = nsa_sel_fwd(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen,
-                             sink=sink)
+                             sink=sink, window=window)
         ctx.save_for_backward(q, k, v, o, lse, block_idx, cu_seqlens, sink)
-        ctx.cfg = (block_size, scale, max_seqlen)
+        ctx.cfg = (block_size, scale, max_seqlen, window)
         return o
 
     @staticmethod
     def backward(ctx, dO):
         q, k, v, o, lse, block_idx, cu_seqlens, sink = ctx.saved_tensors
-        block_size, scale, max_seqlen = ctx.cfg
+        block_size, scale, max_seqlen, window = ctx.cfg
         g = nsa_sel_bwd(q, k, v, o, lse, dO.contiguous(), block_idx, block_size, scale,
-                        cu_seqlens, max_seqlen, sink=sink)
+                        cu_seqlens, max_seqlen, sink=sink, window=window)
         dsink = g[3] if sink is not None else None
-        return g[0], g[1], g[2], None, None, None, None, None, dsink
+        return g[0], g[1], g[2], None, None, None, None, None, dsink, None
 
 
 def selection_attn(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max_seqlen=None,
-                   sink=None):
+                   sink=None, window=0):
     """Differentiable NSA selection attention (page 1's selection_attn call);
-    sink: optional per-head sink logits [Hq] float32 (differentiable)."""
-    return SelectionAttn.apply(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen, sink)
+    sink: optional per-head sink logits [Hq] float32 (differentiable);
+    window > 0: sliding window of that many keys."""
+    return SelectionAttn.apply(q, k, v, block_idx, block_size, scale, cu_seqlens, max_seqlen, sink,
+                               window)

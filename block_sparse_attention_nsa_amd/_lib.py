@@ -47,6 +47,7 @@ class Problem(ctypes.Structure):
         ("max_seqlen", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("window", ctypes.c_int32),
     ]
 
 

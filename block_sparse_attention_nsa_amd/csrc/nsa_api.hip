@@ -47,6 +47,7 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     if (p->S < 1) return fail(NSA_ERR_INVALID_ARG, "S=%d must be >= 1", p->S);
     if (p->block_size < 1) return fail(NSA_ERR_INVALID_ARG, "block_size=%d must be >= 1", p->block_size);
     if (!isfinite(p->scale)) return fail(NSA_ERR_INVALID_ARG, "scale is not finite");
+    if (p->window < 0) return fail(NSA_ERR_INVALID_ARG, "window=%d is negative (0: none)", p->window);
     int Tmax = p->T, Z = p->B;
     if (packed) {
         if (p->B != 1) return fail(NSA_ERR_INVALID_ARG, "packed inputs need B == 1 (got %d)", p->B);
@@ -85,6 +86,7 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     d.bs = p->block_size; d.Z = Z; d.packed = packed ? 1 : 0; d.Tmax = Tmax; d.NBmax = (int)NBmax;
     d.Smin = (int)Smin; d.scale = p->scale; d.scale_log2 = p->scale * nsa::kLog2e; d.cu = nullptr;
     d.sink = nullptr;
+    d.window = p->window;
     hp.dtype = p->dtype;
     hp.ZH = (int)ZH;
     // Inversion chunks of CT tokens: small (16) for short sequences, growing
@@ -104,7 +106,7 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
     if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");
     hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
-    hp.pair_possible = p->dtype == NSA_BF16 && hp.pslots == 0 && p->block_size <= 64 &&
+    hp.pair_possible = p->dtype == NSA_BF16 && hp.pslots == 0 && p->block_size <= 64 && p->window == 0 &&
                        (int64_t)p->S * p->block_size >= Tmax && ZH > 0 && NBmax > 0;
     if (nsa::invert_lds_bytes(hp) > 163840)
         return fail(NSA_ERR_UNSUPPORTED, "the block inversion needs %zu bytes of LDS for %lld blocks (max 163840)",

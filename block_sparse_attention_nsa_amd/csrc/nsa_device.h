@@ -33,6 +33,7 @@ struct Problem {
     float scale_log2;  // scale * log2(e): scores in the base-2 domain
     const int* cu;
     const float* sink;  // [Hq] per-head sink logits (natural log), or null
+    int window;         // sliding window: keys t - window < j <= t; 0 = none
 };
 
 // Where sequence z lives.  Offsets are in elements; "rows" of block_idx and

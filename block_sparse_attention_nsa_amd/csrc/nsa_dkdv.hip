@@ -129,7 +129,9 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // key of block 2U + 1 and the rows it adds see none of them: the causal mask
 // removes those).  pair_on: this is the per-block launch of a problem that
 // also has the paired one, so it runs only when the paired one does not.
-template <int D, int BS, bool PAIRED>
+// WIN: the problem has a sliding window (keys t - window < j only); the
+// paired launch never has one.
+template <int D, int BS, bool PAIRED, bool WIN>
 __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
@@ -277,7 +279,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
                             const float e = fast_exp2(fmaf(sc[rt][kt][i4], c2, nl[i4]));
-                            const float P = key <= tv[i4] ? e : 0.f;
+                            const bool vis = WIN ? key <= tv[i4] && key + p.window > tv[i4]
+                                                 : key <= tv[i4];
+                            const float P = vis ? e : 0.f;
                             pv[kt][rt][i4] = P;
                             dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
                         }
@@ -630,9 +634,12 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
             // selections); the per-block launch then exits at once.
             const unsigned pairs = (unsigned)((int64_t)hp.ZH * ((hp.dev.NBmax + 1) / 2));
             NSA_DISPATCH_D_BS(hp.dev.D, 2 * hp.dev.bs,
-                              go(dkdv_kernel<D, BS, true>, pairs, BS / 16 * 64));
+                              go(dkdv_kernel<D, BS, true, false>, pairs, BS / 16 * 64));
         }
-        NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false>, items, BS / 16 * 64));
+        if (hp.dev.window > 0)
+            NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, true>, items, BS / 16 * 64));
+        else
+            NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, false>, items, BS / 16 * 64));
     }
     if (nred) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,

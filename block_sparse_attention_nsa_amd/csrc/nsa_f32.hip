@@ -66,7 +66,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
         const int u = row[si];
         if (!slot_valid(row, si, u, NBz, p.bs, t)) continue;
         const int j1 = min((u + 1) * p.bs, t + 1);
-        for (int j = u * p.bs; j < j1; ++j) {
+        // Sliding window: keys t - window < j only.
+        const int j0 = p.window > 0 ? max(u * p.bs, t - p.window + 1) : u * p.bs;
+        for (int j = j0; j < j1; ++j) {
             const float* kr = k + k_off(s, hkv, j);
             const float* vr = v + k_off(s, hkv, j);
             float x = 0.f;
@@ -120,7 +122,9 @@ __global__ __launch_bounds__(128) void dq_f32_kernel(Problem p, const float* __r
         const int u = row[si];
         if (!slot_valid(row, si, u, NBz, p.bs, t)) continue;
         const int j1 = min((u + 1) * p.bs, t + 1);
-        for (int j = u * p.bs; j < j1; ++j) {
+        // Sliding window: keys t - window < j only.
+        const int j0 = p.window > 0 ? max(u * p.bs, t - p.window + 1) : u * p.bs;
+        for (int j = j0; j < j1; ++j) {
             const float* kr = k + k_off(s, hkv, j);
             const float* vr = v + k_off(s, hkv, j);
             float x = 0.f, dp = 0.f;
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(128) void dkdv_f32_kernel(
     }
     for (int e = 0; e < cnt; ++e) {
         const int t = list[e];
-        if (j > t) continue;
+        if (j > t || (p.window > 0 && t - p.window >= j)) continue;
         for (int gg = 0; gg < p.G; ++gg) {
             const int h = hkv * p.G + gg;
             const int64_t ro = q_off(s, h, t), lo = l_off(p, s, h, t);

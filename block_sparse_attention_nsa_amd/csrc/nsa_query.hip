@@ -452,7 +452,7 @@ __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int D, int BS, int RT, int NW, bool SYNC>
+template <int D, int BS, int RT, int NW, bool SYNC, bool WIN>
 __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                                                         const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         // ends before the tile's first token, and all rows exist.
         const bool full = ((bm & tmask[i]) == tmask[i]) &&
                           (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
-                          tr[i].valid;
+                          tr[i].valid && (!WIN || cur.j0 > tr[i].t - p.window);
         float mloc = kNegInfQ;
         if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
 #pragma unroll
@@ -549,11 +549,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
             // Key 16 kt + 4 g + e is masked past lim; compared as
             // 16 kt + e > lim - 4 g so the left side is a constant.
             const int lim = (sel ? tr[i].t - cur.j0 : -1) - 4 * g;
+            // Sliding window: keys below t - window + 1 too (same form).
+            const int lo = WIN ? tr[i].t - p.window + 1 - cur.j0 - 4 * g : 0;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (16 * kt + e > lim) sc[kt][e] = kNegInfQ;
+                    if (16 * kt + e > lim || (WIN && 16 * kt + e < lo)) sc[kt][e] = kNegInfQ;
                     mloc = fmaxf(mloc, sc[kt][e]);
                 }
         }
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, int BS, int RT, int NW, bool SYNC>
+template <int D, int BS, int RT, int NW, bool SYNC, bool WIN>
 __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     Problem p, QGeo qg, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO, const float* __restrict__ lse,
@@ -770,16 +772,17 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
                       bf16x8 (&dsb)[NKS]) __attribute__((always_inline)) {
         const bool full = ((bm & tmask[i]) == tmask[i]) &&
                           (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
-                          tr[i].valid;
+                          tr[i].valid && (!WIN || cur.j0 > tr[i].t - p.window);
         if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
             const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
             // Key 16 kt + 4 g + e is masked past lim (constant left side).
             const int lim = (sel ? tr[i].t - cur.j0 : -1) - 4 * g;
+            const int lo = WIN ? tr[i].t - p.window + 1 - cur.j0 - 4 * g : 0;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * kt + e > lim) sc[kt][e] = kNegInfQ;
+                    if (16 * kt + e > lim || (WIN && 16 * kt + e < lo)) sc[kt][e] = kNegInfQ;
         }
 #pragma unroll
         for (int ks_ = 0; ks_ < NKS; ++ks_) {
@@ -940,15 +943,19 @@ hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, 
     const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
     if (grid == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kNW_F * 64), lds, st, hp.dev, qg,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, block_idx,
+                           (uint16_t*)o, lse);
+    };
+    const bool win = hp.dev.window > 0;
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
                    if (q_sync(hp)) {
-                       hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT_F, kNW_F, true>), dim3(grid), dim3(kNW_F * 64),
-                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
-                                          (const uint16_t*)v, block_idx, (uint16_t*)o, lse);
+                       if (win) go(fwd_q_kernel<D, BS, kRT_F, kNW_F, true, true>);
+                       else go(fwd_q_kernel<D, BS, kRT_F, kNW_F, true, false>);
                    } else {
-                       hipLaunchKernelGGL((fwd_q_kernel<D, BS, kRT_F, kNW_F, false>), dim3(grid), dim3(kNW_F * 64),
-                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
-                                          (const uint16_t*)v, block_idx, (uint16_t*)o, lse);
+                       if (win) go(fwd_q_kernel<D, BS, kRT_F, kNW_F, false, true>);
+                       else go(fwd_q_kernel<D, BS, kRT_F, kNW_F, false, false>);
                    });
     return hipGetLastError();
 }
@@ -960,17 +967,19 @@ hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, c
     const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
     if (grid == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kNW_Q * 64), lds, st, hp.dev, qg,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                           (const uint16_t*)dO, lse, delta, block_idx, (uint16_t*)dq);
+    };
+    const bool win = hp.dev.window > 0;
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
                    if (q_sync(hp)) {
-                       hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT_Q, kNW_Q, true>), dim3(grid), dim3(kNW_Q * 64),
-                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
-                                          (const uint16_t*)v, (const uint16_t*)dO, lse, delta, block_idx,
-                                          (uint16_t*)dq);
+                       if (win) go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, true, true>);
+                       else go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, true, false>);
                    } else {
-                       hipLaunchKernelGGL((dq_q_kernel<D, BS, kRT_Q, kNW_Q, false>), dim3(grid), dim3(kNW_Q * 64),
-                                          lds, st, hp.dev, qg, (const uint16_t*)q, (const uint16_t*)k,
-                                          (const uint16_t*)v, (const uint16_t*)dO, lse, delta, block_idx,
-                                          (uint16_t*)dq);
+                       if (win) go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, false, true>);
+                       else go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, false, false>);
                    });
     return hipGetLastError();
 }

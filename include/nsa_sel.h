@@ -16,6 +16,8 @@
  *   Sel = { u : u listed in block_idx[z, hkv, t, :], 0 <= u < NB }   (a set)
  *   A   = { j : j / bs in Sel, j < len, j <= t }
  *   lse = log sum_{j in A} exp(scale <q, k_j>),  o = sum_{j in A} P_j v_j
+ * (with a sliding window W = window > 0, A also keeps only j > t - W; the
+ * page 3 backward lists sliding-window masks among its flavours)
  * and the backward is the exact gradient of o.  An empty A gives o = 0,
  * lse = -inf, dq = 0.  Negative or >= NB entries are padding.  Repeated
  * entries count once.  Keys listed by no row get dk = dv = 0.
@@ -91,6 +93,7 @@ typedef struct nsa_sel_problem {
     int32_t max_seqlen;  /* packed: bound on every sequence length; dense: ignored */
     int32_t dtype;       /* nsa_dtype */
     float scale;         /* softmax scale applied to <q, k> (e.g. 1/sqrt(D)) */
+    int32_t window;      /* sliding window: keys t - window < j <= t only; 0 = none */
 } nsa_sel_problem;
 
 typedef struct hipStream_t_opaque* nsa_stream_t; /* a hipStream_t; NULL = null stream */
