@@ -44,10 +44,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def useful_pairs(block_idx: np.ndarray, G: int, bs: int, lengths) -> int:
+def useful_pairs(block_idx: np.ndarray, G: int, bs: int, lengths, window: int = 0) -> int:
     """N = sum over query-head rows of |A|: a row (z, hkv, t) counts each
     distinct listed block u with 0 <= u < ceil(len/bs) and u*bs <= t, for
-    min((u+1)*bs, t+1) - u*bs keys; times G heads."""
+    min((u+1)*bs, t+1) - max(u*bs, t-window+1) keys (no lower limit without
+    a window); times G heads."""
     total = 0
     for rows, L in lengths:  # rows: [n, S] int array for tokens 0..L-1 of one (z, hkv)
         if L == 0:
@@ -61,7 +62,8 @@ def useful_pairs(block_idx: np.ndarray, G: int, bs: int, lengths) -> int:
         dup = np.zeros_like(ok)
         dup[:, 1:] = (u[:, 1:] == u[:, :-1])
         keep = (u >= 0) & ~dup
-        keys = np.minimum((u + 1) * bs, t + 1) - u * bs
+        lo = u * bs if window <= 0 else np.maximum(u * bs, t - window + 1)
+        keys = np.maximum(np.minimum((u + 1) * bs, t + 1) - lo, 0)
         total += int(np.where(keep, keys, 0).sum())
     return total * G
 
@@ -100,9 +102,10 @@ def stored_traffic(kernel: str, workload: str, src: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_tokens: int):
+def cpu_baseline(w, n_tokens: int, window: int = 0, sink=None):
     """The float64 oracle on the first n_tokens of every (entry, head) of the
-    same draw (a closed causal sub-problem), full forward + backward."""
+    same draw (a closed causal sub-problem), full forward + backward (with
+    the same window and sink logits, and the sink gradient, if any)."""
     import oracle
 
     if w.packed:
@@ -118,10 +121,16 @@ def cpu_baseline(w, n_tokens: int):
         sl = (slice(None), slice(None), slice(0, L))
         q, k, v, dO, idx = (np.ascontiguousarray(x[sl]) for x in (w.q, w.k, w.v, w.dO, w.block_idx))
         what = f"first {L} of {w.T} tokens of every batch entry and head"
-    n = oracle.count_pairs(idx, w.Hq, w.block_size)
+    G = w.Hq // w.Hkv
+    n = useful_pairs(idx, G, w.block_size,
+                     ((idx[b, h], idx.shape[2]) for b in range(idx.shape[0]) for h in range(w.Hkv)),
+                     window)
+    sk = None if sink is None else np.asarray(sink, dtype=np.float64)
     t0 = time.perf_counter()
-    oracle.fwd(q, k, v, idx, w.block_size, w.scale)
-    oracle.bwd(q, k, v, dO, idx, w.block_size, w.scale)
+    oracle.fwd(q, k, v, idx, w.block_size, w.scale, sink=sk, window=window)
+    r = oracle.bwd(q, k, v, dO, idx, w.block_size, w.scale, sink=sk, window=window)
+    if sk is not None:
+        oracle.dsink(sk, r[3], r[4], head_axis=1)
     dt = time.perf_counter() - t0
     flops = 14.0 * w.D * n
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
@@ -139,6 +148,10 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens per (entry, head) of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window of this many keys (0: none); a variant, not the metric's workload")
+    ap.add_argument("--sink", action="store_true",
+                    help="per-head attention-sink logits (forward with sink, dsink stage timed too)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, convert a bf16 tensor of this many MiB to "
                          "float32 once (a kernel of known traffic for scaling counters)")
@@ -161,7 +174,7 @@ def main():
     cfg = WORKLOADS[args.workload]
     w = workloads.make_config(cfg, seed=args.seed)
     G = w.Hq // w.Hkv
-    N = useful_pairs(w.block_idx, G, w.block_size, row_groups(w))
+    N = useful_pairs(w.block_idx, G, w.block_size, row_groups(w), args.window)
     f_fwd, f_bwd = 4.0 * w.D * N, 10.0 * w.D * N
     log(f"[bench] {args.workload}: {workloads.CONFIGS[cfg]}; N = {N} pairs, "
         f"F_fwd = {f_fwd:.4g}, F_bwd = {f_bwd:.4g}")
@@ -174,13 +187,19 @@ def main():
     ms = w.max_seqlen if w.packed else None
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
-    stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms)
-    names = ("fwd", "prepare", "dq", "dkdv", "dkdv_reduce")
+    stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms, window=args.window)
+    names = ("fwd", "prepare", "dq", "dkdv", "dkdv_reduce") + (("dsink",) if args.sink else ())
+    sink = None
+    if args.sink:
+        sink = torch.from_numpy(np.random.default_rng(args.seed + 1).normal(0.0, 1.0, w.Hq)
+                                .astype(np.float32)).to(dev)
+        dsink = torch.empty_like(sink)
 
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse)
+        nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse, sink=sink,
+                        window=args.window)
         if evs is not None:
             evs[1].record()
         stages.prepare(o, dO)
@@ -195,6 +214,10 @@ def main():
         stages.dkdv_reduce()
         if evs is not None:
             evs[5].record()
+        if sink is not None:
+            stages.dsink_stage(lse, sink, out=dsink)
+            if evs is not None:
+                evs[6].record()
 
     for _ in range(args.warmup):
         step()
@@ -218,7 +241,8 @@ def main():
                   "max": round(per_step[-1], 4)}
     ms_step = wall * 1e3 / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"] + stage_ms["dkdv_reduce"]
+    bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"] + stage_ms["dkdv_reduce"] + \
+        stage_ms.get("dsink", 0.0)
     log(f"[bench] ms/step {ms_step:.3f}; stages (ms): " +
         ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()))
 
@@ -246,7 +270,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle sample ({args.cpu_tokens} tokens per head) ...")
-        cpu = cpu_baseline(w, args.cpu_tokens)
+        cpu = cpu_baseline(w, args.cpu_tokens, args.window,
+                           None if sink is None else sink.cpu().numpy())
         log(f"[bench] CPU oracle: {cpu['value'] * 1e3:.2f} GFLOP/s in {cpu['seconds']} s "
             f"on {cpu['cores']} threads")
 
@@ -259,6 +284,10 @@ def main():
                   "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size,
                   "S": w.S}
     config["useful_pairs"] = N
+    if args.window:
+        config["window"] = args.window
+    if args.sink:
+        config["sink"] = "per-head logits ~ N(0, 1)"
     out = {
         "metric": "fwd+bwd useful TFLOP/s (bf16, D128) + % of MI355X bf16 MFMA peak",
         "value": round(value, 3),

@@ -218,6 +218,15 @@ class BwdStages:
         _lib.check("nsa_sel_bwd_dkdv_reduce", st)
         return self.dk, self.dv
 
+    def dsink_stage(self, lse, sink, out=None):
+        """Sink-logit gradient from the prepared workspace (nsa_sel_bwd_dsink)."""
+        _check_sink(sink, self.p)
+        ds = torch.empty_like(sink) if out is None else out
+        st = self.lib.nsa_sel_bwd_dsink(self.p, _ptr(lse), _ptr(sink), _ptr(self.cu), _ptr(ds),
+                                        _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_dsink", st)
+        return ds
+
 
 def nsa_sel_delta(o, dO, block_size, block_idx, k, scale=None, cu_seqlens=None, max_seqlen=None):
     """Delta = rowsum(dO * o) (nsa_sel_delta), laid out like lse."""

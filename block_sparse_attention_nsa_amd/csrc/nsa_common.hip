@@ -515,28 +515,31 @@ hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const B
 // The sink logit of head h joins every row's softmax denominator with no
 // value, so o moves by -P_sink o as it grows and its gradient is
 // dsink[h] = -sum over the rows of head h of exp(sink[h] - lse) Delta
-// (the reading of page 3's dSink chain step).  One 256-thread workgroup per
-// head walks the head's rows (dense: B runs of T, packed: one run of T) in a
-// fixed order and reduces its per-thread sums through LDS in a fixed tree,
-// so the result is deterministic.
-__global__ __launch_bounds__(256) void dsink_kernel(Problem p, const float* __restrict__ lse,
-                                                    const float* __restrict__ delta,
-                                                    const float* __restrict__ sink,
-                                                    float* __restrict__ dsink) {
-    __shared__ float red[256];
+// (the reading of page 3's dSink chain step).  One 1024-thread workgroup
+// per head walks the head's rows (dense: B runs of T, packed: one run of T)
+// in a fixed order, four independent loads in flight per thread, and reduces
+// its per-thread sums through LDS in a fixed tree, so the result is
+// deterministic.
+constexpr int kDsinkThreads = 1024;
+__global__ __launch_bounds__(kDsinkThreads) void dsink_kernel(Problem p, const float* __restrict__ lse,
+                                                              const float* __restrict__ delta,
+                                                              const float* __restrict__ sink,
+                                                              float* __restrict__ dsink) {
+    __shared__ float red[kDsinkThreads];
     const int h = blockIdx.x;
     const float sk = sink[h];
-    const int64_t n = (int64_t)p.B * p.T;
     float acc = 0.f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
-        const int64_t b = i / p.T, t = i - b * p.T;
-        const int64_t r = (b * p.Hq + h) * p.T + t;  // packed: B = 1, [Hq][T]
-        const float x = lse[r];
-        acc += x == -__builtin_huge_valf() ? 0.f : __expf(sk - x) * delta[r];
+    for (int b = 0; b < p.B; ++b) {
+        const int64_t base = ((int64_t)b * p.Hq + h) * p.T;  // packed: B = 1, [Hq][T]
+#pragma unroll 4
+        for (int t = threadIdx.x; t < p.T; t += kDsinkThreads) {
+            const float x = lse[base + t];
+            acc += x == -__builtin_huge_valf() ? 0.f : __expf(sk - x) * delta[base + t];
+        }
     }
     red[threadIdx.x] = acc;
     __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
+    for (int w = kDsinkThreads / 2; w >= 1; w >>= 1) {
         if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
@@ -546,7 +549,8 @@ __global__ __launch_bounds__(256) void dsink_kernel(Problem p, const float* __re
 hipError_t launch_dsink(const HostProblem& hp, const float* lse, const float* delta,
                         const float* sink, float* dsink, hipStream_t st) {
     if (hp.dev.Hq == 0) return hipSuccess;
-    hipLaunchKernelGGL(dsink_kernel, dim3(hp.dev.Hq), dim3(256), 0, st, hp.dev, lse, delta, sink, dsink);
+    hipLaunchKernelGGL(dsink_kernel, dim3(hp.dev.Hq), dim3(kDsinkThreads), 0, st, hp.dev, lse, delta,
+                       sink, dsink);
     return hipGetLastError();
 }
 

@@ -41,3 +41,21 @@ def test_config_pair_counts():
 def test_refuses_several_gpus():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_window_pair_counts_brute_force():
+    """With a sliding window the useful pairs are the selected keys j with
+    t - W < j <= t, counted row by row here."""
+    import numpy as np
+
+    w = workloads.make_dense(1, 4, 2, 150, 32, 5, 16, "f32", seed=3)
+    G, bs = 2, 16
+    for W in (1, 9, 40, 500):
+        n = bench.useful_pairs(w.block_idx, G, bs, ((w.block_idx[0, h], 150) for h in range(2)), W)
+        brute = 0
+        for h in range(2):
+            for t in range(150):
+                sel = {u for u in w.block_idx[0, h, t].tolist() if 0 <= u < 10 and u * bs <= t}
+                brute += sum(1 for u in sel for j in range(u * bs, min((u + 1) * bs, t + 1))
+                             if j > t - W)
+        assert n == brute * G, (W, n, brute * G)
