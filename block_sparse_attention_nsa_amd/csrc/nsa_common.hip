@@ -119,16 +119,18 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
 // and append their tokens in ascending order, so every list is ascending (a
 // stable counting sort; bit-exact).
 //
-// A row's entry u counts when 0 <= u < NBz and u*bs <= t, once however often
-// the row repeats it.  Each wave keeps a 16-bit array `last` over the blocks:
+// A row's entry u counts when 0 <= u < NBz and u*bs <= t (and, with a
+// sliding window W, the block reaches into the window: (u+1)*bs > t - W + 1;
+// a listing whose keys all lie below the window adds nothing), once however
+// often the row repeats it.  Each wave keeps a 16-bit array `last` over the blocks:
 // every valid entry of the row first writes its position in the row to
 // last[u] (lanes of one write that hit the same u leave exactly one of their
 // positions), then the entry whose position survived stands for u.  Every u
 // of the row is written before it is read, so `last` needs no clearing
 // between rows; plain LDS writes and reads replace atomics, and distinct
 // blocks never contend for one word.
-__device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t) {
-    return u >= 0 && u < NBz && u * bs <= t;
+__device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t, int W) {
+    return u >= 0 && u < NBz && u * bs <= t && (W <= 0 || (u + 1) * bs > t - W + 1);
 }
 
 // Calls f(u) once per distinct valid entry u of row (S entries, token t),
@@ -136,16 +138,16 @@ __device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t) {
 // entries (positions fit 16 bits).
 template <typename F>
 __device__ __forceinline__ void for_each_distinct(const int* row, int S, int NBz, int bs, int t,
-                                                  int lane, volatile uint16_t* last, F&& f) {
+                                                  int W, int lane, volatile uint16_t* last, F&& f) {
     for (int s0 = 0; s0 < S; s0 += 64) {
         const int si = s0 + lane;
         const int u = si < S ? row[si] : -1;
-        if (entry_ok(u, NBz, bs, t)) last[u] = (uint16_t)si;
+        if (entry_ok(u, NBz, bs, t, W)) last[u] = (uint16_t)si;
     }
     for (int s0 = 0; s0 < S; s0 += 64) {
         const int si = s0 + lane;
         const int u = si < S ? row[si] : -1;
-        if (entry_ok(u, NBz, bs, t) && last[u] == (uint16_t)si) f(u);
+        if (entry_ok(u, NBz, bs, t, W) && last[u] == (uint16_t)si) f(u);
     }
 }
 
@@ -189,7 +191,7 @@ __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, con
         stage_rows(p, s, idx, hkv, tb, te, rows);
         __syncthreads();
         for (int t = tb + w; t < te; t += kInvWaves)
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last,
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
                               [&](int u) { atomicAdd(&hist[u], 1); });
     }
     __syncthreads();
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
         const int n = te - tb, q = n / NW, rm = n % NW;
         const int r0 = tb + w * q + min(w, rm), r1 = r0 + q + (w < rm ? 1 : 0);
         for (int t = r0; t < r1; ++t)
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last,
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
                               [&](int u) { hw[u] += 1; });
         __syncthreads();
         for (int u = threadIdx.x; u < NB; u += blockDim.x) {
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
         }
         __syncthreads();
         for (int t = r0; t < r1; ++t)
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, lane, last, [&](int u) {
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last, [&](int u) {
                 const int pos = hw[u];
                 hw[u] = pos + 1;
                 out[pos] = t;

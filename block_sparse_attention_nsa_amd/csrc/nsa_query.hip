@@ -183,7 +183,8 @@ __device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
 }
 
 // Union of the blocks listed by tokens T0 .. T0+n_tok-1: umask[u] holds the
-// tokens listing block u (0 <= u < NBz, u*bs <= t); ulist the ascending
+// tokens listing block u (0 <= u < NBz, u*bs <= t, and inside the token's
+// sliding window if there is one); ulist the ascending
 // blocks with a non-empty mask.  Returns their count (same for all threads).
 __device__ int wg_union(const Problem& p, const Seq& s, const int* __restrict__ idx, int hkv,
                         int T0, int n_tok, int NBz, unsigned long long* umask, uint16_t* ulist,
@@ -195,7 +196,11 @@ __device__ int wg_union(const Problem& p, const Seq& s, const int* __restrict__ 
     const int n_ent = n_tok * p.S;
     for (int e = tid; e < n_ent; e += nt) {
         const int a = e / p.S, u = rows[e];
-        if (u >= 0 && u < NBz && u * p.bs <= T0 + a) atomicOr(&umask[u], 1ull << a);
+        // (With a sliding window, only blocks reaching into token T0 + a's
+        // window: the others are masked entirely, so they are not walked.)
+        if (u >= 0 && u < NBz && u * p.bs <= T0 + a &&
+            (p.window <= 0 || (u + 1) * p.bs > T0 + a - p.window + 1))
+            atomicOr(&umask[u], 1ull << a);
     }
     __syncthreads();
     if (tid < 64) {

@@ -163,7 +163,8 @@ nsa_status nsa_sel_delta(const nsa_sel_problem* p, const void* o, const void* dO
 
 /* Block -> query inversion alone.  For every (z, hkv, u) it lists, in
  * ascending order, the tokens t >= u * block_size whose row lists block u
- * (once each).  Z = B (dense) or n_seqs (packed); NBmax = ceil(T /
+ * (once each; with a sliding window, only those whose window reaches the
+ * block: (u + 1) * block_size > t - window + 1).  Z = B (dense) or n_seqs (packed); NBmax = ceil(T /
  * block_size) (dense) or ceil(max_seqlen / block_size) (packed); Smin =
  * min(S, NBmax).  Outputs: offsets [Z][Hkv][NBmax + 1] int32, offsets of
  * each list inside the (z, hkv) region of `tokens` (offsets[..][0] = 0, the
