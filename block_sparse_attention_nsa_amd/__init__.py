@@ -237,9 +237,9 @@ def nsa_sel_delta(o, dO, block_size, block_idx, k, scale=None, cu_seqlens=None, 
     return delta
 
 
-def nsa_sel_invert(q, k, block_idx, block_size, cu_seqlens=None, max_seqlen=None):
+def nsa_sel_invert(q, k, block_idx, block_size, cu_seqlens=None, max_seqlen=None, window=0):
     """Block -> query lists (nsa_sel_invert): (offsets [Z, Hkv, NBmax+1], tokens)."""
-    p = make_problem(q, k, block_idx, block_size, None, cu_seqlens, max_seqlen)
+    p = make_problem(q, k, block_idx, block_size, None, cu_seqlens, max_seqlen, window)
     lib = _lib.load()
     cap = int(lib.nsa_sel_invert_tokens_capacity(p))
     Z = p.B if cu_seqlens is None else p.n_seqs

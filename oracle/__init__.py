@@ -64,7 +64,7 @@ def _load():
     lib.nsa_oracle_fwd_rows.argtypes = shape + [dp, dp, dp, ip, i64, lp, dp, dp]
     lib.nsa_oracle_bwd_rows.argtypes = shape + [dp, dp, dp, dp, ip, i64, lp, dp, dp, dp]
     lib.nsa_oracle_dkdv_keys.argtypes = shape + [dp, dp, dp, dp, ip, dp, dp, i64, lp, dp, dp]
-    lib.nsa_oracle_invert.argtypes = [i, i, i, i, i, ip, ip, ip, i64]
+    lib.nsa_oracle_invert.argtypes = [i, i, i, i, i, i, ip, ip, ip, i64]
     lib.nsa_oracle_invert.restype = i64
     lib.nsa_oracle_count_pairs.argtypes = [i, i, i, i, i, i, ip]
     lib.nsa_oracle_count_pairs.restype = i64
@@ -209,17 +209,18 @@ def dsink(sink, lse, delta, head_axis: int):
     return -(p_sink * delta).sum(axis=axes)
 
 
-def invert(block_idx, block_size) -> Tuple[np.ndarray, np.ndarray]:
+def invert(block_idx, block_size, window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Brute-force block -> token lists: for block u the ascending tokens
-    t >= u*bs that list u.  Returns (counts [B,Hkv,NB], tokens) with the lists
-    concatenated in (b, hkv, u) order."""
+    t >= u*bs that list u (with a window W, only those t whose window reaches
+    a key of u: (u+1)*bs - 1 > t - W).  Returns (counts [B,Hkv,NB], tokens)
+    with the lists concatenated in (b, hkv, u) order."""
     idx = _i32(block_idx)
     B, Hkv, T, S = idx.shape
     NB = -(-T // block_size)
     counts = np.zeros((B, Hkv, NB), dtype=np.int32)
     cap = max(1, B * Hkv * T * min(S, NB))
     tokens = np.zeros(cap, dtype=np.int32)
-    n = _load().nsa_oracle_invert(B, Hkv, T, S, int(block_size), _ptr(idx, ctypes.c_int32),
+    n = _load().nsa_oracle_invert(B, Hkv, T, S, int(block_size), int(window), _ptr(idx, ctypes.c_int32),
                                   _ptr(counts, ctypes.c_int32), _ptr(tokens, ctypes.c_int32), cap)
     if n < 0:
         raise RuntimeError("oracle invert: capacity exceeded")

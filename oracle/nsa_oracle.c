@@ -313,9 +313,9 @@ int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v
  * [B][Hkv][NB]; tokens receives the lists back to back in that order (its
  * capacity is cap entries).  Returns the total entry count, or -1 if cap is
  * too small. */
-int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* idx,
+int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, int window, const int32_t* idx,
                           int32_t* counts, int32_t* tokens, int64_t cap) {
-    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL, 0};
+    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL, window};
     int NB = n_blocks(&sh);
     int64_t n = 0;
     for (int b = 0; b < B; ++b)
@@ -324,6 +324,8 @@ int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, const int32_t* i
                 int32_t c = 0;
                 for (int t = u * bs; t < T; ++t) {
                     if (!row_lists_block(idx_row(&sh, idx, b, hkv, t), S, u)) continue;
+                    /* with a window: only rows whose window reaches a key of u */
+                    if (window > 0 && (u + 1) * bs - 1 <= t - window) continue;
                     if (n >= cap) return -1;
                     tokens[n++] = t;
                     ++c;

@@ -297,10 +297,11 @@ def test_full_size_configs_sampled(cfg):
 
 # ---- inversion: bit-exact -----------------------------------------------
 
-def _inversion_matches(w):
+def _inversion_matches(w, window=0):
     d = to_dev(w)
     ms = w.max_seqlen if w.packed else None
-    offsets, tokens = nsa.nsa_sel_invert(d["q"], d["k"], d["idx"], w.block_size, d["cu"], ms)
+    offsets, tokens = nsa.nsa_sel_invert(d["q"], d["k"], d["idx"], w.block_size, d["cu"], ms,
+                                         window=window)
     torch.cuda.synchronize()
     offsets = offsets.cpu().numpy()
     tokens = tokens.cpu().numpy()
@@ -312,7 +313,7 @@ def _inversion_matches(w):
             idx_z = np.ascontiguousarray(w.block_idx[:, a:b])[None]
         else:
             idx_z = w.block_idx[z:z + 1]
-        counts, ref = oracle.invert(idx_z, w.block_size)
+        counts, ref = oracle.invert(idx_z, w.block_size, window)
         L = idx_z.shape[2]
         NBz = -(-L // w.block_size)
         pos = 0
@@ -341,6 +342,13 @@ def test_inversion_bit_exact_dense_irregular():
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_inversion_bit_exact_configs(cfg):
     _inversion_matches(workloads.make_config(cfg))
+
+
+@pytest.mark.parametrize("cfg,window", [(1, 100), (4, 700)])
+def test_inversion_bit_exact_with_window(cfg, window):
+    """With a sliding window only rows whose window reaches the block are
+    listed (dense and packed)."""
+    _inversion_matches(workloads.make_config(cfg), window)
 
 
 # ---- masking sentinels: bitwise ------------------------------------------

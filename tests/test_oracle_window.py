@@ -125,3 +125,25 @@ def test_window_limits():
     np.testing.assert_allclose(o, vv, rtol=1e-14)
     np.testing.assert_allclose(lse, np.sum(q * kk, axis=-1) / math.sqrt(q.shape[-1]), rtol=1e-13)
     assert np.abs(dq).max() == 0.0
+
+
+def test_window_inversion_brute_force():
+    """With a window, block u's list holds the tokens that list u and can see
+    at least one of its keys (some j of u with t - W < j <= t), ascending,
+    once each: plain Python against the oracle's inversion."""
+    rng = np.random.default_rng(44)
+    B, Hkv, T, bs, S, W = 2, 2, 50, 4, 6, 9
+    idx = pins._weird_idx(rng, B, Hkv, T, bs, S)
+    NB = -(-T // bs)
+    counts, tokens = oracle.invert(idx, bs, window=W)
+    pos = 0
+    for b in range(B):
+        for h in range(Hkv):
+            for u in range(NB):
+                lst = [t for t in range(T)
+                       if u in set(int(x) for x in idx[b, h, t])
+                       and any(t - W < j <= t for j in range(u * bs, min((u + 1) * bs, T)))]
+                assert counts[b, h, u] == len(lst)
+                assert tokens[pos:pos + len(lst)].tolist() == lst
+                pos += len(lst)
+    assert pos == len(tokens)
