@@ -83,3 +83,32 @@ def test_window_wider_than_sequence_is_bitwise_no_window():
         a, b = _run(w, 0, d), _run(w, w.T, d)
         for n in a:
             assert np.array_equal(a[n], b[n]), (recipe, n)
+
+
+def test_window_with_sink():
+    """A sliding window and attention-sink logits together (bf16, irregular
+    lists): o, lse, dq, dk, dv and dsink against the oracle."""
+    import math
+    rng = np.random.default_rng(55)
+    B, Hq, Hkv, T, D, S, bs, W = 1, 8, 2, 260, 64, 5, 32, 45
+    idx = _weird_block_idx(rng, B, Hkv, T, bs, S)
+    w = workloads.make_dense(B, Hq, Hkv, T, D, S, bs, "bf16", seed=56, name="win-sink",
+                             block_idx=idx)
+    sink_np = rng.normal(0.5, 1.5, size=Hq).astype(np.float32)
+    d = to_dev(w)
+    sink = torch.from_numpy(sink_np).cuda()
+    o, lse = nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], bs, w.scale, sink=sink, window=W)
+    dq, dk, dv, ds = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"], bs, w.scale,
+                                     sink=sink, window=W)
+    torch.cuda.synchronize()
+    sk = sink_np.astype(np.float64)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.block_idx, bs, w.scale, sink=sk, window=W)
+    rdq, rdk, rdv, lse64, delta64 = oracle.bwd(w.q, w.k, w.v, w.dO, w.block_idx, bs, w.scale,
+                                               sink=sk, window=W)
+    rds = oracle.dsink(sk, lse64, delta64, head_axis=1)
+    f = lambda x: x.float().cpu().numpy().astype(np.float64)
+    tol = TOL["bf16"]
+    for name, a, b in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rdq), ("dk", dk, rdk),
+                       ("dv", dv, rdv)):
+        assert_close(name, f(a), b, tol)
+    assert_close("dsink", f(ds), rds, tol * math.sqrt(T))
