@@ -1,6 +1,7 @@
 """Benchmark: NSA selection attention fwd + bwd on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload cfg2|cfg3|cfg4|cfg1]
+    python bench.py [--steps K] [--warmup W]
+        [--workload select_T8192|causal_B4_T4096|packed_8seq|bf16_T1024]
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 nsa_sel_fwd, then the backward's stages (Delta + block->query inversion +
@@ -31,7 +32,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 
-WORKLOADS = {"cfg1": 1, "cfg2": 2, "cfg3": 3, "cfg4": 4}
+# Workloads the benchmark runs (the f32 one is a parity case only).
+BENCH_WORKLOADS = ("select_T8192", "causal_B4_T4096", "packed_8seq", "bf16_T1024")
 # Algorithmic flops per (row, key) pair of each timed stage, in units of D:
 # fwd S and PV; dq recomputes S and dP and forms dS K; dkdv recomputes S and
 # dP and forms dV and dK.
@@ -143,7 +145,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cfg2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="select_T8192", choices=BENCH_WORKLOADS)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens per (entry, head) of the CPU oracle sample")
@@ -171,12 +173,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg = WORKLOADS[args.workload]
-    w = workloads.make_config(cfg, seed=args.seed)
+    w = workloads.make_workload(args.workload, seed=args.seed)
     G = w.Hq // w.Hkv
     N = useful_pairs(w.block_idx, G, w.block_size, row_groups(w), args.window)
     f_fwd, f_bwd = 4.0 * w.D * N, 10.0 * w.D * N
-    log(f"[bench] {args.workload}: {workloads.CONFIGS[cfg]}; N = {N} pairs, "
+    log(f"[bench] {args.workload}: {workloads.WORKLOADS[args.workload]}; N = {N} pairs, "
         f"F_fwd = {f_fwd:.4g}, F_bwd = {f_bwd:.4g}")
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -276,11 +277,11 @@ def main():
             f"on {cpu['cores']} threads")
 
     if w.packed:
-        config = {"workload": args.workload, "description": workloads.CONFIGS[cfg],
+        config = {"workload": args.workload, "description": workloads.WORKLOADS[args.workload],
                   "n_seqs": w.n_seqs, "total_tokens": w.T, "max_seqlen": w.max_seqlen,
                   "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "S": w.S}
     else:
-        config = {"workload": args.workload, "description": workloads.CONFIGS[cfg], "B": w.B,
+        config = {"workload": args.workload, "description": workloads.WORKLOADS[args.workload], "B": w.B,
                   "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size,
                   "S": w.S}
     config["useful_pairs"] = N

@@ -9,12 +9,12 @@ hash of the kernel sources it was taken on; bench.py reports it as
 roofline.traffic only while that hash still matches.
 
     rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "(dq_q_kernel|copy)" \\
-        --output-format csv -d <F> -o run -- python bench.py --workload cfg2 \\
+        --output-format csv -d <F> -o run -- python bench.py --workload select_T8192 \\
         --steps 2 --warmup 1 --no-cpu-baseline --calibrate-copy-mb 512
     (the same with WRITE_SIZE into <W>)
     python -m block_sparse_attention_nsa_amd.traffic --kernel dq_q_kernel \\
-        --workload cfg2 --copy-mb 512 --fetch <F>/run_counter_collection.csv \\
-        --write <W>/run_counter_collection.csv --out profiles/dq_q_kernel_cfg2_traffic.json
+        --workload select_T8192 --copy-mb 512 --fetch <F>/run_counter_collection.csv \\
+        --write <W>/run_counter_collection.csv --out profiles/dq_q_kernel_select_T8192_traffic.json
 """
 from __future__ import annotations
 

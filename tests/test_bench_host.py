@@ -25,15 +25,15 @@ def test_useful_pairs_matches_oracle_packed():
     assert n == oracle.count_pairs_thd(w.block_idx, w.cu_seqlens, 8, 8)
 
 
-def test_config_pair_counts():
+def test_workload_pair_counts():
     """Exact N of the small workloads (fp32 T 256, bf16 T 1024, NSA lists T
     8192), and of the dense causal 4 x 4096 workload as a closed form."""
-    for cfg in (0, 1, 2):
-        w = workloads.make_config(cfg)
+    for name in ("f32_T256", "bf16_T1024", "select_T8192"):
+        w = workloads.make_workload(name)
         G = w.Hq // w.Hkv
         n = bench.useful_pairs(w.block_idx, G, w.block_size, bench.row_groups(w))
         assert n == oracle.count_pairs(w.block_idx, w.Hq, w.block_size)
-    w = workloads.make_config(3)
+    w = workloads.make_workload("causal_B4_T4096")
     n = bench.useful_pairs(w.block_idx, 4, 64, bench.row_groups(w))
     assert n == 4 * 32 * 4096 * 4097 // 2
 

@@ -25,11 +25,11 @@ def _full_parity(w):
         assert_close(name, got[name], ref[name], tol)
 
 
-@pytest.mark.parametrize("cfg", [0, 1])
-def test_small_configs_full(cfg):
-    """Configs 0 (fp32, G=2, D32, bs16) and 1 (bf16, G=3, D64, bs32): every
+@pytest.mark.parametrize("name", ["f32_T256", "bf16_T1024"])
+def test_small_workloads_full(name):
+    """The f32 T 256 (G=2, D32, bs16) and bf16 T 1024 (G=3, D64, bs32) workloads: every
     output element against the oracle."""
-    _full_parity(workloads.make_config(cfg))
+    _full_parity(workloads.make_workload(name))
 
 
 def _weird_block_idx(rng, B, Hkv, T, bs, S):
@@ -212,7 +212,7 @@ def test_bf16_full_prefix_pairs(case):
     _full_parity(w2)
 
 
-# ---- full-size configurations: sampled outputs + invariants ---------------
+# ---- full-size workloads: sampled outputs + invariants --------------------
 
 def _sampled_parity(w, out, rng, n_rows=48, blocks=None):
     tol = TOL[w.dtype]
@@ -269,22 +269,22 @@ def _invariants(w, out, d):
         assert np.abs(sdv - sdo).max() < 1e-2 * w.T ** 0.5 * G
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_configs_sampled(cfg):
-    """Configs 2-4 at full size, in the launch configuration the benchmark
+@pytest.mark.parametrize("name", ["select_T8192", "causal_B4_T4096", "packed_8seq"])
+def test_full_size_workloads_sampled(name):
+    """The three D128 workloads at full size, in the launch configuration the benchmark
     times: sampled rows (o, lse, dq) and sampled key blocks (dk, dv) against
     the oracle, plus sum invariants over every key."""
-    w = workloads.make_config(cfg)
-    say(f"[cfg{cfg}] full size: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} S={w.S}")
+    w = workloads.make_workload(name)
+    say(f"[{name}] full size: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} S={w.S}")
     d = to_dev(w)
     out = run_gpu(w, d)
-    for name in out:
-        assert np.isfinite(out[name][~np.isinf(out[name])]).all(), name
-    rng = np.random.default_rng(cfg)
+    for key in out:
+        assert np.isfinite(out[key][~np.isinf(out[key])]).all(), key
+    rng = np.random.default_rng({"select_T8192": 2, "causal_B4_T4096": 3, "packed_8seq": 4}[name])
     NB = -(-w.T // w.block_size) if not w.packed else None
-    if cfg == 2:
+    if name == "select_T8192":
         blocks = [(0, 0, 127), (0, 1, 100), (0, 0, 64)]
-    elif cfg == 3:
+    elif name == "causal_B4_T4096":
         blocks = [(1, 3, 63), (3, 7, 48), (0, 0, 60)]
     else:
         lens = np.diff(w.cu_seqlens)
@@ -339,16 +339,16 @@ def test_inversion_bit_exact_dense_irregular():
     _inversion_matches(w)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4])
-def test_inversion_bit_exact_configs(cfg):
-    _inversion_matches(workloads.make_config(cfg))
+@pytest.mark.parametrize("name", ["bf16_T1024", "select_T8192", "packed_8seq"])
+def test_inversion_bit_exact_workloads(name):
+    _inversion_matches(workloads.make_workload(name))
 
 
-@pytest.mark.parametrize("cfg,window", [(1, 100), (4, 700)])
-def test_inversion_bit_exact_with_window(cfg, window):
+@pytest.mark.parametrize("name,window", [("bf16_T1024", 100), ("packed_8seq", 700)])
+def test_inversion_bit_exact_with_window(name, window):
     """With a sliding window only rows whose window reaches the block are
     listed (dense and packed)."""
-    _inversion_matches(workloads.make_config(cfg), window)
+    _inversion_matches(workloads.make_workload(name), window)
 
 
 # ---- masking sentinels: bitwise ------------------------------------------
@@ -393,25 +393,25 @@ def test_hidden_keys_do_not_move_rows_bitwise():
     assert np.all(out3["dq"][0, :, 64:128] == 0.0)
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_deterministic_bitwise(cfg):
+@pytest.mark.parametrize("name", ["select_T8192", "causal_B4_T4096"])
+def test_deterministic_bitwise(name):
     """Two full passes give identical bits (NSA lists with fp32 partials; the
     dense causal workload on the paired dK/dV path with its flag and iota
     lists rebuilt by each call)."""
-    w = workloads.make_config(cfg)
+    w = workloads.make_workload(name)
     d = to_dev(w)
     a = run_gpu(w, d)
     b = run_gpu(w, d)
-    for name in a:
-        assert np.array_equal(a[name], b[name]), name
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_staged_backward_equals_one_call(cfg):
+@pytest.mark.parametrize("name", ["bf16_T1024", "select_T8192", "causal_B4_T4096", "packed_8seq"])
+def test_staged_backward_equals_one_call(name):
     """prepare, dq, dkdv_blocks, dkdv_reduce in order equal nsa_sel_bwd bit for
     bit (the T 8192, G 16 workload has lists long enough to be split into fp32
     partials)."""
-    w = workloads.make_config(cfg)
+    w = workloads.make_workload(name)
     d = to_dev(w)
     cu = d.get("cu")
     ms = w.max_seqlen if w.packed else None
@@ -430,7 +430,7 @@ def test_staged_backward_equals_one_call(cfg):
 
 def test_runs_on_caller_stream():
     """All work is queued on the caller's (non-default) stream."""
-    w = workloads.make_config(1)
+    w = workloads.make_workload("bf16_T1024")
     d = to_dev(w)
     ref = run_gpu(w, d)
     s = torch.cuda.Stream()
@@ -456,7 +456,7 @@ def test_empty_problem():
 
 def test_autograd_function():
     """selection_attn's autograd gradients equal the direct C-ABI calls."""
-    w = workloads.make_config(1)
+    w = workloads.make_workload("bf16_T1024")
     d = to_dev(w)
     ref = run_gpu(w, d)
     q, k, v = (d[n].clone().requires_grad_(True) for n in ("q", "k", "v"))

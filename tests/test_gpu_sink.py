@@ -106,7 +106,7 @@ def test_sink_autograd_and_determinism():
     """selection_attn with a sink tensor that requires grad: gradients reach
     it and equal nsa_sel_bwd's dsink; two runs agree bit for bit."""
     rng = np.random.default_rng(35)
-    w = workloads.make_config(1)
+    w = workloads.make_workload("bf16_T1024")
     d = to_dev(w)
     sink_np = _sink_vals(rng, w.Hq)
     a = _run(w, d, sink_np)

@@ -48,22 +48,22 @@ def test_dense_recipe():
     _check_rows(idx, 300, 64, 5, True)
 
 
-def test_configs_reproducible_and_shaped():
-    a = workloads.make_config(0, seed=0)
-    b = workloads.make_config(0, seed=0)
-    c = workloads.make_config(0, seed=1)
+def test_workloads_reproducible_and_shaped():
+    a = workloads.make_workload("f32_T256", seed=0)
+    b = workloads.make_workload("f32_T256", seed=0)
+    c = workloads.make_workload("f32_T256", seed=1)
     for x, y in ((a.q, b.q), (a.block_idx, b.block_idx), (a.dO, b.dO)):
         np.testing.assert_array_equal(x, y)
     assert not np.array_equal(a.q, c.q)
     assert a.q.shape == (1, 2, 256, 32) and a.block_idx.shape == (1, 1, 256, 4)
     assert a.q.dtype == np.float32
-    w1 = workloads.make_config(1)
+    w1 = workloads.make_workload("bf16_T1024")
     assert w1.q.shape == (2, 6, 1024, 64) and w1.block_idx.shape == (2, 2, 1024, 8)
     np.testing.assert_array_equal(workloads.round_to_bf16(w1.q), w1.q)
 
 
-def test_thd_config_lengths():
-    w = workloads.make_config(4, seed=0)
+def test_thd_workload_lengths():
+    w = workloads.make_workload("packed_8seq", seed=0)
     lens = np.diff(w.cu_seqlens)
     assert len(lens) == 8 and np.all(lens % 64 == 0)
     assert np.all((lens >= 128) & (lens <= 4096))

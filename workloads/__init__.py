@@ -26,14 +26,14 @@ import numpy as np
 
 __all__ = [
     "Workload",
-    "CONFIGS",
+    "WORKLOADS",
     "round_to_bf16",
     "block_idx_own_random",
     "block_idx_own_first_random",
     "block_idx_dense",
     "make_dense",
     "make_thd",
-    "make_config",
+    "make_workload",
 ]
 
 
@@ -187,28 +187,28 @@ def make_thd(lengths: List[int], Hq, Hkv, D, S, block_size, dtype="bf16",
                     cu_seqlens=cu, max_seqlen=max(lengths) if lengths else 0)
 
 
-# The five benchmark workloads: (label, shape description).
-CONFIGS = {
-    0: "B1 Hq2 Hkv1 D32 T256 bs16 S4 f32, own block + random earlier",
-    1: "B2 Hq6 Hkv2 D64 T1024 bs32 S8 bf16, own block + random earlier",
-    2: "B1 Hq32 Hkv2 D128 T8192 bs64 S16 bf16, own + first + random earlier",
-    3: "B4 Hq32 Hkv8 D128 T4096 bs64 S64 bf16, dense causal",
-    4: "THD 8 seqs len 64*U{2..64} Hq32 Hkv8 D128 bs64 S16 bf16, own + first + random",
+# The five benchmark workloads, named by what they are: shape description.
+WORKLOADS = {
+    "f32_T256": "B1 Hq2 Hkv1 D32 T256 bs16 S4 f32, own block + random earlier",
+    "bf16_T1024": "B2 Hq6 Hkv2 D64 T1024 bs32 S8 bf16, own block + random earlier",
+    "select_T8192": "B1 Hq32 Hkv2 D128 T8192 bs64 S16 bf16, own + first + random earlier",
+    "causal_B4_T4096": "B4 Hq32 Hkv8 D128 T4096 bs64 S64 bf16, dense causal",
+    "packed_8seq": "THD 8 seqs len 64*U{2..64} Hq32 Hkv8 D128 bs64 S16 bf16, own + first + random",
 }
 
 
-def make_config(cfg: int, seed: int = 0) -> Workload:
-    if cfg == 0:
-        return make_dense(1, 2, 1, 256, 32, 4, 16, "f32", "own_random", seed, "cfg0")
-    if cfg == 1:
-        return make_dense(2, 6, 2, 1024, 64, 8, 32, "bf16", "own_random", seed, "cfg1")
-    if cfg == 2:
-        return make_dense(1, 32, 2, 8192, 128, 16, 64, "bf16", "own_first_random", seed, "cfg2")
-    if cfg == 3:
-        return make_dense(4, 32, 8, 4096, 128, 64, 64, "bf16", "dense", seed, "cfg3")
-    if cfg == 4:
+def make_workload(name: str, seed: int = 0) -> Workload:
+    if name == "f32_T256":
+        return make_dense(1, 2, 1, 256, 32, 4, 16, "f32", "own_random", seed, name)
+    if name == "bf16_T1024":
+        return make_dense(2, 6, 2, 1024, 64, 8, 32, "bf16", "own_random", seed, name)
+    if name == "select_T8192":
+        return make_dense(1, 32, 2, 8192, 128, 16, 64, "bf16", "own_first_random", seed, name)
+    if name == "causal_B4_T4096":
+        return make_dense(4, 32, 8, 4096, 128, 64, 64, "bf16", "dense", seed, name)
+    if name == "packed_8seq":
         rng = np.random.default_rng(seed)
         lengths = (64 * rng.integers(2, 65, size=8)).tolist()
         return make_thd(lengths, 32, 8, 128, 16, 64, "bf16", "own_first_random",
-                        name="cfg4", rng=rng)
-    raise ValueError(f"unknown config {cfg}")
+                        name=name, rng=rng)
+    raise ValueError(f"unknown workload {name!r}")
