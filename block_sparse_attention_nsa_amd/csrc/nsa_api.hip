@@ -89,11 +89,15 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     d.window = p->window;
     hp.dtype = p->dtype;
     hp.ZH = (int)ZH;
-    // Inversion chunks of CT tokens: small (16) for short sequences, growing
-    // so that the per-(z, hkv) chunk x block table stays within 2^14 entries.
+    // Inversion chunks of CT tokens: at least 64 (smaller chunks multiply the
+    // count and fill workgroups, whose launch then costs more than their
+    // work: with 16-token chunks the prepare stage took 0.108 / 0.092 ms on 8
+    // packed sequences / a dense causal 4 x 4096 problem, 0.091 / 0.080 with
+    // 64), growing in steps of 16 so that the per-(z, hkv) chunk x block
+    // table stays within 2^14 entries.
     {
         const int64_t work = (int64_t)Tmax * NBmax;
-        hp.CT = 16 * (int)std::max<int64_t>(1, (work + (16ll << 14) - 1) / (16ll << 14));
+        hp.CT = 16 * (int)std::max<int64_t>(4, (work + (16ll << 14) - 1) / (16ll << 14));
     }
     hp.C = (Tmax + hp.CT - 1) / hp.CT;
     hp.rows = (int64_t)p->B * p->Hq * p->T;
