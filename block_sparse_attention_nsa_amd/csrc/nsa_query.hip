@@ -942,6 +942,16 @@ static bool q_sync(const HostProblem& hp) {
     return (int64_t)hp.dev.S * hp.dev.bs >= (int64_t)hp.dev.Tmax;
 }
 
+// The forward also takes the barrier walk when a tile holds 4 or more tokens
+// (G <= 4): a tile then needs most of its workgroup's jobs even on sparse
+// lists, and a barrier per job costs less than the counters (8 packed
+// sequences, 32 / 8 heads, 16 blocks per row: forward 0.364 -> 0.340 ms; with
+// 16 heads per tile, one token, the barrier walk took 0.346 -> 0.641 ms).
+// dQ measured the same either way and keeps the counters.
+static bool fwd_sync(const HostProblem& hp) {
+    return q_sync(hp) || hp.dev.G <= 4;
+}
+
 hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, const void* v,
                            const int* block_idx, void* o, float* lse, hipStream_t st) {
     const QGeo qg = q_geo(hp, kRT_F, kNW_F);
@@ -955,7 +965,7 @@ hipError_t launch_fwd_bf16(const HostProblem& hp, const void* q, const void* k, 
     };
     const bool win = hp.dev.window > 0;
     NSA_Q_DISPATCH(hp.dev.D, hp.dev.bs,
-                   if (q_sync(hp)) {
+                   if (fwd_sync(hp)) {
                        if (win) go(fwd_q_kernel<D, BS, kRT_F, kNW_F, true, true>);
                        else go(fwd_q_kernel<D, BS, kRT_F, kNW_F, true, false>);
                    } else {
