@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_pins as pins
 import test_oracle_sink as sink_pins
+import test_oracle_subsets as subset_pins
 import test_oracle_window as window_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "nsa_oracle.c")
@@ -38,6 +39,9 @@ MUTANTS = {
     "sink ignored on empty rows": ("if (n == 0) return sk;", "if (n == 0) return -INFINITY;"),
     "window off by one": ("j > t - sh->window) keys[n++] = j;", "j >= t - sh->window) keys[n++] = j;"),
     "dkdv ignores the window": ("if (sh->window > 0 && t >= j + sh->window) break;", ";"),
+    # the subset calls: a listed row / key computed as if the list were absent
+    "row list ignored": ("int64_t r = rows ? rows[i] : i;", "int64_t r = i;"),
+    "key list ignored": ("int64_t r = keys ? keys[i] : i;", "int64_t r = i;"),
 }
 
 
@@ -70,6 +74,8 @@ CHECKS = [
     lambda: sink_pins.test_sink_closed_forms_and_empty_rows(),
     lambda: window_pins.test_window_finite_differences(window_pins.WTINY[0]),
     lambda: window_pins.test_window_dense_autograd(41, 2, 4, 2, 40, 8, 4, 5, 7),
+    lambda: subset_pins.test_row_and_key_subsets_equal_full_call(),
+    lambda: subset_pins.test_packed_batch_equals_block_diagonal_autograd(subset_pins.PACKED[0]),
 ]
 
 
