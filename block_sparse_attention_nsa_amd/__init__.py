@@ -10,7 +10,10 @@ Layouts (page 1 of the reference text, run_one): dense q/dO [B, Hq, T, D],
 k/v [B, Hkv, T, D], block_idx [B, Hkv, T, S] int32.  Packed sequences
 (page 3, cumulative sequence lengths): q [T, Hq, D], k/v [T, Hkv, D],
 block_idx [Hkv, T, S] with sequence-local block numbers, cu_seqlens int32
-[n_seqs + 1] on the device.
+[n_seqs + 1] on the device.  q, k, v, o, dO and the gradients may be strided
+views (e.g. a [B, T, H, D] buffer transposed to [B, H, T, D]) as long as the
+last dimension is contiguous: their strides are passed to the library, which
+checks them.  block_idx, lse and cu_seqlens must be contiguous.
 """
 from __future__ import annotations
 
@@ -29,6 +32,8 @@ __all__ = [
     "nsa_sel_check_block_idx",
     "bwd_workspace_bytes",
     "make_problem",
+    "set_strides",
+    "wait_timeouts",
     "selection_attn",
     "SelectionAttn",
 ]
@@ -44,10 +49,33 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+_STRIDE_FIELDS = {"q": "stride_q", "k": "stride_k", "v": "stride_v", "o": "stride_o",
+                  "dO": "stride_do", "dq": "stride_dq", "dk": "stride_dk", "dv": "stride_dv"}
+
+
+def set_strides(p: _lib.Problem, **tensors: Optional[torch.Tensor]) -> _lib.Problem:
+    """Record the (batch entry, head, token) element strides of the given
+    tensors (names q, k, v, o, dO, dq, dk, dv) in the problem and mark it
+    strided.  Dense tensors are [B, H, T, D] views, packed ones [T, H, D]."""
+    p.strided = 1
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous (stride {t.stride(-1)})")
+        arr = getattr(p, _STRIDE_FIELDS[name])
+        if t.dim() == 4:
+            arr[0], arr[1], arr[2] = t.stride(0), t.stride(1), t.stride(2)
+        else:
+            arr[0], arr[1], arr[2] = 0, t.stride(1), t.stride(0)
+    return p
+
+
 def make_problem(q: torch.Tensor, k: torch.Tensor, block_idx: torch.Tensor, block_size: int,
                  scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
                  max_seqlen: Optional[int] = None, window: int = 0) -> _lib.Problem:
-    """The nsa_sel_problem describing these tensors."""
+    """The nsa_sel_problem describing these tensors (contiguous layouts until
+    set_strides records the actual strides)."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"q dtype {q.dtype} is not float32 or bfloat16")
     p = _lib.Problem()
@@ -82,8 +110,6 @@ def _check_tensors(q, k, v, block_idx, cu_seqlens, p: _lib.Problem):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != q.dtype:
             raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if k.shape != v.shape:
         raise ValueError("k and v shapes differ")
     if block_idx.dtype != torch.int32 or not block_idx.is_contiguous():
@@ -114,7 +140,12 @@ def nsa_sel_fwd(q, k, v, block_idx, block_size, scale=None, cu_seqlens=None, max
     p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
     lse_t = torch.empty(_lse_shape(q, cu_seqlens), dtype=torch.float32, device=q.device) if lse is None else lse
+    if not lse_t.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    set_strides(p, q=q, k=k, v=v, o=o)
     lib = _lib.load()
     if sink is None:
         st = lib.nsa_sel_fwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(cu_seqlens),
@@ -144,8 +175,8 @@ def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqle
     p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     for name, t in (("o", o), ("dO", dO)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must match q in shape, dtype and contiguity")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
     if lse.dtype != torch.float32 or not lse.is_contiguous():
         raise TypeError("lse must be a contiguous float32 tensor")
     nbytes = bwd_workspace_bytes(p)
@@ -155,6 +186,10 @@ def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqle
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{name} must match the shape and dtype of its input")
+    set_strides(p, q=q, k=k, v=v, o=o, dO=dO, dq=dq, dk=dk, dv=dv)
     st = _lib.load().nsa_sel_bwd(p, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO),
                                  _ptr(block_idx), _ptr(cu_seqlens), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(ws), ws.numel(), _stream())
@@ -182,14 +217,17 @@ class BwdStages:
         self.ws = torch.empty(max(bwd_workspace_bytes(self.p), 1), dtype=torch.uint8,
                               device=q.device)
         self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        set_strides(self.p, q=q, k=k, v=v, dq=self.dq, dk=self.dk, dv=self.dv)
         self.lib = _lib.load()
 
     def prepare(self, o, dO):
+        set_strides(self.p, o=o, dO=dO)
         st = self.lib.nsa_sel_bwd_prepare(self.p, _ptr(o), _ptr(dO), _ptr(self.idx),
                                           _ptr(self.cu), _ptr(self.ws), self.ws.numel(), _stream())
         _lib.check("nsa_sel_bwd_prepare", st)
 
     def dq_stage(self, dO, lse):
+        set_strides(self.p, dO=dO)
         st = self.lib.nsa_sel_bwd_dq(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(dO),
                                      _ptr(lse), _ptr(self.idx), _ptr(self.cu), _ptr(self.dq),
                                      _ptr(self.ws), self.ws.numel(), _stream())
@@ -197,6 +235,7 @@ class BwdStages:
         return self.dq
 
     def dkdv_stage(self, dO, lse):
+        set_strides(self.p, dO=dO)
         st = self.lib.nsa_sel_bwd_dkdv(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v),
                                        _ptr(dO), _ptr(lse), _ptr(self.cu), _ptr(self.dk),
                                        _ptr(self.dv), _ptr(self.ws), self.ws.numel(), _stream())
@@ -205,6 +244,7 @@ class BwdStages:
 
     def dkdv_blocks(self, dO, lse):
         """First kernel of the dK/dV stage (nsa_sel_bwd_dkdv_blocks)."""
+        set_strides(self.p, dO=dO)
         st = self.lib.nsa_sel_bwd_dkdv_blocks(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v),
                                               _ptr(dO), _ptr(lse), _ptr(self.cu), _ptr(self.dk),
                                               _ptr(self.dv), _ptr(self.ws), self.ws.numel(),
@@ -231,6 +271,7 @@ class BwdStages:
 def nsa_sel_delta(o, dO, block_size, block_idx, k, scale=None, cu_seqlens=None, max_seqlen=None):
     """Delta = rowsum(dO * o) (nsa_sel_delta), laid out like lse."""
     p = make_problem(o, k, block_idx, block_size, scale, cu_seqlens, max_seqlen)
+    set_strides(p, o=o, dO=dO)
     delta = torch.empty(_lse_shape(o, cu_seqlens), dtype=torch.float32, device=o.device)
     st = _lib.load().nsa_sel_delta(p, _ptr(o), _ptr(dO), _ptr(cu_seqlens), _ptr(delta), _stream())
     _lib.check("nsa_sel_delta", st)
@@ -265,6 +306,17 @@ def nsa_sel_check_block_idx(q, k, block_idx, block_size, cu_seqlens=None, max_se
     _lib.check("nsa_sel_check_block_idx", st)
     c = counts.cpu().tolist()
     return {"padding": c[0], "out_of_range": c[1], "future": c[2], "repeated": c[3]}
+
+
+def wait_timeouts() -> int:
+    """Bounded in-kernel waits that gave up on the current device since the
+    library was loaded (nsa_sel_wait_timeouts); 0 is the only healthy value.
+    Synchronises the device."""
+    import ctypes
+    n = ctypes.c_uint64(0)
+    st = _lib.load().nsa_sel_wait_timeouts(ctypes.byref(n))
+    _lib.check("nsa_sel_wait_timeouts", st)
+    return int(n.value)
 
 
 class SelectionAttn(torch.autograd.Function):

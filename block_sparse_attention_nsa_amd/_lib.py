@@ -27,6 +27,7 @@ EXPORTS = (
     "nsa_sel_check_block_idx",
     "nsa_sel_fwd_sink",
     "nsa_sel_bwd_dsink",
+    "nsa_sel_wait_timeouts",
     "nsa_status_string",
     "nsa_last_error",
 )
@@ -48,6 +49,15 @@ class Problem(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("window", ctypes.c_int32),
+        ("strided", ctypes.c_int32),
+        ("stride_q", ctypes.c_int64 * 3),
+        ("stride_k", ctypes.c_int64 * 3),
+        ("stride_v", ctypes.c_int64 * 3),
+        ("stride_o", ctypes.c_int64 * 3),
+        ("stride_do", ctypes.c_int64 * 3),
+        ("stride_dq", ctypes.c_int64 * 3),
+        ("stride_dk", ctypes.c_int64 * 3),
+        ("stride_dv", ctypes.c_int64 * 3),
     ]
 
 
@@ -100,6 +110,8 @@ def load():
     lib.nsa_sel_fwd_sink.restype = st
     lib.nsa_sel_bwd_dsink.argtypes = [P, fp, fp, ip, fp, vp, sz, vp]
     lib.nsa_sel_bwd_dsink.restype = st
+    lib.nsa_sel_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    lib.nsa_sel_wait_timeouts.restype = st
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "nsa_internal.h"
@@ -80,6 +81,13 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     if (ZH > 8192) return fail(NSA_ERR_UNSUPPORTED, "(batch or sequences) * Hkv = %lld exceeds 8192", (long long)ZH);
     const int64_t idx_rows = (int64_t)p->B * p->Hkv * p->T;
     const int64_t Smin = std::min<int64_t>(p->S, std::max<int64_t>(NBmax, 1));
+    // The inverted lists of one (z, hkv) hold up to Tmax * Smin entries,
+    // addressed with 32-bit offsets (scans, cursors, the fill's positions).
+    if ((int64_t)Tmax * Smin >= (1ll << 31))
+        return fail(NSA_ERR_UNSUPPORTED, "max length * min(S, NBmax) = %lld list entries per (batch, KV head) "
+                    "exceeds 2^31 - 1", (long long)Tmax * Smin);
+    if (p->strided != 0 && p->strided != 1)
+        return fail(NSA_ERR_INVALID_ARG, "strided=%d is not 0 or 1", p->strided);
 
     nsa::Problem& d = hp.dev;
     d.B = p->B; d.T = p->T; d.Hq = p->Hq; d.Hkv = p->Hkv; d.G = G; d.D = p->D; d.S = p->S;
@@ -87,6 +95,33 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     d.Smin = (int)Smin; d.scale = p->scale; d.scale_log2 = p->scale * nsa::kLog2e; d.cu = nullptr;
     d.sink = nullptr;
     d.window = p->window;
+    // Element strides (batch entry, head, token) of the eight tensors.
+    {
+        const int64_t D = p->D, T = p->T;
+        auto dflt = [&](int64_t H) {
+            // (32-bit head / token strides: check_qk bounds them before any use)
+            return packed ? nsa::TLayout{0, (int32_t)D, (int32_t)(H * D)}
+                          : nsa::TLayout{H * T * D, (int32_t)(T * D), (int32_t)D};
+        };
+        auto given = [&](const int64_t* x) {
+            auto c32 = [](int64_t v) { return (int32_t)std::max<int64_t>(-1, std::min<int64_t>(v, INT32_MAX)); };
+            return nsa::TLayout{packed ? 0 : x[0], c32(x[1]), c32(x[2])};
+        };
+        const bool st = p->strided == 1;
+        d.strided = st ? 1 : 0;
+        const int64_t* src[8] = {p->stride_q, p->stride_k, p->stride_v, p->stride_o,
+                                 p->stride_do, p->stride_dq, p->stride_dk, p->stride_dv};
+        for (int i = 0; i < 8; ++i)
+            for (int j = 0; j < 3; ++j) hp.given[i][j] = st ? src[i][j] : 0;
+        d.lq = st ? given(p->stride_q) : dflt(p->Hq);
+        d.lo = st ? given(p->stride_o) : dflt(p->Hq);
+        d.ldo = st ? given(p->stride_do) : dflt(p->Hq);
+        d.ldq = st ? given(p->stride_dq) : dflt(p->Hq);
+        d.lk = st ? given(p->stride_k) : dflt(p->Hkv);
+        d.lv = st ? given(p->stride_v) : dflt(p->Hkv);
+        d.ldk = st ? given(p->stride_dk) : dflt(p->Hkv);
+        d.ldv = st ? given(p->stride_dv) : dflt(p->Hkv);
+    }
     hp.dtype = p->dtype;
     hp.ZH = (int)ZH;
     // Inversion chunks of CT tokens: at least 64 (smaller chunks multiply the
@@ -160,6 +195,74 @@ nsa_status check_tensor(const void* ptr, int64_t elems, size_t align, const char
     return NSA_OK;
 }
 
+// The eight tensors with a (batch entry, head, token, D) layout.
+enum Which { kQ, kK, kV, kO, kDO, kDQ, kDK, kDV };
+const char* const kWhichName[] = {"q", "k", "v", "o", "dO", "dq", "dk", "dv"};
+
+const nsa::TLayout& layout_of(const nsa::Problem& d, Which w) {
+    switch (w) {
+        case kQ: return d.lq;
+        case kK: return d.lk;
+        case kV: return d.lv;
+        case kO: return d.lo;
+        case kDO: return d.ldo;
+        case kDQ: return d.ldq;
+        case kDK: return d.ldk;
+        default: return d.ldv;
+    }
+}
+
+// Pointer, alignment and strides of one of the eight tensors.  Strides are
+// >= 0, multiples of 8 elements for bf16 (every row 16-byte aligned), the
+// token stride at most 2^24 (the kernels form 32-bit byte offsets of up to
+// 64 consecutive tokens), and one batch entry spans less than 2^31 elements
+// (offsets inside an entry are 32-bit).  Outputs
+// must map distinct (entry, head, token, d) to distinct elements: with the
+// dimensions sorted by stride, each stride reaches past everything the
+// smaller ones span.
+nsa_status check_qk(const nsa::HostProblem& hp, Which w, const void* ptr) {
+    const nsa::Problem& d = hp.dev;
+    const char* name = kWhichName[w];
+    const bool qlike = w == kQ || w == kO || w == kDO || w == kDQ;
+    const int64_t nb = d.packed ? 1 : d.B, nh = qlike ? d.Hq : d.Hkv, nt = d.T, D = d.D;
+    if (nb * nh * nt == 0) return NSA_OK;
+    if (!ptr) return fail(NSA_ERR_INVALID_ARG, "%s is NULL", name);
+    const bool bf16 = hp.dtype == NSA_BF16;
+    if (misaligned(ptr, bf16 ? 16 : 4))
+        return fail(NSA_ERR_INVALID_ARG, "%s is not %d-byte aligned", name, bf16 ? 16 : 4);
+    const nsa::TLayout& L = layout_of(d, w);
+    const int64_t* x = d.strided ? hp.given[w] : nullptr;
+    const int64_t sb = x ? (d.packed ? 0 : x[0]) : L.sb, sh0 = x ? x[1] : L.sh, st0 = x ? x[2] : L.st;
+    if (sb < 0 || sh0 < 0 || st0 < 0)
+        return fail(NSA_ERR_INVALID_ARG, "%s strides (%lld, %lld, %lld) must be >= 0", name,
+                    (long long)sb, (long long)sh0, (long long)st0);
+    if (bf16 && (sb % 8 || sh0 % 8 || st0 % 8))
+        return fail(NSA_ERR_INVALID_ARG, "%s strides (%lld, %lld, %lld) are not multiples of 8 "
+                    "(bf16 rows must be 16-byte aligned)", name, (long long)sb, (long long)sh0,
+                    (long long)st0);
+    // (The 32-bit device strides were clamped; read the caller's values.)
+    const int64_t sh = d.strided ? hp.given[w][1] : L.sh, stt = d.strided ? hp.given[w][2] : L.st;
+    if (stt > (1ll << 24))
+        return fail(NSA_ERR_UNSUPPORTED, "%s token stride %lld exceeds 2^24 elements", name, (long long)stt);
+    const int64_t entry = (nh - 1) * sh + (nt - 1) * stt + D;
+    if (entry >= (1ll << 31))
+        return fail(NSA_ERR_UNSUPPORTED, "%s spans %lld elements per batch entry (limit 2^31 - 1)",
+                    name, (long long)entry);
+    if (w == kO || w == kDQ || w == kDK || w == kDV) {
+        struct Dim { int64_t n, s; } dims[4] = {{D, 1}, {nb, sb}, {nh, sh}, {nt, stt}};
+        std::sort(dims, dims + 4, [](const Dim& a, const Dim& b) { return a.s < b.s; });
+        int64_t span = 0;  // elements spanned by the dimensions taken so far, minus 1
+        for (const Dim& x : dims) {
+            if (x.n <= 1) continue;
+            if (x.s <= span)
+                return fail(NSA_ERR_INVALID_ARG, "output %s has overlapping rows (stride %lld within "
+                            "a span of %lld elements)", name, (long long)x.s, (long long)span + 1);
+            span += (x.n - 1) * x.s;
+        }
+    }
+    return NSA_OK;
+}
+
 struct Sizes {
     int64_t q, kv, idx, lse;
 };
@@ -168,8 +271,6 @@ Sizes sizes_of(const nsa::HostProblem& hp) {
     return {(int64_t)d.B * d.Hq * d.T * d.D, (int64_t)d.B * d.Hkv * d.T * d.D,
             (int64_t)d.B * d.Hkv * d.T * d.S, (int64_t)d.B * d.Hq * d.T};
 }
-
-size_t elem_align(const nsa::HostProblem& hp) { return hp.dtype == NSA_BF16 ? 16 : 4; }
 
 #define NSA_TRY(x)                       \
     do {                                 \
@@ -202,18 +303,15 @@ nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProble
     NSA_TRY(make_problem(p, hp));
     NSA_TRY(check_cu(hp, a.cu));
     const Sizes sz = sizes_of(hp);
-    const size_t al = elem_align(hp);
     const struct {
         const void* ptr;
-        int64_t n;
-        size_t al;
-        const char* name;
-    } ts[] = {{a.q, sz.q, al, "q"},     {a.k, sz.kv, al, "k"},      {a.v, sz.kv, al, "v"},
-              {a.o, sz.q, al, "o"},     {a.dO, sz.q, al, "dO"},     {a.dq, sz.q, al, "dq"},
-              {a.dk, sz.kv, al, "dk"},  {a.dv, sz.kv, al, "dv"},    {a.lse, sz.lse, 4, "lse"},
-              {a.idx, sz.idx, 4, "block_idx"}};
+        Which w;
+    } ts[] = {{a.q, kQ}, {a.k, kK}, {a.v, kV}, {a.o, kO}, {a.dO, kDO}, {a.dq, kDQ}, {a.dk, kDK},
+              {a.dv, kDV}};
     for (const auto& t : ts)
-        if (t.ptr != kAbsent) NSA_TRY(check_tensor(t.ptr, t.n, t.al, t.name));
+        if (t.ptr != kAbsent) NSA_TRY(check_qk(hp, t.w, t.ptr));
+    if (a.lse != kAbsent) NSA_TRY(check_tensor(a.lse, sz.lse, 4, "lse"));
+    if (a.idx != kAbsent) NSA_TRY(check_tensor(a.idx, sz.idx, 4, "block_idx"));
     const nsa::BwdWorkspace need = carve(hp, nullptr);
     if (need.bytes && (!a.ws || a.ws_bytes < need.bytes))
         return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a.ws_bytes, need.bytes);
@@ -279,6 +377,16 @@ const char* nsa_status_string(nsa_status s) {
 
 const char* nsa_last_error(void) { return g_last_error.c_str(); }
 
+nsa_status nsa_sel_wait_timeouts(uint64_t* count) {
+    g_last_error.clear();
+    if (!count) return fail(NSA_ERR_INVALID_ARG, "count is NULL");
+    unsigned a = 0, b = 0;
+    NSA_HIP(nsa::read_wait_timeouts_query(&a), "reading the query kernels' wait counter");
+    NSA_HIP(nsa::read_wait_timeouts_dkdv(&b), "reading the dK/dV kernel's wait counter");
+    *count = (uint64_t)a + b;
+    return NSA_OK;
+}
+
 nsa_status nsa_sel_fwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
                        const int32_t* block_idx, const int32_t* cu_seqlens, void* o, float* lse,
                        nsa_stream_t stream) {
@@ -295,11 +403,10 @@ nsa_status nsa_sel_fwd_sink(const nsa_sel_problem* p, const void* q, const void*
     if (sink) NSA_TRY(check_tensor(sink, hp.dev.Hq, 4, "sink"));
     hp.dev.sink = sink;
     const Sizes sz = sizes_of(hp);
-    const size_t a = elem_align(hp);
-    NSA_TRY(check_tensor(q, sz.q, a, "q"));
-    NSA_TRY(check_tensor(k, sz.kv, a, "k"));
-    NSA_TRY(check_tensor(v, sz.kv, a, "v"));
-    NSA_TRY(check_tensor(o, sz.q, a, "o"));
+    NSA_TRY(check_qk(hp, kQ, q));
+    NSA_TRY(check_qk(hp, kK, k));
+    NSA_TRY(check_qk(hp, kV, v));
+    NSA_TRY(check_qk(hp, kO, o));
     NSA_TRY(check_tensor(block_idx, sz.idx, 4, "block_idx"));
     NSA_TRY(check_tensor(lse, sz.lse, 4, "lse"));
     if (sz.q == 0) return NSA_OK;
@@ -344,9 +451,8 @@ nsa_status nsa_sel_delta(const nsa_sel_problem* p, const void* o, const void* dO
     NSA_TRY(make_problem(p, hp));
     NSA_TRY(check_cu(hp, cu_seqlens));
     const Sizes sz = sizes_of(hp);
-    const size_t a = elem_align(hp);
-    NSA_TRY(check_tensor(o, sz.q, a, "o"));
-    NSA_TRY(check_tensor(dO, sz.q, a, "dO"));
+    NSA_TRY(check_qk(hp, kO, o));
+    NSA_TRY(check_qk(hp, kDO, dO));
     NSA_TRY(check_tensor(delta, sz.lse, 4, "delta"));
     if (sz.q == 0) return NSA_OK;
     hp.dev.cu = cu_seqlens;

@@ -16,8 +16,17 @@ namespace nsa {
 
 // ---- Delta ----------------------------------------------------------------
 
+// Row r of lse / delta ([B][Hq][T] dense, [Hq][T] packed) -> element
+// offsets of its rows in o and dO.
+__device__ __forceinline__ void delta_row_offsets(const Problem& p, int64_t r, int64_t& oo,
+                                                  int64_t& od) {
+    const int64_t t = r % p.T, bh = r / p.T, h = bh % p.Hq, b = bh / p.Hq;
+    oo = b * p.lo.sb + h * p.lo.sh + t * p.lo.st;
+    od = b * p.ldo.sb + h * p.ldo.sh + t * p.ldo.st;
+}
+
 // bf16 rows: D/8 lanes per row, 16-byte loads, fp32 products and sums; one
-// 256-thread block covers rows [blk * 256 / (D/8), ...).
+// 256-thread block covers rows [blk * 256 / (D/8), ...) in lse order.
 template <int D>
 __device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t* __restrict__ o,
                                                 const uint16_t* __restrict__ dO,
@@ -28,8 +37,10 @@ __device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t
     int part = threadIdx.x % TPR;
     float acc = 0.f;
     if (r < nrows) {
-        uint4 a = ldg16(o + r * D + part * 8);
-        uint4 b = ldg16(dO + r * D + part * 8);
+        int64_t oo, od;
+        delta_row_offsets(p, r, oo, od);
+        uint4 a = ldg16(o + oo + part * 8);
+        uint4 b = ldg16(dO + od + part * 8);
         const uint32_t av[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -40,14 +51,7 @@ __device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t
     }
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
-    if (r < nrows && part == 0) {
-        int64_t out = r;
-        if (p.packed) {  // q rows are (token, h); delta is [Hq][T]
-            int64_t tok = r / p.Hq, h = r % p.Hq;
-            out = h * p.T + tok;
-        }
-        delta[out] = acc;
-    }
+    if (r < nrows && part == 0) delta[r] = acc;
 }
 
 template <int D>
@@ -65,14 +69,11 @@ __global__ __launch_bounds__(256) void delta_f32_kernel(Problem p, const float* 
                                                         float* __restrict__ delta, int64_t nrows) {
     int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= nrows) return;
+    int64_t oo, od;
+    delta_row_offsets(p, r, oo, od);
     float acc = 0.f;
-    for (int d = 0; d < p.D; ++d) acc += o[r * p.D + d] * dO[r * p.D + d];
-    int64_t out = r;
-    if (p.packed) {
-        int64_t tok = r / p.Hq, h = r % p.Hq;
-        out = h * p.T + tok;
-    }
-    delta[out] = acc;
+    for (int d = 0; d < p.D; ++d) acc += o[oo + d] * dO[od + d];
+    delta[r] = acc;
 }
 
 hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, float* delta,

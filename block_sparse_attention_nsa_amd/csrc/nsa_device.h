@@ -21,6 +21,15 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Element strides of one tensor: batch entry (dense only), head, token.  The
+// last dimension (D) is contiguous.  Packed tensors have their sequences back
+// to back along the token dimension.  The host checks that one batch entry
+// spans less than 2^31 elements, so offsets inside an entry are 32-bit.
+struct TLayout {
+    int64_t sb;
+    int32_t sh, st;
+};
+
 // Everything a kernel needs to know about the problem (passed by value).
 struct Problem {
     int B, T, Hq, Hkv, G, D, S, bs;
@@ -34,17 +43,20 @@ struct Problem {
     const int* cu;
     const float* sink;  // [Hq] per-head sink logits (natural log), or null
     int window;         // sliding window: keys t - window < j <= t; 0 = none
+    int strided;        // the layouts below were declared by the caller
+    // Layouts of q, k, v, o, dO, dq, dk, dv (lse / delta are contiguous).
+    TLayout lq, lk, lv, lo, ldo, ldq, ldk, ldv;
 };
 
-// Where sequence z lives.  Offsets are in elements; "rows" of block_idx and
-// lse/delta are counted in their own arrays.  Packed lengths are clamped so
-// every access stays inside the T-token arrays whatever cu holds.
+// Where sequence z lives: its first token along the token dimension (packed)
+// and its batch entry (dense).  Packed lengths are clamped so every access
+// stays inside the T-token arrays whatever cu holds.  block_idx rows and
+// lse / delta entries are counted in their own (contiguous) arrays.
 struct Seq {
     int start, len;
-    int64_t q_base, q_sh, q_st;    // q/o/dO/dq: element offset of (h, t)
-    int64_t k_base, k_sh, k_st;    // k/v/dk/dv
-    int64_t i_base;                // block_idx row of (hkv, t) = i_base + hkv*T + t
-    int64_t l_base;                // lse/delta index of (h, t)  = l_base + h*T + t
+    int zb;            // batch entry of the dense layouts (0 when packed)
+    int64_t i_base;    // block_idx row of (hkv, t) = i_base + hkv*T + t
+    int64_t l_base;    // lse/delta index of (h, t)  = l_base + h*T + t
 };
 
 __device__ __forceinline__ Seq seq_of(const Problem& p, int z) {
@@ -55,34 +67,26 @@ __device__ __forceinline__ Seq seq_of(const Problem& p, int z) {
         b = min(max(b, a), p.T);
         s.start = a;
         s.len = min(b - a, p.Tmax);
-        s.q_base = (int64_t)a * p.Hq * p.D;
-        s.q_sh = p.D;
-        s.q_st = (int64_t)p.Hq * p.D;
-        s.k_base = (int64_t)a * p.Hkv * p.D;
-        s.k_sh = p.D;
-        s.k_st = (int64_t)p.Hkv * p.D;
+        s.zb = 0;
         s.i_base = a;
         s.l_base = a;
     } else {
         s.start = 0;
         s.len = p.T;
-        s.q_base = (int64_t)z * p.Hq * p.T * p.D;
-        s.q_sh = (int64_t)p.T * p.D;
-        s.q_st = p.D;
-        s.k_base = (int64_t)z * p.Hkv * p.T * p.D;
-        s.k_sh = (int64_t)p.T * p.D;
-        s.k_st = p.D;
+        s.zb = z;
         s.i_base = (int64_t)z * p.Hkv * p.T;
         s.l_base = (int64_t)z * p.Hq * p.T;
     }
     return s;
 }
 
-__device__ __forceinline__ int64_t q_off(const Seq& s, int h, int t) {
-    return s.q_base + h * s.q_sh + (int64_t)t * s.q_st;
+// Element offset of row (h, t) of sequence s in a tensor of layout L, and of
+// its token-0 row (the base the token stride is added to).
+__device__ __forceinline__ int64_t row_off(const TLayout& L, const Seq& s, int h, int t) {
+    return (int64_t)s.zb * L.sb + (h * L.sh + (s.start + t) * L.st);
 }
-__device__ __forceinline__ int64_t k_off(const Seq& s, int h, int t) {
-    return s.k_base + h * s.k_sh + (int64_t)t * s.k_st;
+__device__ __forceinline__ int64_t head_base(const TLayout& L, const Seq& s, int h) {
+    return row_off(L, s, h, 0);
 }
 __device__ __forceinline__ int64_t l_off(const Problem& p, const Seq& s, int h, int t) {
     return s.l_base + (int64_t)h * p.T + t;
@@ -236,18 +240,26 @@ __device__ __forceinline__ uint32_t lds_addr(const int* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)p;
 }
 
+// Waits of spin_ge that gave up, per source file that waits (each file has
+// its own copy; nsa_sel_wait_timeouts() reads them).  Never expected: a
+// nonzero count means a launch computed from a stage that may not have been
+// complete.
+static __device__ unsigned int g_wait_timeouts;
+
 // Waits until the LDS counter reaches target.  Callers make sure the waves
 // that add to it always get there, so the wait ends; the iteration cap only
-// bounds it should that ever fail.  The counter is read with a plain
-// ds_read_b32 in asm: to the compiler it is unrelated to the stages that
-// buffer-to-LDS loads are filling, so it adds no vector-memory wait.
+// bounds it should that ever fail, and then the give-up is counted in
+// g_wait_timeouts.  The counter is read with a plain ds_read_b32 in asm: to
+// the compiler it is unrelated to the stages that buffer-to-LDS loads are
+// filling, so it adds no vector-memory wait.
 __device__ __forceinline__ void spin_ge(const int* ctr, int target) {
     const uint32_t a = lds_addr(ctr);
     for (int it = 0; it < (1 << 18); ++it) {
         int v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-        if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+        if (__builtin_amdgcn_readfirstlane(v) >= target) return;
     }
+    if (__lane_id() == 0) atomicAdd(&g_wait_timeouts, 1u);
 }
 // One count from this wave (LDS operations of a wave are processed in order,
 // so its earlier LDS reads and writes are done first).

@@ -203,11 +203,12 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
             const bool in = key < s.len;
-            const int64_t ko = k_off(s, hkv, in ? key : 0);
+            const uint16_t* kr = k + row_off(p.lk, s, hkv, in ? key : 0) + 8 * g;
+            const uint16_t* vr = v + row_off(p.lv, s, hkv, in ? key : 0) + 8 * g;
 #pragma unroll
             for (int kk = 0; kk < KD; ++kk) {
-                kf[kt][kk] = in ? as_bf16x8(ldg16(k + ko + 32 * kk + 8 * g)) : as_bf16x8(make_uint4(0, 0, 0, 0));
-                vf[kt][kk] = in ? as_bf16x8(ldg16(v + ko + 32 * kk + 8 * g)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+                kf[kt][kk] = in ? as_bf16x8(ldg16(kr + 32 * kk)) : as_bf16x8(make_uint4(0, 0, 0, 0));
+                vf[kt][kk] = in ? as_bf16x8(ldg16(vr + 32 * kk)) : as_bf16x8(make_uint4(0, 0, 0, 0));
             }
         }
         uint32_t a_off[KD];
@@ -318,20 +319,22 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     // Buffers of this (z, kv group): rows (h, t) of q / dO and lse / Delta.
     // Every valid row lies below the sizes; invalid rows use an offset past
     // them and load zeros.
-    const uint16_t* qb = q + s.q_base + (int64_t)(hkv * G) * s.q_sh;
-    const uint16_t* db = dO + s.q_base + (int64_t)(hkv * G) * s.q_sh;
-    const int64_t q_elems = (int64_t)(G - 1) * s.q_sh + (int64_t)(s.len - 1) * s.q_st + D;
+    const uint16_t* qb = q + head_base(p.lq, s, hkv * G);
+    const uint16_t* db = dO + head_base(p.ldo, s, hkv * G);
+    const int64_t q_elems = (int64_t)(G - 1) * p.lq.sh + (int64_t)(s.len - 1) * p.lq.st + D;
+    const int64_t d_elems = (int64_t)(G - 1) * p.ldo.sh + (int64_t)(s.len - 1) * p.ldo.st + D;
     const buf_rsrc rq = make_rsrc(qb, (uint32_t)(2 * q_elems));
-    const buf_rsrc rd = make_rsrc(db, (uint32_t)(2 * q_elems));
+    const buf_rsrc rd = make_rsrc(db, (uint32_t)(2 * d_elems));
     const int64_t l_first = s.l_base + (int64_t)(hkv * G) * p.T;
     const uint32_t l_bytes = (uint32_t)(4 * ((int64_t)(G - 1) * p.T + s.len));
     const buf_rsrc rl = make_rsrc(lse + l_first, l_bytes);
     const buf_rsrc rdl = make_rsrc(delta + l_first, l_bytes);
     constexpr uint32_t kOob = 0xFFFFFFF0u;
-    const uint32_t qsh_b = (uint32_t)(2 * s.q_sh), qst_b = (uint32_t)(2 * s.q_st);
+    // Byte strides of a head and of a token in q and in dO.
+    const uint32_t qsh_b = (uint32_t)(2 * p.lq.sh), qst_b = (uint32_t)(2 * p.lq.st);
+    const uint32_t dsh_b = (uint32_t)(2 * p.ldo.sh), dst_b = (uint32_t)(2 * p.ldo.st);
     const uint32_t lsh_b = (uint32_t)(4 * p.T);
     const int q32 = 32 / G, r32 = 32 % G;
-    const uint32_t q_r32 = (uint32_t)r32 * qsh_b, q_G = (uint32_t)G * qsh_b;
     const uint32_t l_r32 = (uint32_t)r32 * lsh_b, l_G = (uint32_t)G * lsh_b;
 
     // Rows this lane loads: 1 KB load jj = a + NP * j of a tile covers the
@@ -346,7 +349,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         const int pos = 64 * jj + lane;
         qrow[j] = pos / QCH;
         cofs[j] = 16u * (uint32_t)L::chunk(qrow[j], pos % QCH);
-        cq[j] = cursor_at(f_end - 32 + qrow[j], G, qsh_b);
+        cq[j] = cursor_at(f_end - 32 + qrow[j], G, 0u);
     }
     // Lanes < 32: row `lane` of each step, once for the token list (one step
     // ahead of the rows) and once for lse / Delta, into this accumulator's
@@ -376,12 +379,14 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         for (int j = 0; j < NJ; ++j) {
             const int jj = a + NP * j;
             if (kEven || jj < NI) {
-                const uint32_t vo = cq[j].f >= f_begin
-                                        ? cq[j].hoff + (uint32_t)tj[j] * qst_b + cofs[j] : kOob;
-                dma16(rq, reinterpret_cast<uint8_t*>(sg.q) + 1024 * jj, vo);
-                dma16(rd, reinterpret_cast<uint8_t*>(sg.dO) + 1024 * jj, vo);
+                const bool in = cq[j].f >= f_begin;
+                const uint32_t h = (uint32_t)cq[j].h, t = (uint32_t)tj[j];
+                const uint32_t vq = in ? h * qsh_b + t * qst_b + cofs[j] : kOob;
+                const uint32_t vd = in ? h * dsh_b + t * dst_b + cofs[j] : kOob;
+                dma16(rq, reinterpret_cast<uint8_t*>(sg.q) + 1024 * jj, vq);
+                dma16(rd, reinterpret_cast<uint8_t*>(sg.dO) + 1024 * jj, vd);
             }
-            retreat32(cq[j], G, q32, r32, q_r32, q_G);
+            retreat32(cq[j], G, q32, r32, 0u, 0u);
         }
         {
             const uint32_t lo = meta && cm.f >= f_begin ? cm.hoff + 4u * (uint32_t)tm : kOob;
@@ -488,14 +493,15 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
             if (key >= s.len) continue;
-            const int64_t ko = k_off(s, hkv, key);
+            uint16_t* dkr = dk + row_off(p.ldk, s, hkv, key) + 4 * g;
+            uint16_t* dvr = dv + row_off(p.ldv, s, hkv, key) + 4 * g;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
                 const f32x4 x = dkt[kt][dt], y = dvt[kt][dt];
-                *reinterpret_cast<uint2*>(dk + ko + 16 * dt + 4 * g) =
+                *reinterpret_cast<uint2*>(dkr + 16 * dt) =
                     make_uint2(pack_bf16x2(x[0] * p.scale, x[1] * p.scale),
                                pack_bf16x2(x[2] * p.scale, x[3] * p.scale));
-                *reinterpret_cast<uint2*>(dv + ko + 16 * dt + 4 * g) =
+                *reinterpret_cast<uint2*>(dvr + 16 * dt) =
                     make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             }
         }
@@ -587,7 +593,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
         const int dt = (x / 64) % ND, d = 16 * dt + 4 * ((x % 64) >> 4);
         const float m = plane == 0 ? p.scale : 1.f;
         const uint2 pk = make_uint2(pack_bf16x2(acc[q].x * m, acc[q].y * m), pack_bf16x2(acc[q].z * m, acc[q].w * m));
-        uint16_t* dst = (plane == 0 ? dk : dv) + k_off(s, hkv, key[q]) + d;
+        uint16_t* dst = plane == 0 ? dk + row_off(p.ldk, s, hkv, key[q]) + d
+                                   : dv + row_off(p.ldv, s, hkv, key[q]) + d;
         *reinterpret_cast<uint2*>(dst) = pk;
     }
 }
@@ -648,6 +655,12 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
                                              ws.partials, rs, (uint16_t*)dk, (uint16_t*)dv));
     }
     return hipGetLastError();
+}
+
+// Bounded waits of this file's kernels that gave up (see spin_ge).
+hipError_t read_wait_timeouts_dkdv(unsigned* out) {
+    return hipMemcpyFromSymbol(out, HIP_SYMBOL(g_wait_timeouts), sizeof(unsigned), 0,
+                               hipMemcpyDeviceToHost);
 }
 
 }  // namespace nsa

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
     const int hkv = h / p.G, NBz = (s.len + p.bs - 1) / p.bs;
     const int* row = idx_row(p, s, idx, hkv, t);
     float qv[D], acc[D];
-    const float* qr = q + q_off(s, h, t);
+    const float* qr = q + row_off(p.lq, s, h, t);
     for (int d = 0; d < D; ++d) {
         qv[d] = qr[d] * p.scale_log2;
         acc[d] = 0.f;
@@ -69,8 +69,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
         // Sliding window: keys t - window < j only.
         const int j0 = p.window > 0 ? max(u * p.bs, t - p.window + 1) : u * p.bs;
         for (int j = j0; j < j1; ++j) {
-            const float* kr = k + k_off(s, hkv, j);
-            const float* vr = v + k_off(s, hkv, j);
+            const float* kr = k + row_off(p.lk, s, hkv, j);
+            const float* vr = v + row_off(p.lv, s, hkv, j);
             float x = 0.f;
             for (int d = 0; d < D; ++d) x += qv[d] * kr[d];
             const float mn = fmaxf(m, x);
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
             m = mn;
         }
     }
-    float* orow = o + q_off(s, h, t);
+    float* orow = o + row_off(p.lo, s, h, t);
     float inv, lse_r;
     if (p.sink) {
         finish_row_sink(p.sink[h], m, l, inv, lse_r);
@@ -110,11 +110,13 @@ __global__ __launch_bounds__(128) void dq_f32_kernel(Problem p, const float* __r
     if (t < 0 || t >= s.len) return;
     const int hkv = h / p.G, NBz = (s.len + p.bs - 1) / p.bs;
     const int* row = idx_row(p, s, idx, hkv, t);
-    const int64_t ro = q_off(s, h, t), lo = l_off(p, s, h, t);
+    const int64_t lo = l_off(p, s, h, t);
+    const float* qr = q + row_off(p.lq, s, h, t);
+    const float* dr = dO + row_off(p.ldo, s, h, t);
     float qv[D], dov[D], acc[D];
     for (int d = 0; d < D; ++d) {
-        qv[d] = q[ro + d] * p.scale_log2;
-        dov[d] = dO[ro + d];
+        qv[d] = qr[d] * p.scale_log2;
+        dov[d] = dr[d];
         acc[d] = 0.f;
     }
     const float lse2 = lse[lo] * kLog2e, dl = delta[lo];
@@ -125,8 +127,8 @@ __global__ __launch_bounds__(128) void dq_f32_kernel(Problem p, const float* __r
         // Sliding window: keys t - window < j only.
         const int j0 = p.window > 0 ? max(u * p.bs, t - p.window + 1) : u * p.bs;
         for (int j = j0; j < j1; ++j) {
-            const float* kr = k + k_off(s, hkv, j);
-            const float* vr = v + k_off(s, hkv, j);
+            const float* kr = k + row_off(p.lk, s, hkv, j);
+            const float* vr = v + row_off(p.lv, s, hkv, j);
             float x = 0.f, dp = 0.f;
             for (int d = 0; d < D; ++d) {
                 x += qv[d] * kr[d];
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(128) void dq_f32_kernel(Problem p, const float* __r
             for (int d = 0; d < D; ++d) acc[d] += ds * kr[d];
         }
     }
-    for (int d = 0; d < D; ++d) dq[ro + d] = acc[d] * p.scale;
+    float* dqr = dq + row_off(p.ldq, s, h, t);
+    for (int d = 0; d < D; ++d) dqr[d] = acc[d] * p.scale;
 }
 
 // One thread per key (z, hkv, j): its block's inverted list gives the rows.
@@ -158,11 +161,12 @@ __global__ __launch_bounds__(128) void dkdv_f32_kernel(
     const int* off = offsets + (int64_t)zh * (p.NBmax + 1);
     const int* list = tokens + region_base(p, s, hkv) + off[u];
     const int cnt = off[u + 1] - off[u];
-    const int64_t ko = k_off(s, hkv, j);
+    const float* kr = k + row_off(p.lk, s, hkv, j);
+    const float* vr = v + row_off(p.lv, s, hkv, j);
     float kv[D], vv[D], ak[D], av[D];
     for (int d = 0; d < D; ++d) {
-        kv[d] = k[ko + d] * p.scale_log2;
-        vv[d] = v[ko + d];
+        kv[d] = kr[d] * p.scale_log2;
+        vv[d] = vr[d];
         ak[d] = 0.f;
         av[d] = 0.f;
     }
@@ -171,9 +175,9 @@ __global__ __launch_bounds__(128) void dkdv_f32_kernel(
         if (j > t || (p.window > 0 && t - p.window >= j)) continue;
         for (int gg = 0; gg < p.G; ++gg) {
             const int h = hkv * p.G + gg;
-            const int64_t ro = q_off(s, h, t), lo = l_off(p, s, h, t);
-            const float* qr = q + ro;
-            const float* dr = dO + ro;
+            const int64_t lo = l_off(p, s, h, t);
+            const float* qr = q + row_off(p.lq, s, h, t);
+            const float* dr = dO + row_off(p.ldo, s, h, t);
             float x = 0.f, dp = 0.f;
             for (int d = 0; d < D; ++d) {
                 x += qr[d] * kv[d];
@@ -187,9 +191,11 @@ __global__ __launch_bounds__(128) void dkdv_f32_kernel(
             }
         }
     }
+    float* dkr = dk + row_off(p.ldk, s, hkv, j);
+    float* dvr = dv + row_off(p.ldv, s, hkv, j);
     for (int d = 0; d < D; ++d) {
-        dk[ko + d] = ak[d] * p.scale;
-        dv[ko + d] = av[d];
+        dkr[d] = ak[d] * p.scale;
+        dvr[d] = av[d];
     }
 }
 

@@ -27,6 +27,9 @@ struct HostProblem {
     // the device, possible only without partial slots, for block_size <= 64,
     // bf16, and S * block_size >= the longest sequence.
     bool pair_possible;
+    // The caller's strides of q, k, v, o, dO, dq, dk, dv when the problem is
+    // strided (the device copies hold 32-bit head / token strides).
+    int64_t given[8][3];
 };
 
 // Backward workspace carve (all offsets 256-byte aligned).
@@ -90,6 +93,11 @@ hipError_t launch_dq_f32(const HostProblem& hp, const float* q, const float* k, 
 hipError_t launch_dkdv_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
                            const float* dO, const float* lse, const float* delta,
                            const BwdWorkspace& ws, float* dk, float* dv, hipStream_t st);
+
+// Give-ups of the bounded in-kernel waits of the query and dK/dV kernels on
+// the current device (synchronous reads of each file's counter).
+hipError_t read_wait_timeouts_query(unsigned* out);
+hipError_t read_wait_timeouts_dkdv(unsigned* out);
 
 // Dynamic LDS the bf16 forward / dQ kernels need (0 if unsupported).
 size_t query_lds_bytes(const HostProblem& hp);

@@ -93,15 +93,22 @@ __device__ __forceinline__ TileRow tile_row(const Problem& p, const QGeo& qg, in
     return x;
 }
 
-// Mask of the workgroup tokens of tile tau.
+// Mask of the workgroup tokens of tile tau (wave-uniform: stated with
+// readfirstlane so the mask lives in scalar registers; as a vector-register
+// pair it was spilled and reloaded inside the job loop, and a reload waits
+// for every load in flight, ring stages included).
 __device__ __forceinline__ uint64_t tile_tokens(const Problem& p, const QGeo& qg, int tau) {
+    uint64_t m;
     if (p.G >= 16) {
         const int a = tau / qg.n_ht;
-        return a < qg.TW ? 1ull << a : 0ull;
+        m = a < qg.TW ? 1ull << a : 0ull;
+    } else {
+        const int a = tau * qg.tpt;
+        m = a >= qg.TW ? 0ull : ((1ull << qg.tpt) - 1ull) << a;  // past the tokens: idle
     }
-    const int a = tau * qg.tpt;
-    if (a >= qg.TW) return 0ull;  // tile past the workgroup's tokens: idle
-    return ((1ull << qg.tpt) - 1ull) << a;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)m);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(m >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
 struct WgCoord {
@@ -266,13 +273,15 @@ struct KVLoad {
     uint32_t voff[NJ];   // byte offset of this lane's 16 bytes inside the slice
     int jj[NJ];          // load index (>= 2 NI: none)
     // w must be wave-uniform (it selects the descriptor of each load).
-    __device__ void init(int w, int lane, int kst2) {
+    // kst2 / vst2: byte strides between the keys of K / V.
+    __device__ void init(int w, int lane, int kst2, int vst2) {
         w = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             jj[j] = w + NW * j;
             const int pos = 64 * (jj[j] % NI) + lane, row = pos / L::QCH;
-            voff[j] = (uint32_t)(row * kst2 + 16 * L::chunk(row, pos % L::QCH));
+            voff[j] = (uint32_t)row * (uint32_t)(jj[j] < NI ? kst2 : vst2) +
+                      16u * (uint32_t)L::chunk(row, pos % L::QCH);
         }
     }
     // Loads this wave issues per job when it has its full share; kEven: all
@@ -283,13 +292,13 @@ struct KVLoad {
     // Issued for every job slot, also past the last job (ok == false): those
     // loads see an empty descriptor and write zeros into a free stage, so a
     // wave always has the same number of loads in flight.
-    __device__ void issue(const uint16_t* kb, const uint16_t* vb, int kst2, int j0, int len,
-                          bool ok, KVStage<D, JK>& st) const {
+    __device__ void issue(const uint16_t* kb, const uint16_t* vb, int kst2, int vst2, int j0,
+                          int len, bool ok, KVStage<D, JK>& st) const {
         j0 = ok ? j0 : 0;
-        const int64_t base = (int64_t)j0 * kst2;
-        const uint32_t bytes = ok ? (uint32_t)((int64_t)(len - 1 - j0) * kst2 + 2 * D) : 0u;
-        const buf_rsrc rk = make_rsrc(reinterpret_cast<const char*>(kb) + base, bytes);
-        const buf_rsrc rv = make_rsrc(reinterpret_cast<const char*>(vb) + base, bytes);
+        const uint32_t kbytes = ok ? (uint32_t)((int64_t)(len - 1 - j0) * kst2 + 2 * D) : 0u;
+        const uint32_t vbytes = ok ? (uint32_t)((int64_t)(len - 1 - j0) * vst2 + 2 * D) : 0u;
+        const buf_rsrc rk = make_rsrc(reinterpret_cast<const char*>(kb) + (int64_t)j0 * kst2, kbytes);
+        const buf_rsrc rv = make_rsrc(reinterpret_cast<const char*>(vb) + (int64_t)j0 * vst2, vbytes);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if constexpr (kEven) {
@@ -332,7 +341,7 @@ __device__ __forceinline__ void wait_vm() {
 // u-th use of a stage is complete at NW * (u + 1).
 template <int D, int BS, int NW, class Compute>
 __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const uint16_t* kb,
-                                       const uint16_t* vb, int kst2, int len,
+                                       const uint16_t* vb, int kst2, int vst2, int len,
                                        const uint16_t* ulist, int nU, int t_last, int lane,
                                        Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK, NS = kQStages, A = kQAhead;
@@ -358,7 +367,7 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
                     int* land_c, int* land_n, int* done_c, int* done_i) {
         const int jf = j + A - NS;
         if (jf >= 0) spin_ge(done_i, NW * (jf / NS + 1));
-        ld.issue(kb, vb, kst2, iss.j0, len, iss.ok, is);
+        ld.issue(kb, vb, kst2, vst2, iss.j0, len, iss.ok, is);
         own_landed();
         signal(land_n, lane);
         spin_ge(land_c, NW * (j / NS + 1));
@@ -368,9 +377,9 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
     };
     Job jc = first_job<BS>(ulist, nU);
     Job ji = jc;
-    ld.issue(kb, vb, kst2, ji.j0, len, ji.ok, s0);
+    ld.issue(kb, vb, kst2, vst2, ji.j0, len, ji.ok, s0);
     ji = next_job_q<BS>(ji, ulist, nU, t_last);
-    ld.issue(kb, vb, kst2, ji.j0, len, ji.ok, s1);
+    ld.issue(kb, vb, kst2, vst2, ji.j0, len, ji.ok, s1);
     ji = next_job_q<BS>(ji, ulist, nU, t_last);
     own_landed();
     signal(&landed[0], lane);
@@ -395,15 +404,16 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
     wait_vm<0>();
 }
 
-// The same walk with a workgroup barrier after every job, for selections
-// that cover whole causal prefixes (every tile busy on every job, so the
-// counters above only add waiting): job j is computed from stage j % 4 while
+// The same walk with a workgroup barrier after every job, for the cases
+// where most tiles work on most jobs, so the counters above only add
+// waiting: selections that can cover whole causal prefixes (forward and
+// dQ), and forward tiles of 4 or more tokens (G <= 4): job j is computed from stage j % 4 while
 // the loads of job j + 3 go to stage (j + 3) % 4, last read by job j - 1
 // (freed by the barrier that ended it); the end-of-job wait leaves the
 // loads of jobs j + 2 and j + 3 in flight.
 template <int D, int BS, int NW, class Compute>
 __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const uint16_t* kb,
-                                            const uint16_t* vb, int kst2, int len,
+                                            const uint16_t* vb, int kst2, int vst2, int len,
                                             const uint16_t* ulist, int nU, int t_last,
                                             Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK;
@@ -422,16 +432,16 @@ __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>
     Job j1 = next_job_q<BS>(jc, ulist, nU, t_last);
     Job j2 = next_job_q<BS>(j1, ulist, nU, t_last);
     Job j3 = next_job_q<BS>(j2, ulist, nU, t_last);
-    ld.issue(kb, vb, kst2, jc.j0, len, jc.ok, s0);
-    ld.issue(kb, vb, kst2, j1.j0, len, j1.ok, s1);
-    ld.issue(kb, vb, kst2, j2.j0, len, j2.ok, s2);
+    ld.issue(kb, vb, kst2, vst2, jc.j0, len, jc.ok, s0);
+    ld.issue(kb, vb, kst2, vst2, j1.j0, len, j1.ok, s1);
+    ld.issue(kb, vb, kst2, vst2, j2.j0, len, j2.ok, s2);
     if constexpr (LD::kEven) {
         wait_vm_barrier<2 * LD::kPerWave>();
     } else {
         if (full) wait_vm_barrier<2 * LD::kPerWave>(); else wait_vm_barrier<0>();
     }
     auto step = [&](const KVStage<D, JK>& cs, KVStage<D, JK>& is) {
-        ld.issue(kb, vb, kst2, j3.j0, len, j3.ok, is);
+        ld.issue(kb, vb, kst2, vst2, j3.j0, len, j3.ok, is);
         compute(jc, cs);
         ring_wait();
         jc = j1;
@@ -479,12 +489,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const int n_tok = min(qg.TW, s.len - wc.T0);
     const int t_last = wc.T0 + n_tok - 1;
     const int NBz = (s.len + BS - 1) / BS;
-    const int kst2 = (int)s.k_st * 2;
-    const uint16_t* kb = k + s.k_base + wc.hkv * s.k_sh;
-    const uint16_t* vb = v + s.k_base + wc.hkv * s.k_sh;
+    const int kst2 = (int)p.lk.st * 2, vst2 = (int)p.lv.st * 2;
+    const uint16_t* kb = k + head_base(p.lk, s, wc.hkv);
+    const uint16_t* vb = v + head_base(p.lv, s, wc.hkv);
     using LD = KVLoad<D, NW, JK>;
     LD ld;
-    ld.init(w, lane, kst2);
+    ld.init(w, lane, kst2, vst2);
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
@@ -502,7 +512,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         const int tau = w * RT + i;
         tr[i] = tile_row(p, qg, wc.hkv, wc.T0, s.len, tau, r);
         tmask[i] = tile_tokens(p, qg, tau);
-        const uint16_t* qrow = q + s.q_base + (int)(tr[i].h * s.q_sh + tr[i].t * s.q_st) + 8 * g;
+        const uint16_t* qrow = q + row_off(p.lq, s, tr[i].h, tr[i].t) + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk)
             qf[i][kk] = tr[i].valid ? as_bf16x8(ldg16(qrow + 32 * kk)) : zero8();
@@ -646,6 +656,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
         const uint64_t bm = umask[cur.u];
+        // Neither tile's tokens list the block (or both tiles are idle: past
+        // the workgroup's tokens when G < 4): nothing to compute.  Loads and
+        // barriers happen outside, so leaving early is safe.
+        if (!__builtin_amdgcn_readfirstlane((int)((bm & (tmask[0] | tmask[1])) != 0ull))) return;
         f32x4 sc0[NKT], sc1[NKT];
         {
             KOps ka;
@@ -685,9 +699,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     };
 
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, compute_pair);
+        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, compute_pair);
     } else {
-        q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
+        q_ring<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, lane, compute);
     }
 
 #pragma unroll
@@ -697,7 +711,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         float lse_r = l_tot > 0.f ? (m_run[i] * c2 + fast_log2(l_tot)) * kLn2 : kNegInfQ;
         if (p.sink) finish_row_sink(p.sink[tr[i].h], m_run[i] * c2, l_tot, inv, lse_r);
         if (tr[i].valid) {
-            uint16_t* orow = o + s.q_base + (int)(tr[i].h * s.q_sh + tr[i].t * s.q_st) + 4 * g;
+            uint16_t* orow = o + row_off(p.lo, s, tr[i].h, tr[i].t) + 4 * g;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) {
                 const uint2 pk = make_uint2(pack_bf16x2(acc[i][dt][0] * inv, acc[i][dt][1] * inv),
@@ -731,12 +745,12 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const int n_tok = min(qg.TW, s.len - wc.T0);
     const int t_last = wc.T0 + n_tok - 1;
     const int NBz = (s.len + BS - 1) / BS;
-    const int kst2 = (int)s.k_st * 2;
-    const uint16_t* kb = k + s.k_base + wc.hkv * s.k_sh;
-    const uint16_t* vb = v + s.k_base + wc.hkv * s.k_sh;
+    const int kst2 = (int)p.lk.st * 2, vst2 = (int)p.lv.st * 2;
+    const uint16_t* kb = k + head_base(p.lk, s, wc.hkv);
+    const uint16_t* vb = v + head_base(p.lv, s, wc.hkv);
     using LD = KVLoad<D, NW, JK>;
     LD ld;
-    ld.init(w, lane, kst2);
+    ld.init(w, lane, kst2, vst2);
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
@@ -753,11 +767,12 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
         const int tau = w * RT + i;
         tr[i] = tile_row(p, qg, wc.hkv, wc.T0, s.len, tau, r);
         tmask[i] = tile_tokens(p, qg, tau);
-        const int ro = (int)(tr[i].h * s.q_sh + tr[i].t * s.q_st) + 8 * g;
+        const uint16_t* qrow = q + row_off(p.lq, s, tr[i].h, tr[i].t) + 8 * g;
+        const uint16_t* drow = dO + row_off(p.ldo, s, tr[i].h, tr[i].t) + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) {
-            qf[i][kk] = tr[i].valid ? as_bf16x8(ldg16(q + s.q_base + ro + 32 * kk)) : zero8();
-            df[i][kk] = tr[i].valid ? as_bf16x8(ldg16(dO + s.q_base + ro + 32 * kk)) : zero8();
+            qf[i][kk] = tr[i].valid ? as_bf16x8(ldg16(qrow + 32 * kk)) : zero8();
+            df[i][kk] = tr[i].valid ? as_bf16x8(ldg16(drow + 32 * kk)) : zero8();
         }
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -855,15 +870,15 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     };
 
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, compute);
+        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, compute);
     } else {
-        q_ring<D, BS, NW>(ld, kb, vb, kst2, s.len, ulist, nU, t_last, lane, compute);
+        q_ring<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, lane, compute);
     }
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         if (!tr[i].valid) continue;
-        uint16_t* drow = dq + s.q_base + (int)(tr[i].h * s.q_sh + tr[i].t * s.q_st) + 4 * g;
+        uint16_t* drow = dq + row_off(p.ldq, s, tr[i].h, tr[i].t) + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
             const uint2 pk = make_uint2(pack_bf16x2(acc[i][dt][0] * p.scale, acc[i][dt][1] * p.scale),
@@ -945,7 +960,7 @@ static bool q_sync(const HostProblem& hp) {
 // The forward also takes the barrier walk when a tile holds 4 or more tokens
 // (G <= 4): a tile then needs most of its workgroup's jobs even on sparse
 // lists, and a barrier per job costs less than the counters (8 packed
-// sequences, 32 / 8 heads, 16 blocks per row: forward 0.364 -> 0.340 ms; with
+// sequences, 32 / 8 heads, 16 blocks per row: forward 0.364 -> 0.345 ms; with
 // 16 heads per tile, one token, the barrier walk took 0.346 -> 0.641 ms).
 // dQ measured the same either way and keeps the counters.
 static bool fwd_sync(const HostProblem& hp) {
@@ -997,6 +1012,12 @@ hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, c
                        else go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, false, false>);
                    });
     return hipGetLastError();
+}
+
+// Bounded waits of this file's kernels that gave up (see spin_ge).
+hipError_t read_wait_timeouts_query(unsigned* out) {
+    return hipMemcpyFromSymbol(out, HIP_SYMBOL(g_wait_timeouts), sizeof(unsigned), 0,
+                               hipMemcpyDeviceToHost);
 }
 
 }  // namespace nsa

@@ -22,7 +22,7 @@
  * lse = -inf, dq = 0.  Negative or >= NB entries are padding.  Repeated
  * entries count once.  Keys listed by no row get dk = dv = 0.
  *
- * Layouts (all contiguous, row-major, last dimension D):
+ * Layouts (row-major, last dimension D contiguous):
  *   dense  (layout NSA_DENSE, cu_seqlens == NULL): q, o, dO, dq [B][Hq][T][D];
  *          k, v, dk, dv [B][Hkv][T][D]; block_idx [B][Hkv][T][S] int32;
  *          lse, delta [B][Hq][T] float.
@@ -32,6 +32,12 @@
  *          lse, delta [Hq][T]; cu_seqlens [n_seqs + 1] int32 on the device,
  *          cu_seqlens[0] = 0, non-decreasing, cu_seqlens[n_seqs] = T, and
  *          max_seqlen >= every sequence length (host value).
+ *   q, k, v, o, dO, dq, dk and dv are contiguous in these layouts when the
+ *   problem's `strided` is 0; with strided = 1 each of them has its own
+ *   element strides for its (batch entry, head, token) dimensions (page 3's
+ *   backward honours the output strides its caller declares), so e.g. a
+ *   [B][T][H][D] buffer is passed as the dense layout with strides
+ *   (T*H*D, D, H*D).  block_idx, lse, delta and cu_seqlens stay contiguous.
  * Element type: dtype NSA_F32 (float) or NSA_BF16 (bfloat16) for q, k, v, o,
  * dO, dq, dk, dv; lse/delta are float; block_idx/cu_seqlens are int32.
  *
@@ -47,12 +53,15 @@
  *
  * Supported (else NSA_ERR_UNSUPPORTED): dtype f32 with D in {16, 32, 64,
  * 128} and any block_size >= 1 (vector-ALU kernels); dtype bf16 with D in
- * {32, 64, 128} and block_size in {32, 64, 128} (matrix-core kernels), and
- * 12 * JK * D + 10 * NBmax + 32 <= 163840 bytes of forward/dQ LDS (JK = 64
- * for block_size >= 64, else 32; NBmax = ceil(max length / block_size); e.g.
- * NBmax <= 6550 at D = 128, block_size 64).  For both:
- * S <= 4096, NBmax <= 8192, (B or n_seqs) * Hkv <= 8192, max length * G
- * <= 2^30, Hq * T * D < 2^31 (per batch entry).
+ * {32, 64, 128} and block_size in {16, 32, 64, 128} (matrix-core kernels),
+ * and 12 * JK * D + 10 * NBmax + 32 <= 163840 bytes of forward/dQ LDS (JK =
+ * 64 for block_size >= 64, else 32; NBmax = ceil(max length / block_size);
+ * e.g. NBmax <= 6550 at D = 128, block_size 64).  For both: S <= 4096,
+ * NBmax <= 8192, (B or n_seqs) * Hkv <= 8192, max length * G <= 2^30,
+ * Hq * T * D < 2^31, max length * min(S, NBmax) < 2^31 (inverted-list
+ * entries of one (batch entry, KV head)); for each of the eight q-like and
+ * k-like tensors a token stride <= 2^24 elements and, per batch entry,
+ * (H - 1) * head stride + (T - 1) * token stride + D < 2^31 elements.
  */
 #ifndef NSA_SEL_H
 #define NSA_SEL_H
@@ -94,6 +103,18 @@ typedef struct nsa_sel_problem {
     int32_t dtype;       /* nsa_dtype */
     float scale;         /* softmax scale applied to <q, k> (e.g. 1/sqrt(D)) */
     int32_t window;      /* sliding window: keys t - window < j <= t only; 0 = none */
+    /* Memory layout of the eight q-like / k-like tensors.  strided = 0: the
+     * contiguous layouts above (the arrays below are not read).  strided = 1:
+     * stride_x = element strides of tensor x's batch-entry, head and token
+     * dimensions (packed problems do not read stride_x[0]); the D elements of
+     * a row are contiguous.  Only the strides of tensors a call takes are
+     * read.  Each stride must be >= 0 (0 repeats an input along that
+     * dimension), a multiple of 8 for bf16 (16-byte aligned rows), and the
+     * rows of an output must not overlap one another (checked:
+     * NSA_ERR_INVALID_ARG). */
+    int32_t strided;
+    int64_t stride_q[3], stride_k[3], stride_v[3], stride_o[3];
+    int64_t stride_do[3], stride_dq[3], stride_dk[3], stride_dv[3];
 } nsa_sel_problem;
 
 typedef struct hipStream_t_opaque* nsa_stream_t; /* a hipStream_t; NULL = null stream */
@@ -198,7 +219,7 @@ nsa_status nsa_sel_bwd_dsink(const nsa_sel_problem* p, const float* lse, const f
                              const int32_t* cu_seqlens, float* dsink, void* workspace,
                              size_t workspace_bytes, nsa_stream_t stream);
 
-/* Validation of a block_idx (optional; the other calls accept any entry)./* Validation of a block_idx (optional; the other calls accept any entry).
+/* Validation of a block_idx (optional; the other calls accept any entry).
  * Writes four counts over all rows of the problem into counts[4] (device
  * memory, uint64, overwritten): [0] padding entries (negative), [1] entries
  * out of range (>= NB of the row's sequence), [2] future entries (in range
@@ -215,6 +236,16 @@ nsa_status nsa_sel_check_block_idx(const nsa_sel_problem* p, const int32_t* bloc
 /* Entries the tokens array of nsa_sel_invert must hold: Smin * B * Hkv * T
  * (dense) or Smin * Hkv * T (packed). */
 size_t nsa_sel_invert_tokens_capacity(const nsa_sel_problem* p);
+
+/* Health check of the kernels' internal synchronisation.  The waves of a
+ * forward, dQ or dK/dV workgroup order their use of shared LDS stages with
+ * counters, and every wait on a counter is bounded (about 2^18 polls) so that
+ * a kernel always finishes.  *count receives the number of such waits that
+ * gave up on the current device since the library was loaded; each one means
+ * a launch may have computed from an incomplete stage (a library defect,
+ * never expected: 0 is the only healthy value).  Synchronises the current
+ * device (a blocking device-to-host copy of the counters). */
+nsa_status nsa_sel_wait_timeouts(uint64_t* count);
 
 /* Text of a status code, and the detail of the calling thread's last
  * error (empty string if none). */

@@ -52,6 +52,39 @@ def oracle_full(w: workloads.Workload):
     return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
 
 
+def dsink_bound(w, got, ref, sink, lse_ref, delta_ref):
+    """Per-head bound on |dsink_gpu - dsink_oracle| derived from the arithmetic
+    the GPU performs on the o and lse it produced itself (the pages fix no
+    dsink tolerance).  Per row r of head h the GPU adds P_g * Delta_g with
+    Delta_g = fp32 sum of dO * o_gpu and P_g = exp(sink[h] - lse_gpu) in fp32;
+    the oracle adds P_r * Delta_r in float64.  With u = 2^-24:
+      |Delta_g - Delta_r| <= |<dO, o_gpu - o_ref>| + D u sum|dO o_gpu|
+      |P_g - P_r|         <= P_r (exp(|lse_gpu - lse_ref| + 8u) - 1)
+    and the fixed-order fp32 sum over the head's rows adds at most
+    rows * u * sum|P_r Delta_g|.  Returns [Hq] bounds.
+    got/ref: GPU / oracle o (and dO from w) in the workload layout;
+    lse_ref / delta_ref: the oracle backward's row arrays."""
+    u = 2.0 ** -24
+    f = lambda x: np.asarray(x, np.float64)
+    if w.packed:   # [T, Hq, D] -> [Hq, T, D]; lse [Hq, T]
+        o_g, o_r, dO = (f(x).transpose(1, 0, 2) for x in (got["o"], ref["o"], w.dO))
+        lse_g, lse_r, dl_r = f(got["lse"]), f(lse_ref), f(delta_ref)
+    else:          # [B, Hq, T, D] -> [Hq, B*T, D]; lse [B, Hq, T] -> [Hq, B*T]
+        hm = lambda x: f(x).transpose(1, 0, 2, 3).reshape(w.Hq, -1, w.D)
+        o_g, o_r, dO = hm(got["o"]), hm(ref["o"]), hm(w.dO)
+        hl = lambda x: f(x).transpose(1, 0, 2).reshape(w.Hq, -1)
+        lse_g, lse_r, dl_r = hl(got["lse"]), hl(lse_ref), hl(delta_ref)
+    sk = f(sink)[:, None]
+    P_r = np.exp(sk - lse_r)
+    dl_g = np.sum(dO * o_g, axis=-1)
+    e_dl = np.abs(np.sum(dO * (o_g - o_r), axis=-1)) + w.D * u * np.sum(np.abs(dO * o_g), axis=-1)
+    e_dl = np.maximum(e_dl, np.abs(dl_g - dl_r))
+    e_p = P_r * np.expm1(np.abs(lse_g - lse_r) + 8 * u)
+    rows = lse_r.shape[1]
+    term = P_r * e_dl + np.abs(dl_g) * e_p
+    return term.sum(axis=1) + rows * u * np.sum(np.abs(P_r * dl_g), axis=1)
+
+
 def max_err(a, b):
     a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))

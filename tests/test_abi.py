@@ -38,9 +38,21 @@ def test_problem_struct_matches_header():
     text = open(HEADER).read()
     body = text[text.index("typedef struct nsa_sel_problem"):]
     body = body[:body.index("} nsa_sel_problem;")]
-    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
-    assert [f for _, f in fields] == [f for f, _ in _lib.Problem._fields_]
-    assert ctypes.sizeof(_lib.Problem) == 4 * len(fields)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for ty, names in re.findall(r"(int32_t|int64_t|float)\s+([^;]+);", body):
+        for n in names.split(","):
+            m = re.match(r"\s*(\w+)(?:\[(\d+)\])?", n)
+            fields.append((m.group(1), ty, int(m.group(2) or 1)))
+    assert [f for f, _, _ in fields] == [f for f, _ in _lib.Problem._fields_]
+    size = {"int32_t": 4, "float": 4, "int64_t": 8}
+    off = 0
+    for (name, ty, n), (_, ct) in zip(fields, _lib.Problem._fields_):
+        off = -(-off // size[ty]) * size[ty]
+        assert getattr(_lib.Problem, name).offset == off, name
+        assert ctypes.sizeof(ct) == size[ty] * n, name
+        off += size[ty] * n
+    assert ctypes.sizeof(_lib.Problem) == -(-off // 8) * 8
 
 
 def _prob(**kw):
@@ -143,3 +155,85 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def _strided(p, **strides):
+    """Mark p strided with contiguous dense strides, then override some."""
+    H = {"q": p.Hq, "o": p.Hq, "do": p.Hq, "dq": p.Hq, "k": p.Hkv, "v": p.Hkv, "dk": p.Hkv,
+         "dv": p.Hkv}
+    p.strided = 1
+    for name, h in H.items():
+        arr = getattr(p, "stride_" + name)
+        arr[0], arr[1], arr[2] = h * p.T * p.D, p.T * p.D, p.D
+    for name, st in strides.items():
+        arr = getattr(p, "stride_" + name)
+        arr[0], arr[1], arr[2] = st
+    return p
+
+
+def _bwd_small_ws(p):
+    """nsa_sel_bwd with every tensor given and a workspace one byte short:
+    NSA_ERR_WORKSPACE means every tensor check passed (no HIP call made)."""
+    lib = _lib.load()
+    need = lib.nsa_sel_bwd_workspace_bytes(p)
+    assert need > 0, _lib.last_error()
+    return lib.nsa_sel_bwd(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                           FAKE, need - 1, None)
+
+
+def test_declared_strides_accepted():
+    """BTHD buffers viewed as BHTD, a KV head repeated over the batch (batch
+    stride 0 on an input), and gradients written into a wider buffer."""
+    B, Hq, Hkv, T, D = 2, 4, 2, 96, 64
+    p = _prob(dtype=1, B=B, Hq=Hq, Hkv=Hkv, T=T, D=D, S=4, block_size=32)
+    _strided(p, q=(T * Hq * D, D, Hq * D), o=(T * Hq * D, D, Hq * D),
+             k=(0, T * D, D), v=(T * Hkv * D, D, Hkv * D),
+             dq=(T * Hq * 2 * D, 2 * D, Hq * 2 * D), dk=(Hkv * T * D, T * D, D))
+    assert _bwd_small_ws(p) == _lib.NSA_ERR_WORKSPACE, _lib.last_error()
+    p2 = _prob(dtype=1, layout=1, B=1, Hq=Hq, Hkv=Hkv, T=T, D=D, S=4, block_size=32, n_seqs=2,
+               max_seqlen=64)
+    _strided(p2, q=(12345, D, Hq * D), dq=(0, 2 * D, Hq * 2 * D))   # packed: [0] unread
+    lib = _lib.load()
+    need = lib.nsa_sel_bwd_workspace_bytes(p2)
+    st = lib.nsa_sel_bwd(p2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, need - 1, None)
+    assert st == _lib.NSA_ERR_WORKSPACE, _lib.last_error()
+
+
+@pytest.mark.parametrize("which,st,status,word", [
+    ("q", (-8, 64, 64 * 4), _lib.NSA_ERR_INVALID_ARG, ">= 0"),
+    ("k", (96 * 64, 96 * 64 + 4, 64), _lib.NSA_ERR_INVALID_ARG, "multiples of 8"),
+    ("v", (0, 64, (1 << 24) + 8), _lib.NSA_ERR_UNSUPPORTED, "token stride"),
+    ("dO", (0, 1 << 30, 64), _lib.NSA_ERR_UNSUPPORTED, "2^31"),
+    ("o", (4 * 96 * 64, 0, 64), _lib.NSA_ERR_INVALID_ARG, "overlapping"),   # heads alias
+    ("dq", (4 * 96 * 64, 96 * 64, 32), _lib.NSA_ERR_INVALID_ARG, "overlapping"),  # rows overlap
+    ("dk", (0, 96 * 64, 64), _lib.NSA_ERR_INVALID_ARG, "overlapping"),      # batch entries alias
+    ("dv", (2 * 96 * 64, 2 * 96 * 64, 64), _lib.NSA_ERR_INVALID_ARG, "overlapping"),  # head 1 = entry 1
+])
+def test_bad_strides_rejected_before_any_hip_call(which, st, status, word):
+    p = _prob(dtype=1, B=2, Hq=4, Hkv=2, T=96, D=64, S=4, block_size=32)
+    _strided(p, **{which.lower() if which != "dO" else "do": st})
+    assert _bwd_small_ws(p) == status
+    assert word in _lib.last_error() and which in _lib.last_error()
+
+
+def test_inputs_may_overlap_outputs_may_not():
+    """A zero head stride is a valid input (one row shared by every head) but
+    an invalid output."""
+    p = _prob(dtype=1, B=1, Hq=4, Hkv=1, T=64, D=64, S=2, block_size=32)
+    _strided(p, q=(0, 0, 64))
+    assert _bwd_small_ws(p) == _lib.NSA_ERR_WORKSPACE, _lib.last_error()
+    _strided(p, dq=(0, 0, 64))
+    assert _bwd_small_ws(p) == _lib.NSA_ERR_INVALID_ARG and "overlapping" in _lib.last_error()
+
+
+def test_list_entry_bound():
+    """max length * min(S, NBmax) inverted-list entries per (batch, KV head)
+    must stay below 2^31 (32-bit list offsets): the last accepted length and
+    the first refused one."""
+    lib = _lib.load()
+    ok = _prob(dtype=0, D=16, T=(1 << 19) - 1, block_size=64, S=4096, Hq=1, Hkv=1)
+    assert lib.nsa_sel_bwd_workspace_bytes(ok) > 0, _lib.last_error()
+    bad = _prob(dtype=0, D=16, T=1 << 19, block_size=64, S=4096, Hq=1, Hkv=1)
+    assert lib.nsa_sel_bwd_workspace_bytes(bad) == 0
+    assert "list entries" in _lib.last_error()

@@ -3,12 +3,10 @@ nsa_sel_bwd with the sink-inclusive lse, nsa_sel_bwd_dsink) against the
 float64 oracle on the same seeded inputs.
 
 o, lse, dq, dk, dv use page 1's max-abs gates (2e-3 fp32, 6e-2 bf16).
-dsink[h] sums one term per row of head h; each term is P_sink * Delta, with
-P_sink <= 1 and Delta from the outputs checked above, so its gate is the
-element gate times sqrt(rows per head): independent per-row rounding adds in
-quadrature."""
-import math
-
+The pages fix no gate for dsink[h], a sum of one term P_sink * Delta per row
+of head h: each head is gated by the bound the GPU's own arithmetic implies
+(_harness.dsink_bound: Delta from the o the GPU produced, P_sink from its lse,
+fp32 rounding of both and of the sum), with 25 % slack."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +14,7 @@ import torch
 import block_sparse_attention_nsa_amd as nsa
 import oracle
 import workloads
-from _harness import TOL, assert_close, say, to_dev
+from _harness import TOL, assert_close, dsink_bound, say, to_dev
 from test_gpu_parity import _weird_block_idx
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +50,7 @@ def _oracle(w, sink_np):
                                             w.scale, sink=sk)
         o, lse_f = oracle.fwd(w.q, w.k, w.v, w.block_idx, w.block_size, w.scale, sink=sk)
         ds = oracle.dsink(sk, lse, delta, head_axis=1)
-    return dict(o=o, lse=lse_f, dq=dq, dk=dk, dv=dv, dsink=ds)
+    return dict(o=o, lse=lse_f, dq=dq, dk=dk, dv=dv, dsink=ds, lse_b=lse, delta=delta)
 
 
 def _check(w, sink_np):
@@ -63,8 +61,11 @@ def _check(w, sink_np):
     ref = _oracle(w, sink_np)
     for name in ("o", "lse", "dq", "dk", "dv"):
         assert_close(name, got[name], ref[name], tol)
-    rows = w.T * (1 if w.packed else w.B)
-    assert_close("dsink", got["dsink"], ref["dsink"], tol * math.sqrt(rows))
+    bound = dsink_bound(w, got, ref, sink_np, ref["lse_b"], ref["delta"])
+    err = np.abs(got["dsink"] - ref["dsink"])
+    say(f"  dsink: max|err| = {err.max():.3e}, per-head bound {bound.min():.3e}..{bound.max():.3e}, "
+        f"max|dsink| = {np.abs(ref['dsink']).max():.3g}")
+    assert np.all(err <= 1.25 * bound + 1e-6), (err, bound)
     return got, ref
 
 
