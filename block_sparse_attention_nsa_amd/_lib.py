@@ -15,6 +15,7 @@ NSA_DENSE, NSA_PACKED = 0, 1
 EXPORTS = (
     "nsa_sel_fwd",
     "nsa_sel_bwd",
+    "nsa_sel_bwd_noalloc",
     "nsa_sel_bwd_workspace_bytes",
     "nsa_sel_bwd_prepare",
     "nsa_sel_bwd_dq",
@@ -86,6 +87,8 @@ def load():
     lib.nsa_sel_fwd.restype = st
     lib.nsa_sel_bwd.argtypes = [P, vp, vp, vp, vp, fp, vp, ip, ip, vp, vp, vp, vp, sz, vp]
     lib.nsa_sel_bwd.restype = st
+    lib.nsa_sel_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, fp, vp, ip, ip, vp, vp, vp, vp]
+    lib.nsa_sel_bwd_noalloc.restype = st
     lib.nsa_sel_bwd_workspace_bytes.argtypes = [P]
     lib.nsa_sel_bwd_workspace_bytes.restype = sz
     lib.nsa_sel_bwd_prepare.argtypes = [P, vp, vp, ip, ip, vp, sz, vp]

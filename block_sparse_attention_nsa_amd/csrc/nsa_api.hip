@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "nsa_internal.h"
@@ -299,7 +300,10 @@ struct BwdArgs {
     size_t ws_bytes;
 };
 
-nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProblem& hp) {
+// check_ws = false: the workspace is the built-in scratch (its size is
+// checked by the caller), so only the problem and tensors are checked.
+nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProblem& hp,
+                     bool check_ws = true) {
     NSA_TRY(make_problem(p, hp));
     NSA_TRY(check_cu(hp, a.cu));
     const Sizes sz = sizes_of(hp);
@@ -312,10 +316,12 @@ nsa_status check_bwd(const nsa_sel_problem* p, const BwdArgs& a, nsa::HostProble
         if (t.ptr != kAbsent) NSA_TRY(check_qk(hp, t.w, t.ptr));
     if (a.lse != kAbsent) NSA_TRY(check_tensor(a.lse, sz.lse, 4, "lse"));
     if (a.idx != kAbsent) NSA_TRY(check_tensor(a.idx, sz.idx, 4, "block_idx"));
-    const nsa::BwdWorkspace need = carve(hp, nullptr);
-    if (need.bytes && (!a.ws || a.ws_bytes < need.bytes))
-        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a.ws_bytes, need.bytes);
-    if (a.ws && misaligned(a.ws, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (check_ws) {
+        const nsa::BwdWorkspace need = carve(hp, nullptr);
+        if (need.bytes && (!a.ws || a.ws_bytes < need.bytes))
+            return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", a.ws_bytes, need.bytes);
+        if (a.ws && misaligned(a.ws, 256)) return fail(NSA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    }
     hp.dev.cu = a.cu;
     return NSA_OK;
 }
@@ -361,6 +367,39 @@ nsa_status run_dkdv(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st
 namespace nsa {
 BwdWorkspace carve_bwd_workspace(const HostProblem& hp, void* base) { return carve(hp, base); }
 }  // namespace nsa
+
+// ---- backward without allocation -----------------------------------------
+// A fixed device array stands in for the backward's workspace in
+// nsa_sel_bwd_noalloc.  Each device the library runs on holds its own copy
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, looked up once per device.
+nsa_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(NSA_ERR_UNSUPPORTED, "device %d is beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(NSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NSA_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -537,6 +576,27 @@ nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, c
     const BwdArgs a{q, k, v, o, dO, dq, dk, dv, lse, block_idx, cu_seqlens, workspace, workspace_bytes};
     NSA_TRY(check_bwd(p, a, hp));
     if (sizes_of(hp).q == 0) return NSA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    NSA_TRY(run_prepare(hp, a, st));
+    NSA_TRY(run_dq(hp, a, st));
+    return run_dkdv(hp, a, st);
+}
+
+nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* dO,
+                               const int32_t* block_idx, const int32_t* cu_seqlens, void* dq,
+                               void* dk, void* dv, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    BwdArgs a{q, k, v, o, dO, dq, dk, dv, lse, block_idx, cu_seqlens, nullptr, kScratchBytes};
+    NSA_TRY(check_bwd(p, a, hp, false));
+    const size_t need = carve(hp, nullptr).bytes;
+    if (need > kScratchBytes)
+        return fail(NSA_ERR_WORKSPACE, "this backward needs %zu bytes of workspace; the built-in scratch of "
+                    "nsa_sel_bwd_noalloc holds %zu (use nsa_sel_bwd with a caller workspace)",
+                    need, kScratchBytes);
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    NSA_TRY(scratch_address(&a.ws));
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     NSA_TRY(run_prepare(hp, a, st));
     NSA_TRY(run_dq(hp, a, st));

@@ -142,6 +142,24 @@ nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, c
                        void* dv, void* workspace, size_t workspace_bytes,
                        nsa_stream_t stream);
 
+/* nsa_sel_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from a 64 MiB
+ * device array built into the library instead of a caller buffer.  Nothing
+ * is allocated (no hipMalloc, hipFree or allocating library call); each GPU
+ * the library runs on holds its own copy of the array until the process
+ * ends, its address looked up once per device.  A problem whose backward
+ * needs more workspace (nsa_sel_bwd_workspace_bytes() > 64 MiB) is refused
+ * with NSA_ERR_WORKSPACE before any HIP call.  The array keeps the last
+ * call's contents; nothing in it needs to start at zero.  All calls on one
+ * GPU share that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and corrupt each other's results -- order
+ * them on one stream or serialise them. */
+nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* dO,
+                               const int32_t* block_idx, const int32_t* cu_seqlens, void* dq,
+                               void* dk, void* dv, nsa_stream_t stream);
+
 /* The backward in three stages on one workspace; nsa_sel_bwd is exactly
  * prepare, dq, dkdv in this order.  prepare computes Delta and the block ->
  * query inversion (and the dK/dV work plan) into the workspace; dq and dkdv

@@ -237,3 +237,18 @@ def test_list_entry_bound():
     bad = _prob(dtype=0, D=16, T=1 << 19, block_size=64, S=4096, Hq=1, Hkv=1)
     assert lib.nsa_sel_bwd_workspace_bytes(bad) == 0
     assert "list entries" in _lib.last_error()
+
+
+def test_noalloc_backward_checks_before_any_hip_call():
+    """nsa_sel_bwd_noalloc refuses bad tensors and problems whose workspace
+    exceeds its built-in 64 MiB scratch on the host, before any HIP call."""
+    lib = _lib.load()
+    ok = _prob(dtype=1, D=64, block_size=32, Hq=6, Hkv=2, T=1024, B=2, S=8)
+    st = lib.nsa_sel_bwd_noalloc(ok, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                                 FAKE, None)
+    assert st == _lib.NSA_ERR_INVALID_ARG and "dq is NULL" in _lib.last_error()
+    big = _prob(dtype=1, D=128, block_size=64, Hq=32, Hkv=2, T=8192, B=1, S=16)
+    assert lib.nsa_sel_bwd_workspace_bytes(big) > 64 << 20
+    st = lib.nsa_sel_bwd_noalloc(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                 FAKE, None)
+    assert st == _lib.NSA_ERR_WORKSPACE and str(64 << 20) in _lib.last_error()

@@ -1,0 +1,61 @@
+"""nsa_sel_bwd_noalloc (the backward for callers that cannot allocate: its
+workspace is a fixed device array inside the library) against nsa_sel_bwd on
+the same inputs, through the C ABI: two calls in a row, the second with a
+smaller problem (the array keeps the first call's contents), each bitwise
+equal to nsa_sel_bwd and within the bf16 gate of the float64 oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_nsa_amd as nsa
+import workloads
+from block_sparse_attention_nsa_amd import _lib
+from _harness import TOL, assert_close, oracle_full, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _noalloc(w, d, o, lse):
+    """dq, dk, dv from nsa_sel_bwd_noalloc, called through ctypes."""
+    cu = d["cu"]
+    ms = w.max_seqlen if w.packed else None
+    p = nsa.make_problem(d["q"], d["k"], d["idx"], w.block_size, w.scale, cu, ms)
+    dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+    nsa.set_strides(p, q=d["q"], k=d["k"], v=d["v"], o=o, dO=d["dO"], dq=dq, dk=dk, dv=dv)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = _lib.load().nsa_sel_bwd_noalloc(
+        ctypes.byref(p), ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(o), ptr(lse), ptr(d["dO"]),
+        ptr(d["idx"]), ptr(cu), ptr(dq), ptr(dk), ptr(dv),
+        torch.cuda.current_stream().cuda_stream)
+    _lib.check("nsa_sel_bwd_noalloc", st)
+    return dq, dk, dv
+
+
+def test_noalloc_backward_equals_workspace_backward_twice():
+    cases = [
+        # lists long enough to be split into fp32 partials (the largest part
+        # of the workspace), then a smaller packed problem
+        workloads.make_dense(2, 8, 2, 2048, 128, 8, 64, "bf16", "own_first_random", seed=61,
+                             name="noalloc-dense"),
+        workloads.make_thd([300, 0, 77, 160], 6, 2, 64, 5, 32, "bf16", "own_first_random",
+                           seed=62, name="noalloc-packed"),
+    ]
+    for w in cases:
+        say(f"[{w.name}] B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} S={w.S} "
+            f"bs={w.block_size} packed={w.packed}")
+        d = to_dev(w)
+        ms = w.max_seqlen if w.packed else None
+        o, lse = nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, d["cu"], ms)
+        dq0, dk0, dv0 = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"],
+                                        w.block_size, w.scale, d["cu"], ms)
+        dq1, dk1, dv1 = _noalloc(w, d, o, lse)
+        torch.cuda.synchronize()
+        for name, a, b in (("dq", dq0, dq1), ("dk", dk0, dk1), ("dv", dv0, dv1)):
+            assert torch.equal(a, b), f"{name}: nsa_sel_bwd_noalloc differs from nsa_sel_bwd"
+        ref = oracle_full(w)
+        f = lambda x: x.float().cpu().numpy().astype(np.float64)
+        for name, a in (("dq", dq1), ("dk", dk1), ("dv", dv1)):
+            assert_close(name, f(a), ref[name], TOL[w.dtype])
+    assert nsa.wait_timeouts() == 0
