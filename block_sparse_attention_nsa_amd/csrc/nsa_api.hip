@@ -65,8 +65,8 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     if (p->dtype == NSA_BF16) {
         if (p->D != 32 && p->D != 64 && p->D != 128)
             return fail(NSA_ERR_UNSUPPORTED, "bf16 needs D in {32, 64, 128} (got %d)", p->D);
-        if (p->block_size != 32 && p->block_size != 64 && p->block_size != 128)
-            return fail(NSA_ERR_UNSUPPORTED, "bf16 needs block_size in {32, 64, 128} (got %d)", p->block_size);
+        if (p->block_size != 16 && p->block_size != 32 && p->block_size != 64 && p->block_size != 128)
+            return fail(NSA_ERR_UNSUPPORTED, "bf16 needs block_size in {16, 32, 64, 128} (got %d)", p->block_size);
     } else {
         if (p->D != 16 && p->D != 32 && p->D != 64 && p->D != 128)
             return fail(NSA_ERR_UNSUPPORTED, "f32 needs D in {16, 32, 64, 128} (got %d)", p->D);
@@ -176,7 +176,8 @@ nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
     w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 3 * ZH + 1));
     w.ticket = (int*)take(sizeof(int));
     w.iota = (int*)take(hp.pair_possible ? sizeof(int) * hp.dev.Tmax : 0);
-    w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * hp.dev.bs * hp.dev.D);
+    // (16-key blocks use the 32-key tile's slot layout)
+    w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * std::max(32, hp.dev.bs) * hp.dev.D);
     w.bytes = off;
     return w;
 }
@@ -215,9 +216,10 @@ const nsa::TLayout& layout_of(const nsa::Problem& d, Which w) {
 
 // Pointer, alignment and strides of one of the eight tensors.  Strides are
 // >= 0, multiples of 8 elements for bf16 (every row 16-byte aligned), the
-// token stride at most 2^24 (the kernels form 32-bit byte offsets of up to
-// 64 consecutive tokens), and one batch entry spans less than 2^31 elements
-// (offsets inside an entry are 32-bit).  Outputs
+// token stride below 2^23 elements (the kernels form byte offsets of tokens
+// with 24-bit multiplies), and one batch entry spans less than 2^31 - 128
+// elements (offsets inside an entry are 32-bit, and one past every such
+// offset marks a load out of range).  Outputs
 // must map distinct (entry, head, token, d) to distinct elements: with the
 // dimensions sorted by stride, each stride reaches past everything the
 // smaller ones span.
@@ -243,11 +245,11 @@ nsa_status check_qk(const nsa::HostProblem& hp, Which w, const void* ptr) {
                     (long long)st0);
     // (The 32-bit device strides were clamped; read the caller's values.)
     const int64_t sh = d.strided ? hp.given[w][1] : L.sh, stt = d.strided ? hp.given[w][2] : L.st;
-    if (stt > (1ll << 24))
-        return fail(NSA_ERR_UNSUPPORTED, "%s token stride %lld exceeds 2^24 elements", name, (long long)stt);
+    if (stt >= (1ll << 23))
+        return fail(NSA_ERR_UNSUPPORTED, "%s token stride %lld is not below 2^23 elements", name, (long long)stt);
     const int64_t entry = (nh - 1) * sh + (nt - 1) * stt + D;
-    if (entry >= (1ll << 31))
-        return fail(NSA_ERR_UNSUPPORTED, "%s spans %lld elements per batch entry (limit 2^31 - 1)",
+    if (entry > (1ll << 31) - 128)
+        return fail(NSA_ERR_UNSUPPORTED, "%s spans %lld elements per batch entry (limit 2^31 - 128)",
                     name, (long long)entry);
     if (w == kO || w == kDQ || w == kDK || w == kDV) {
         struct Dim { int64_t n, s; } dims[4] = {{D, 1}, {nb, sb}, {nh, sh}, {nt, stt}};

@@ -17,12 +17,22 @@ namespace nsa {
 // ---- Delta ----------------------------------------------------------------
 
 // Row r of lse / delta ([B][Hq][T] dense, [Hq][T] packed) -> element
-// offsets of its rows in o and dO.
-__device__ __forceinline__ void delta_row_offsets(const Problem& p, int64_t r, int64_t& oo,
-                                                  int64_t& od) {
-    const int64_t t = r % p.T, bh = r / p.T, h = bh % p.Hq, b = bh / p.Hq;
-    oo = b * p.lo.sb + h * p.lo.sh + t * p.lo.st;
-    od = b * p.ldo.sb + h * p.ldo.sh + t * p.ldo.st;
+// offsets of its rows in o and dO.  r0 is a row of the same workgroup at or
+// before r (wave-uniform), so the one 64-bit division per workgroup is
+// scalar; a batch entry holds Hq * T < 2^31 rows (checked on the host), so
+// the rest is 32-bit.
+__device__ __forceinline__ void delta_row_offsets(const Problem& p, int64_t r0, int64_t r,
+                                                  int64_t& oo, int64_t& od) {
+    const uint32_t per = (uint32_t)p.Hq * (uint32_t)p.T;
+    uint32_t b = (uint32_t)(r0 / per);
+    uint32_t rr = (uint32_t)(r - (int64_t)b * per);
+    while (rr >= per) {  // a workgroup's rows span few entries
+        rr -= per;
+        ++b;
+    }
+    const uint32_t h = rr / (uint32_t)p.T, t = rr - h * (uint32_t)p.T;
+    oo = (int64_t)b * p.lo.sb + (int32_t)(h * p.lo.sh + t * p.lo.st);
+    od = (int64_t)b * p.ldo.sb + (int32_t)(h * p.ldo.sh + t * p.ldo.st);
 }
 
 // bf16 rows: D/8 lanes per row, 16-byte loads, fp32 products and sums; one
@@ -38,7 +48,7 @@ __device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t
     float acc = 0.f;
     if (r < nrows) {
         int64_t oo, od;
-        delta_row_offsets(p, r, oo, od);
+        delta_row_offsets(p, blk * RPB, r, oo, od);
         uint4 a = ldg16(o + oo + part * 8);
         uint4 b = ldg16(dO + od + part * 8);
         const uint32_t av[4] = {a.x, a.y, a.z, a.w};
@@ -70,7 +80,7 @@ __global__ __launch_bounds__(256) void delta_f32_kernel(Problem p, const float* 
     int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= nrows) return;
     int64_t oo, od;
-    delta_row_offsets(p, r, oo, od);
+    delta_row_offsets(p, (int64_t)blockIdx.x * blockDim.x, r, oo, od);
     float acc = 0.f;
     for (int d = 0; d < p.D; ++d) acc += o[oo + d] * dO[od + d];
     delta[r] = acc;

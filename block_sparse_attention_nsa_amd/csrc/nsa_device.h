@@ -248,19 +248,29 @@ static __device__ unsigned int g_wait_timeouts;
 
 // Waits until the LDS counter reaches target.  Callers make sure the waves
 // that add to it always get there, so the wait ends; the iteration cap only
-// bounds it should that ever fail, and then the give-up is counted in
-// g_wait_timeouts.  The counter is read with a plain ds_read_b32 in asm: to
-// the compiler it is unrelated to the stages that buffer-to-LDS loads are
-// filling, so it adds no vector-memory wait.
-__device__ __forceinline__ void spin_ge(const int* ctr, int target) {
+// bounds it should that ever fail, and then the wave sets the workgroup's
+// LDS flag *fail (a plain LDS store on that path only: nothing is carried
+// through the callers' loops).  After its loop each wave passes the flag to
+// report_wait_timeouts, which counts it in g_wait_timeouts.  The counter is
+// read with a plain ds_read_b32 in asm: to the compiler it is unrelated to
+// the stages that buffer-to-LDS loads are filling, so it adds no
+// vector-memory wait.
+__device__ __forceinline__ void spin_ge(const int* ctr, int target, int* fail) {
     const uint32_t a = lds_addr(ctr);
     for (int it = 0; it < (1 << 18); ++it) {
         int v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
         if (__builtin_amdgcn_readfirstlane(v) >= target) return;
     }
-    if (__lane_id() == 0) atomicAdd(&g_wait_timeouts, 1u);
+    asm volatile("ds_write_b32 %0, %1" : : "v"(lds_addr(fail)), "v"(1) : "memory");
 }
+// Counts a wave's view of its workgroup's give-up flag (after its loop).
+__device__ __forceinline__ void report_wait_timeouts(const int* fail) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(fail)) : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) != 0 && __lane_id() == 0) atomicAdd(&g_wait_timeouts, 1u);
+}
+
 // One count from this wave (LDS operations of a wave are processed in order,
 // so its earlier LDS reads and writes are done first).
 __device__ __forceinline__ void signal(int* ctr, int lane) {

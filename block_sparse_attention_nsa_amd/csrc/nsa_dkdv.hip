@@ -71,33 +71,39 @@ __device__ __forceinline__ void find_item(int b, int ZH, int NB, const int* __re
 }
 
 // Cursor over the flattened row list (row f = e * G + h), walked downwards 32
-// rows at a time without dividing.  hoff = h * (byte stride of a head).
+// rows at a time without dividing.  hoff / hoff2 = h * (byte stride of a head)
+// in two tensors.
 struct Cursor {
     int f, e, h;
-    uint32_t hoff;
+    uint32_t hoff, hoff2;
 };
 
-__device__ __forceinline__ Cursor cursor_at(int f, int G, uint32_t hstride) {
+__device__ __forceinline__ Cursor cursor_at(int f, int G, uint32_t hstride, uint32_t hstride2 = 0) {
     Cursor c;
     c.f = f;
     const int ff = max(f, 0);
     c.e = ff / G;
     c.h = ff - c.e * G;
     c.hoff = (uint32_t)c.h * hstride;
+    c.hoff2 = (uint32_t)c.h * hstride2;
     return c;
 }
 
-// Moves the cursor 32 rows down: q32 = 32 / G, r32 = 32 % G.
+// Moves the cursor 32 rows down: q32 = 32 / G, r32 = 32 % G; the strides
+// are r32 and G times the heads' byte strides.
 __device__ __forceinline__ void retreat32(Cursor& c, int G, int q32, int r32, uint32_t r32_stride,
-                                          uint32_t G_stride) {
+                                          uint32_t G_stride, uint32_t r32_stride2 = 0,
+                                          uint32_t G_stride2 = 0) {
     c.f -= 32;
     c.h -= r32;
     c.e -= q32;
     c.hoff -= r32_stride;
+    c.hoff2 -= r32_stride2;
     if (c.h < 0) {
         c.h += G;
         c.e -= 1;
         c.hoff += G_stride;
+        c.hoff2 += G_stride2;
     }
 }
 
@@ -130,8 +136,10 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // removes those).  pair_on: this is the per-block launch of a problem that
 // also has the paired one, so it runs only when the paired one does not.
 // WIN: the problem has a sliding window (keys t - window < j only); the
-// paired launch never has one.
-template <int D, int BS, bool PAIRED, bool WIN>
+// paired launch never has one.  BK: keys of one block (BS, except 16-key
+// blocks, which run on a 32-key tile whose upper 16 keys -- the next
+// block's -- are masked out and never written).
+template <int D, int BS, bool PAIRED, bool WIN, int BK = BS>
 __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
@@ -150,6 +158,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     __shared__ __attribute__((aligned(16))) int tkr[NP][4][64];
     __shared__ uint4 pbuf[NP][2][2][64];  // [pair][P, dS][key tile][lane]
     __shared__ int freed[NP];
+    __shared__ int wait_fail;  // an S wave's wait gave up (see spin_ge)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r = lane & 15;
     const bool s_wave = w < NP;
@@ -190,8 +199,10 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const int R = (off[lu + 1] - off[lu]) * G;
     const int f_begin = it.kitem * CR, f_end = min(R, f_begin + CR);
     const int nsteps = (f_end - f_begin + 31) / 32;
-    const int kbase = u * BS + 32 * a;
+    static_assert(BK == BS || (BK == 16 && BS == 32 && !PAIRED), "a 16-key block on a 32-key tile");
+    const int kbase = u * BK + 32 * a;
     if (tid < NP) freed[tid] = 0;
+    if (tid == 0) wait_fail = 0;
 
     f32x4 dkt[2][ND], dvt[2][ND];  // accumulators: dK^T / dV^T of keys kbase + 16 kt + r
 
@@ -202,7 +213,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
-            const bool in = key < s.len;
+            const bool in = 16 * kt < BK && key < s.len;
             const uint16_t* kr = k + row_off(p.lk, s, hkv, in ? key : 0) + 8 * g;
             const uint16_t* vr = v + row_off(p.lv, s, hkv, in ? key : 0) + 8 * g;
 #pragma unroll
@@ -280,8 +291,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
                             const float e = fast_exp2(fmaf(sc[rt][kt][i4], c2, nl[i4]));
-                            const bool vis = WIN ? key <= tv[i4] && key + p.window > tv[i4]
-                                                 : key <= tv[i4];
+                            const bool vis = 16 * kt < BK &&
+                                             (WIN ? key <= tv[i4] && key + p.window > tv[i4]
+                                                  : key <= tv[i4]);
                             const float P = vis ? e : 0.f;
                             pv[kt][rt][i4] = P;
                             dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
@@ -295,7 +307,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                     pk[1][kt] = __builtin_bit_cast(uint4, pack8(dsv[kt][0], dsv[kt][1]));
                 }
                 // The accumulator has read the previous step's P / dS.
-                if (i > 0) spin_ge(&freed[a], i);
+                if (i > 0) spin_ge(&freed[a], i, &wait_fail);
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -312,6 +324,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
             if (i + 2 <= nsteps) s_step(i + 2, st2);
             if (i + 3 <= nsteps) s_step(i + 3, st3);
         }
+        report_wait_timeouts(&wait_fail);
         return;
     }
 
@@ -335,6 +348,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const uint32_t dsh_b = (uint32_t)(2 * p.ldo.sh), dst_b = (uint32_t)(2 * p.ldo.st);
     const uint32_t lsh_b = (uint32_t)(4 * p.T);
     const int q32 = 32 / G, r32 = 32 % G;
+    const bool same_qd = qsh_b == dsh_b && qst_b == dst_b;
+    const uint32_t q_r32 = (uint32_t)r32 * qsh_b, q_G = (uint32_t)G * qsh_b;
+    const uint32_t d_r32 = (uint32_t)r32 * dsh_b, d_G = (uint32_t)G * dsh_b;
     const uint32_t l_r32 = (uint32_t)r32 * lsh_b, l_G = (uint32_t)G * lsh_b;
 
     // Rows this lane loads: 1 KB load jj = a + NP * j of a tile covers the
@@ -349,7 +365,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         const int pos = 64 * jj + lane;
         qrow[j] = pos / QCH;
         cofs[j] = 16u * (uint32_t)L::chunk(qrow[j], pos % QCH);
-        cq[j] = cursor_at(f_end - 32 + qrow[j], G, 0u);
+        cq[j] = cursor_at(f_end - 32 + qrow[j], G, qsh_b, dsh_b);
     }
     // Lanes < 32: row `lane` of each step, once for the token list (one step
     // ahead of the rows) and once for lse / Delta, into this accumulator's
@@ -379,14 +395,17 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
         for (int j = 0; j < NJ; ++j) {
             const int jj = a + NP * j;
             if (kEven || jj < NI) {
+                // Token ids are < 2^20 and byte token strides < 2^24 (both
+                // checked on the host): 24-bit multiplies, full rate.  When
+                // q and dO share a layout (uniform) one offset serves both.
                 const bool in = cq[j].f >= f_begin;
-                const uint32_t h = (uint32_t)cq[j].h, t = (uint32_t)tj[j];
-                const uint32_t vq = in ? h * qsh_b + t * qst_b + cofs[j] : kOob;
-                const uint32_t vd = in ? h * dsh_b + t * dst_b + cofs[j] : kOob;
+                const uint32_t vq = in ? cq[j].hoff + __umul24((uint32_t)tj[j], qst_b) + cofs[j] : kOob;
+                const uint32_t vd = same_qd ? vq
+                                  : in ? cq[j].hoff2 + __umul24((uint32_t)tj[j], dst_b) + cofs[j] : kOob;
                 dma16(rq, reinterpret_cast<uint8_t*>(sg.q) + 1024 * jj, vq);
                 dma16(rd, reinterpret_cast<uint8_t*>(sg.dO) + 1024 * jj, vd);
             }
-            retreat32(cq[j], G, q32, r32, 0u, 0u);
+            retreat32(cq[j], G, q32, r32, q_r32, q_G, d_r32, d_G);
         }
         {
             const uint32_t lo = meta && cm.f >= f_begin ? cm.hoff + 4u * (uint32_t)tm : kOob;
@@ -492,7 +511,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
-            if (key >= s.len) continue;
+            if (16 * kt >= BK || key >= s.len) continue;
             uint16_t* dkr = dk + row_off(p.ldk, s, hkv, key) + 4 * g;
             uint16_t* dvr = dv + row_off(p.ldv, s, hkv, key) + 4 * g;
 #pragma unroll
@@ -533,7 +552,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 // to 16 per block, so a block listed by many rows does not hold back the
 // others; with many, fewer, since most blocks need no reduction and their
 // workgroups only exit).
-template <int D, int BS>
+template <int D, int BS, int BK = BS>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     Problem p, const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
     const int* __restrict__ zh_base, const float* __restrict__ partials, int rs,
@@ -544,7 +563,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     const int zh = bu / NB, u = bu % NB;
     const int z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
-    if (u * BS >= s.len) return;
+    if (u * BK >= s.len) return;
     const int* ip = item_pre + (int64_t)zh * (NB + 1);
     const int n = ip[u + 1] - ip[u];
     if (n == 1) return;
@@ -563,8 +582,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
         pos[q] = e0 + (int)threadIdx.x + 256 * q;
         const int x = pos[q] % E4;
         const int ln = x % 64, tile = x / (64 * ND);
-        key[q] = u * BS + 16 * tile + (ln & 15);
-        on[q] = pos[q] < e_end && key[q] < s.len;
+        key[q] = u * BK + 16 * tile + (ln & 15);
+        on[q] = pos[q] < e_end && 16 * tile < BK && key[q] < s.len;
     }
     float4 acc[kP];
 #pragma unroll
@@ -623,7 +642,8 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
     if (hp.ZH == 0) return hipSuccess;
     const unsigned items = (parts & kDkdvBlocks) ? (unsigned)hp.items_ub : 0u;
     const int64_t n_blocks = (int64_t)hp.ZH * hp.dev.NBmax;
-    const int64_t rs_min = ((int64_t)hp.dev.bs * hp.dev.D / 2 + 1023) / 1024;  // 2 E4 / (256 * 4)
+    const int tile = std::max(32, hp.dev.bs);  // keys per partial slot
+    const int64_t rs_min = ((int64_t)tile * hp.dev.D / 2 + 1023) / 1024;  // 2 E4 / (256 * 4)
     const int rs = (int)std::max<int64_t>(rs_min, std::min<int64_t>(16, 4096 / std::max<int64_t>(1, n_blocks)));
     // Without partial slots every list (empty ones included) is written whole
     // by the block kernel: nothing to reduce.
@@ -643,12 +663,24 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
             NSA_DISPATCH_D_BS(hp.dev.D, 2 * hp.dev.bs,
                               go(dkdv_kernel<D, BS, true, false>, pairs, BS / 16 * 64));
         }
-        if (hp.dev.window > 0)
+        if (hp.dev.bs == 16) {
+            // 16-key blocks on the 32-key tile (two waves).
+            if (hp.dev.window > 0)
+                NSA_DISPATCH_D_BS(hp.dev.D, 32, go(dkdv_kernel<D, 32, false, true, 16>, items, 128));
+            else
+                NSA_DISPATCH_D_BS(hp.dev.D, 32, go(dkdv_kernel<D, 32, false, false, 16>, items, 128));
+        } else if (hp.dev.window > 0) {
             NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, true>, items, BS / 16 * 64));
-        else
+        } else {
             NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, false>, items, BS / 16 * 64));
+        }
     }
-    if (nred) {
+    if (nred && hp.dev.bs == 16) {
+        NSA_DISPATCH_D_BS(hp.dev.D, 32,
+                          hipLaunchKernelGGL((dkdv_reduce_kernel<D, 32, 16>), dim3(nred), dim3(256), 0,
+                                             st, hp.dev, ws.item_pre, ws.pslot_pre, ws.zh_base,
+                                             ws.partials, rs, (uint16_t*)dk, (uint16_t*)dv));
+    } else if (nred) {
         NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
                           hipLaunchKernelGGL((dkdv_reduce_kernel<D, BS>), dim3(nred), dim3(256), 0,
                                              st, hp.dev, ws.item_pre, ws.pslot_pre, ws.zh_base,

@@ -33,10 +33,14 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
                                 pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])));
 }
 
-// Keys per job: whole 64-key blocks (half blocks of 128), 32 for 32-key blocks.
+// Keys per job: whole 64-key blocks (half blocks of 128), 32 for 32-key
+// blocks.  A 16-key block is walked as a 32-key job (the matrix-core step
+// contracts 32 keys) whose second 16 keys -- the next block's -- are masked
+// out: KT keys of the job belong to its block.
 template <int BS>
 struct JobKeys {
     static constexpr int JK = BS >= 64 ? 64 : 32;
+    static constexpr int KT = BS < JK ? BS : JK;
 };
 
 // One stage of the K/V ring: JK-key slices of K and V, rows in the RowTile
@@ -263,19 +267,34 @@ __device__ __forceinline__ Job next_job_q(Job c, const uint16_t* ulist, int nU, 
 
 // Buffer-to-LDS loads of one job's K and V slices (JK keys from key j0):
 // 1 KB load jj (< 2 NI; K for jj < NI, V after) is issued by wave jj % NW,
-// lane l writing RowTile position 64 (jj % NI) + l.  Keys past the sequence
-// lie past the descriptors and load as zeros.
+// lane l writing RowTile position 64 (jj % NI) + l.  The K and V buffer
+// descriptors cover the (sequence, KV head) and are built once; a job adds
+// its first key's offset to each lane's 32-bit offset, and a lane whose key
+// lies past the sequence (or a job slot past the last job) gets an offset
+// past every descriptor, which loads zeros.
 template <int D, int NW, int JK>
 struct KVLoad {
     using L = RowTile<D>;
     static constexpr int NI = JK * 2 * D / 1024;
     static constexpr int NJ = (2 * NI + NW - 1) / NW;  // loads per wave (at most)
-    uint32_t voff[NJ];   // byte offset of this lane's 16 bytes inside the slice
+    static constexpr int RPL = 64 / L::QCH;            // key rows per 1 KB load
+    static constexpr uint32_t kOob = 0xFFFFFFF0u;      // past every descriptor's size
+    buf_rsrc rk, rv;     // K and V of the (sequence, KV head)
+    uint32_t voff[NJ];   // byte offset of this lane's 16 bytes in a slice from key 0
     int jj[NJ];          // load index (>= 2 NI: none)
+    int lrow;            // this lane's key row inside its load
+    int kst2, vst2, len;
     // w must be wave-uniform (it selects the descriptor of each load).
-    // kst2 / vst2: byte strides between the keys of K / V.
-    __device__ void init(int w, int lane, int kst2, int vst2) {
+    // kst2 / vst2: byte strides between the keys of K / V; len >= 1 keys.
+    __device__ void init(int w, int lane, const uint16_t* kb, const uint16_t* vb, int kst2_,
+                         int vst2_, int len_) {
         w = __builtin_amdgcn_readfirstlane(w);
+        kst2 = kst2_;
+        vst2 = vst2_;
+        len = len_;
+        rk = make_rsrc(kb, (uint32_t)((int64_t)(len - 1) * kst2 + 2 * D));
+        rv = make_rsrc(vb, (uint32_t)((int64_t)(len - 1) * vst2 + 2 * D));
+        lrow = lane / L::QCH;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             jj[j] = w + NW * j;
@@ -290,27 +309,26 @@ struct KVLoad {
     static constexpr bool kEven = (2 * NI) % NW == 0;
     __device__ bool full_share() const { return jj[NJ - 1] < 2 * NI; }
     // Issued for every job slot, also past the last job (ok == false): those
-    // loads see an empty descriptor and write zeros into a free stage, so a
+    // loads all fall out of range and write zeros into a free stage, so a
     // wave always has the same number of loads in flight.
-    __device__ void issue(const uint16_t* kb, const uint16_t* vb, int kst2, int vst2, int j0,
-                          int len, bool ok, KVStage<D, JK>& st) const {
-        j0 = ok ? j0 : 0;
-        const uint32_t kbytes = ok ? (uint32_t)((int64_t)(len - 1 - j0) * kst2 + 2 * D) : 0u;
-        const uint32_t vbytes = ok ? (uint32_t)((int64_t)(len - 1 - j0) * vst2 + 2 * D) : 0u;
-        const buf_rsrc rk = make_rsrc(reinterpret_cast<const char*>(kb) + (int64_t)j0 * kst2, kbytes);
-        const buf_rsrc rv = make_rsrc(reinterpret_cast<const char*>(vb) + (int64_t)j0 * vst2, vbytes);
+    __device__ void issue(int j0, bool ok, KVStage<D, JK>& st) const {
+        const uint32_t ko = (uint32_t)j0 * (uint32_t)kst2, vo = (uint32_t)j0 * (uint32_t)vst2;
+        const int lim = ok ? len - j0 : 0;  // rows r < lim of the job exist
+        const bool whole = lim >= JK;       // wave-uniform: no row past the sequence
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
+            const bool isk = jj[j] < NI;
+            const uint32_t on = voff[j] + (isk ? ko : vo);
+            const uint32_t o = whole || lrow < lim - RPL * (jj[j] % NI) ? on : kOob;
             if constexpr (kEven) {
                 // Every wave has NJ loads: pick K or V without branching, so
                 // the count of loads in flight is the same on every path.
-                const bool isk = jj[j] < NI;
                 uint8_t* dst = isk ? reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j]
                                    : reinterpret_cast<uint8_t*>(st.v) + 1024 * (jj[j] - NI);
-                dma16(isk ? rk : rv, dst, voff[j]);
+                dma16(isk ? rk : rv, dst, o);
             } else {
-                if (jj[j] < NI) dma16(rk, reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j], voff[j]);
-                else if (jj[j] < 2 * NI) dma16(rv, reinterpret_cast<uint8_t*>(st.v) + 1024 * (jj[j] - NI), voff[j]);
+                if (jj[j] < NI) dma16(rk, reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j], o);
+                else if (jj[j] < 2 * NI) dma16(rv, reinterpret_cast<uint8_t*>(st.v) + 1024 * (jj[j] - NI), o);
             }
         }
     }
@@ -340,19 +358,19 @@ __device__ __forceinline__ void wait_vm() {
 // by waves at or ahead of it), so the walk ends.  Counts are cumulative: the
 // u-th use of a stage is complete at NW * (u + 1).
 template <int D, int BS, int NW, class Compute>
-__device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const uint16_t* kb,
-                                       const uint16_t* vb, int kst2, int vst2, int len,
+__device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
                                        const uint16_t* ulist, int nU, int t_last, int lane,
                                        Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK, NS = kQStages, A = kQAhead;
     using LD = KVLoad<D, NW, JK>;
     static_assert(NS == 4 && A == 2, "the unrolled walk below is written for 4 stages, 2 ahead");
     __shared__ KVStage<D, JK> s0, s1, s2, s3;
-    __shared__ int landed[NS], done[NS];
+    __shared__ int landed[NS], done[NS], wait_fail;
     if (threadIdx.x < NS) {
         landed[threadIdx.x] = 0;
         done[threadIdx.x] = 0;
     }
+    if (threadIdx.x == 0) wait_fail = 0;
     __syncthreads();
     const bool full = ld.full_share();
     auto own_landed = [&]() {
@@ -366,20 +384,20 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
     auto step = [&](const Job& cur, const Job& iss, const KVStage<D, JK>& cs, KVStage<D, JK>& is,
                     int* land_c, int* land_n, int* done_c, int* done_i) {
         const int jf = j + A - NS;
-        if (jf >= 0) spin_ge(done_i, NW * (jf / NS + 1));
-        ld.issue(kb, vb, kst2, vst2, iss.j0, len, iss.ok, is);
+        if (jf >= 0) spin_ge(done_i, NW * (jf / NS + 1), &wait_fail);
+        ld.issue(iss.j0, iss.ok, is);
         own_landed();
         signal(land_n, lane);
-        spin_ge(land_c, NW * (j / NS + 1));
+        spin_ge(land_c, NW * (j / NS + 1), &wait_fail);
         compute(cur, cs);
         signal(done_c, lane);
         ++j;
     };
     Job jc = first_job<BS>(ulist, nU);
     Job ji = jc;
-    ld.issue(kb, vb, kst2, vst2, ji.j0, len, ji.ok, s0);
+    ld.issue(ji.j0, ji.ok, s0);
     ji = next_job_q<BS>(ji, ulist, nU, t_last);
-    ld.issue(kb, vb, kst2, vst2, ji.j0, len, ji.ok, s1);
+    ld.issue(ji.j0, ji.ok, s1);
     ji = next_job_q<BS>(ji, ulist, nU, t_last);
     own_landed();
     signal(&landed[0], lane);
@@ -402,6 +420,7 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
     }
     // Loads of job slots past the end finish before the wave leaves.
     wait_vm<0>();
+    report_wait_timeouts(&wait_fail);
 }
 
 // The same walk with a workgroup barrier after every job, for the cases
@@ -412,8 +431,7 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
 // (freed by the barrier that ended it); the end-of-job wait leaves the
 // loads of jobs j + 2 and j + 3 in flight.
 template <int D, int BS, int NW, class Compute>
-__device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const uint16_t* kb,
-                                            const uint16_t* vb, int kst2, int vst2, int len,
+__device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
                                             const uint16_t* ulist, int nU, int t_last,
                                             Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK;
@@ -432,16 +450,16 @@ __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>
     Job j1 = next_job_q<BS>(jc, ulist, nU, t_last);
     Job j2 = next_job_q<BS>(j1, ulist, nU, t_last);
     Job j3 = next_job_q<BS>(j2, ulist, nU, t_last);
-    ld.issue(kb, vb, kst2, vst2, jc.j0, len, jc.ok, s0);
-    ld.issue(kb, vb, kst2, vst2, j1.j0, len, j1.ok, s1);
-    ld.issue(kb, vb, kst2, vst2, j2.j0, len, j2.ok, s2);
+    ld.issue(jc.j0, jc.ok, s0);
+    ld.issue(j1.j0, j1.ok, s1);
+    ld.issue(j2.j0, j2.ok, s2);
     if constexpr (LD::kEven) {
         wait_vm_barrier<2 * LD::kPerWave>();
     } else {
         if (full) wait_vm_barrier<2 * LD::kPerWave>(); else wait_vm_barrier<0>();
     }
     auto step = [&](const KVStage<D, JK>& cs, KVStage<D, JK>& is) {
-        ld.issue(kb, vb, kst2, vst2, j3.j0, len, j3.ok, is);
+        ld.issue(j3.j0, j3.ok, is);
         compute(jc, cs);
         ring_wait();
         jc = j1;
@@ -477,6 +495,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                                                         float* __restrict__ lse) {
     using L = RowTile<D>;
     constexpr int KD = D / 32, ND = D / 16, JK = JobKeys<BS>::JK, NKT = JK / 16, NKS = JK / 32;
+    constexpr int KT = JobKeys<BS>::KT;  // keys of the job inside its block
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
@@ -489,12 +508,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const int n_tok = min(qg.TW, s.len - wc.T0);
     const int t_last = wc.T0 + n_tok - 1;
     const int NBz = (s.len + BS - 1) / BS;
-    const int kst2 = (int)p.lk.st * 2, vst2 = (int)p.lv.st * 2;
-    const uint16_t* kb = k + head_base(p.lk, s, wc.hkv);
-    const uint16_t* vb = v + head_base(p.lv, s, wc.hkv);
     using LD = KVLoad<D, NW, JK>;
     LD ld;
-    ld.init(w, lane, kst2, vst2);
+    ld.init(w, lane, k + head_base(p.lk, s, wc.hkv), v + head_base(p.lv, s, wc.hkv),
+            2 * p.lk.st, 2 * p.lv.st, s.len);
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
                        bf16x8 (&pb)[NKS]) __attribute__((always_inline)) {
         // No mask when every token of the tile lists the block, the slice
         // ends before the tile's first token, and all rows exist.
-        const bool full = ((bm & tmask[i]) == tmask[i]) &&
+        const bool full = KT == JK && ((bm & tmask[i]) == tmask[i]) &&
                           (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
                           tr[i].valid && (!WIN || cur.j0 > tr[i].t - p.window);
         float mloc = kNegInfQ;
@@ -570,7 +587,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (16 * kt + e > lim || (WIN && 16 * kt + e < lo)) sc[kt][e] = kNegInfQ;
+                    if (16 * kt >= KT || 16 * kt + e > lim || (WIN && 16 * kt + e < lo))
+                        sc[kt][e] = kNegInfQ;
                     mloc = fmaxf(mloc, sc[kt][e]);
                 }
         }
@@ -699,9 +717,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     };
 
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, compute_pair);
+        q_ring_sync<D, BS, NW>(ld, ulist, nU, t_last, compute_pair);
     } else {
-        q_ring<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, lane, compute);
+        q_ring<D, BS, NW>(ld, ulist, nU, t_last, lane, compute);
     }
 
 #pragma unroll
@@ -733,6 +751,7 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const float* __restrict__ delta, const int* __restrict__ idx, uint16_t* __restrict__ dq) {
     using L = RowTile<D>;
     constexpr int KD = D / 32, ND = D / 16, JK = JobKeys<BS>::JK, NKT = JK / 16, NKS = JK / 32;
+    constexpr int KT = JobKeys<BS>::KT;  // keys of the job inside its block
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
@@ -745,12 +764,10 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const int n_tok = min(qg.TW, s.len - wc.T0);
     const int t_last = wc.T0 + n_tok - 1;
     const int NBz = (s.len + BS - 1) / BS;
-    const int kst2 = (int)p.lk.st * 2, vst2 = (int)p.lv.st * 2;
-    const uint16_t* kb = k + head_base(p.lk, s, wc.hkv);
-    const uint16_t* vb = v + head_base(p.lv, s, wc.hkv);
     using LD = KVLoad<D, NW, JK>;
     LD ld;
-    ld.init(w, lane, kst2, vst2);
+    ld.init(w, lane, k + head_base(p.lk, s, wc.hkv), v + head_base(p.lv, s, wc.hkv),
+            2 * p.lk.st, 2 * p.lv.st, s.len);
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
@@ -790,7 +807,7 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     // selection and causal range), then dS = P (dP - Delta) in bf16.
     auto dscore = [&](int i, f32x4 (&sc)[NKT], const f32x4 (&dp)[NKT], const Job& cur, uint64_t bm,
                       bf16x8 (&dsb)[NKS]) __attribute__((always_inline)) {
-        const bool full = ((bm & tmask[i]) == tmask[i]) &&
+        const bool full = KT == JK && ((bm & tmask[i]) == tmask[i]) &&
                           (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
                           tr[i].valid && (!WIN || cur.j0 > tr[i].t - p.window);
         if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
@@ -802,7 +819,8 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (16 * kt + e > lim || (WIN && 16 * kt + e < lo)) sc[kt][e] = kNegInfQ;
+                    if (16 * kt >= KT || 16 * kt + e > lim || (WIN && 16 * kt + e < lo))
+                        sc[kt][e] = kNegInfQ;
         }
 #pragma unroll
         for (int ks_ = 0; ks_ < NKS; ++ks_) {
@@ -870,9 +888,9 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     };
 
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, compute);
+        q_ring_sync<D, BS, NW>(ld, ulist, nU, t_last, compute);
     } else {
-        q_ring<D, BS, NW>(ld, kb, vb, kst2, vst2, s.len, ulist, nU, t_last, lane, compute);
+        q_ring<D, BS, NW>(ld, ulist, nU, t_last, lane, compute);
     }
 
 #pragma unroll
@@ -938,7 +956,10 @@ size_t query_dynamic_lds(const HostProblem& hp) {
 // still take part in staging).
 #define NSA_Q_DISPATCH(D_, BS_, CALL)                                                      \
     do {                                                                                   \
-        if ((D_) == 32 && (BS_) == 32) { constexpr int D = 32, BS = 32; CALL; }            \
+        if ((D_) == 32 && (BS_) == 16) { constexpr int D = 32, BS = 16; CALL; }            \
+        else if ((D_) == 64 && (BS_) == 16) { constexpr int D = 64, BS = 16; CALL; }       \
+        else if ((D_) == 128 && (BS_) == 16) { constexpr int D = 128, BS = 16; CALL; }     \
+        else if ((D_) == 32 && (BS_) == 32) { constexpr int D = 32, BS = 32; CALL; }       \
         else if ((D_) == 32 && (BS_) == 64) { constexpr int D = 32, BS = 64; CALL; }       \
         else if ((D_) == 32 && (BS_) == 128) { constexpr int D = 32, BS = 128; CALL; }     \
         else if ((D_) == 64 && (BS_) == 32) { constexpr int D = 64, BS = 32; CALL; }       \

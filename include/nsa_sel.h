@@ -60,8 +60,8 @@
  * NBmax <= 8192, (B or n_seqs) * Hkv <= 8192, max length * G <= 2^30,
  * Hq * T * D < 2^31, max length * min(S, NBmax) < 2^31 (inverted-list
  * entries of one (batch entry, KV head)); for each of the eight q-like and
- * k-like tensors a token stride <= 2^24 elements and, per batch entry,
- * (H - 1) * head stride + (T - 1) * token stride + D < 2^31 elements.
+ * k-like tensors a token stride < 2^23 elements and, per batch entry,
+ * (H - 1) * head stride + (T - 1) * token stride + D <= 2^31 - 128 elements.
  */
 #ifndef NSA_SEL_H
 #define NSA_SEL_H

@@ -78,7 +78,7 @@ def _fwd(p, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cu=None, o=FAKE, lse=FAKE):
     (dict(T=-1), _lib.NSA_ERR_INVALID_ARG, "T="),
     (dict(scale=float("nan")), _lib.NSA_ERR_INVALID_ARG, "scale"),
     (dict(dtype=1, D=48), _lib.NSA_ERR_UNSUPPORTED, "D in"),
-    (dict(dtype=1, D=64, block_size=16), _lib.NSA_ERR_UNSUPPORTED, "block_size in"),
+    (dict(dtype=1, D=64, block_size=8), _lib.NSA_ERR_UNSUPPORTED, "block_size in"),
     (dict(D=24), _lib.NSA_ERR_UNSUPPORTED, "D in"),
     (dict(T=1 << 20, block_size=16), _lib.NSA_ERR_UNSUPPORTED, "8192"),
     (dict(S=5000), _lib.NSA_ERR_UNSUPPORTED, "slots"),
@@ -203,7 +203,7 @@ def test_declared_strides_accepted():
 @pytest.mark.parametrize("which,st,status,word", [
     ("q", (-8, 64, 64 * 4), _lib.NSA_ERR_INVALID_ARG, ">= 0"),
     ("k", (96 * 64, 96 * 64 + 4, 64), _lib.NSA_ERR_INVALID_ARG, "multiples of 8"),
-    ("v", (0, 64, (1 << 24) + 8), _lib.NSA_ERR_UNSUPPORTED, "token stride"),
+    ("v", (0, 64, 1 << 23), _lib.NSA_ERR_UNSUPPORTED, "token stride"),
     ("dO", (0, 1 << 30, 64), _lib.NSA_ERR_UNSUPPORTED, "2^31"),
     ("o", (4 * 96 * 64, 0, 64), _lib.NSA_ERR_INVALID_ARG, "overlapping"),   # heads alias
     ("dq", (4 * 96 * 64, 96 * 64, 32), _lib.NSA_ERR_INVALID_ARG, "overlapping"),  # rows overlap
