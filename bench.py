@@ -5,7 +5,7 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 nsa_sel_fwd, then the backward's stages (Delta + block->query inversion +
-plan, dQ, the dK/dV block kernel, the dK/dV partial reduction).  Inputs are
+plan, the dK/dV block kernel, the dK/dV partial reduction, dQ).  Inputs are
 resident in HBM before timing.
 The metric is useful TFLOP/s: F_fwd = 4*D*N and F_bwd = 10*D*N with N the
 exact number of (query-head row, key) pairs the block lists select (counted
@@ -189,7 +189,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
     stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms, window=args.window)
-    names = ("fwd", "prepare", "dq", "dkdv", "dkdv_reduce") + (("dsink",) if args.sink else ())
+    names = ("fwd", "prepare", "dkdv", "dkdv_reduce", "dq") + (("dsink",) if args.sink else ())
     sink = None
     if args.sink:
         sink = torch.from_numpy(np.random.default_rng(args.seed + 1).normal(0.0, 1.0, w.Hq)
@@ -206,13 +206,13 @@ def main():
         stages.prepare(o, dO)
         if evs is not None:
             evs[2].record()
-        stages.dq_stage(dO, lse)
-        if evs is not None:
-            evs[3].record()
         stages.dkdv_blocks(dO, lse)
         if evs is not None:
-            evs[4].record()
+            evs[3].record()
         stages.dkdv_reduce()
+        if evs is not None:
+            evs[4].record()
+        stages.dq_stage(dO, lse)
         if evs is not None:
             evs[5].record()
         if sink is not None:

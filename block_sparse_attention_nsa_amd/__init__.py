@@ -206,8 +206,9 @@ def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqle
 
 class BwdStages:
     """The backward as its three C-ABI stages on one workspace
-    (nsa_sel_bwd_prepare, nsa_sel_bwd_dq, nsa_sel_bwd_dkdv); calling them in
-    that order equals nsa_sel_bwd.  Buffers are allocated once here."""
+    (nsa_sel_bwd_prepare, nsa_sel_bwd_dkdv, nsa_sel_bwd_dq); calling them in
+    that order equals nsa_sel_bwd (dq may read the dS the dK/dV stage hands
+    over, so it comes last).  Buffers are allocated once here."""
 
     def __init__(self, q, k, v, block_idx, block_size, scale=None, cu_seqlens=None,
                  max_seqlen=None, window=0):

@@ -148,6 +148,9 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
     hp.pair_possible = p->dtype == NSA_BF16 && hp.pslots == 0 && p->block_size <= 64 && p->window == 0 &&
                        (int64_t)p->S * p->block_size >= Tmax && ZH > 0 && NBmax > 0;
+    hp.ds_handoff = p->dtype == NSA_BF16 && G % 16 == 0 && p->window == 0 && p->block_size >= 32 &&
+                    p->S <= 64 && (int64_t)p->S * p->block_size < Tmax;
+    if (hp.ds_handoff && nsa::dq_ds_lds_bytes(hp) > 163840) hp.ds_handoff = false;
     if (nsa::invert_lds_bytes(hp) > 163840)
         return fail(NSA_ERR_UNSUPPORTED, "the block inversion needs %zu bytes of LDS for %lld blocks (max 163840)",
                     nsa::invert_lds_bytes(hp), (long long)NBmax);
@@ -178,6 +181,9 @@ nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
     w.iota = (int*)take(hp.pair_possible ? sizeof(int) * hp.dev.Tmax : 0);
     // (16-key blocks use the 32-key tile's slot layout)
     w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * std::max(32, hp.dev.bs) * hp.dev.D);
+    const bool ho = hp.ds_handoff;
+    w.posmap = (int*)take(ho ? sizeof(int) * (size_t)hp.dev.B * hp.dev.Hkv * hp.dev.T * hp.dev.S : 0);
+    w.ds = (uint16_t*)take(ho ? sizeof(uint16_t) * (size_t)hp.cap * hp.dev.bs * hp.dev.G : 0);
     w.bytes = off;
     return w;
 }
@@ -336,7 +342,9 @@ nsa_status run_prepare(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t
 
 nsa_status run_dq(const nsa::HostProblem& hp, const BwdArgs& a, hipStream_t st) {
     const nsa::BwdWorkspace ws = carve(hp, a.ws);
-    if (hp.dtype == NSA_BF16) {
+    if (hp.dtype == NSA_BF16 && hp.ds_handoff) {
+        NSA_HIP(nsa::launch_dq_handoff(hp, a.k, a.idx, ws, (void*)a.dq, st), "dQ (dS hand-off) launch");
+    } else if (hp.dtype == NSA_BF16) {
         NSA_HIP(nsa::launch_dq_bf16(hp, a.q, a.k, a.v, a.dO, a.lse, ws.delta, a.idx, (void*)a.dq, st), "dQ launch");
     } else {
         NSA_HIP(nsa::launch_dq_f32(hp, (const float*)a.q, (const float*)a.k, (const float*)a.v,
@@ -580,8 +588,8 @@ nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, c
     if (sizes_of(hp).q == 0) return NSA_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     NSA_TRY(run_prepare(hp, a, st));
-    NSA_TRY(run_dq(hp, a, st));
-    return run_dkdv(hp, a, st);
+    NSA_TRY(run_dkdv(hp, a, st));
+    return run_dq(hp, a, st);
 }
 
 nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const void* k,
@@ -592,7 +600,13 @@ nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const vo
     nsa::HostProblem hp;
     BwdArgs a{q, k, v, o, dO, dq, dk, dv, lse, block_idx, cu_seqlens, nullptr, kScratchBytes};
     NSA_TRY(check_bwd(p, a, hp, false));
-    const size_t need = carve(hp, nullptr).bytes;
+    size_t need = carve(hp, nullptr).bytes;
+    // Without room for the dS hand-off, dQ recomputes dS (the same results
+    // within the stated tolerance; the hand-off buffers dominate its need).
+    if (need > kScratchBytes && hp.ds_handoff) {
+        hp.ds_handoff = false;
+        need = carve(hp, nullptr).bytes;
+    }
     if (need > kScratchBytes)
         return fail(NSA_ERR_WORKSPACE, "this backward needs %zu bytes of workspace; the built-in scratch of "
                     "nsa_sel_bwd_noalloc holds %zu (use nsa_sel_bwd with a caller workspace)",
@@ -601,8 +615,8 @@ nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const vo
     NSA_TRY(scratch_address(&a.ws));
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     NSA_TRY(run_prepare(hp, a, st));
-    NSA_TRY(run_dq(hp, a, st));
-    return run_dkdv(hp, a, st);
+    NSA_TRY(run_dkdv(hp, a, st));
+    return run_dq(hp, a, st);
 }
 
 nsa_status nsa_sel_bwd_prepare(const nsa_sel_problem* p, const void* o, const void* dO,

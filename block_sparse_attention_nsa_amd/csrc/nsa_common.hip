@@ -144,9 +144,9 @@ __device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t, int W) {
     return u >= 0 && u < NBz && u * bs <= t && (W <= 0 || (u + 1) * bs > t - W + 1);
 }
 
-// Calls f(u) once per distinct valid entry u of row (S entries, token t),
-// from the lane holding the representative entry.  Rows of up to 65535
-// entries (positions fit 16 bits).
+// Calls f(u, si) once per distinct valid entry u of row (S entries, token
+// t), from the lane holding the representative entry si (lane si % 64).
+// Rows of up to 65535 entries (positions fit 16 bits).
 template <typename F>
 __device__ __forceinline__ void for_each_distinct(const int* row, int S, int NBz, int bs, int t,
                                                   int W, int lane, volatile uint16_t* last, F&& f) {
@@ -158,7 +158,7 @@ __device__ __forceinline__ void for_each_distinct(const int* row, int S, int NBz
     for (int s0 = 0; s0 < S; s0 += 64) {
         const int si = s0 + lane;
         const int u = si < S ? row[si] : -1;
-        if (entry_ok(u, NBz, bs, t, W) && last[u] == (uint16_t)si) f(u);
+        if (entry_ok(u, NBz, bs, t, W) && last[u] == (uint16_t)si) f(u, si);
     }
 }
 
@@ -203,7 +203,7 @@ __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, con
         __syncthreads();
         for (int t = tb + w; t < te; t += kInvWaves)
             for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
-                              [&](int u) { atomicAdd(&hist[u], 1); });
+                              [&](int u, int) { atomicAdd(&hist[u], 1); });
     }
     __syncthreads();
     int* out = chunk_pos + (int64_t)zh * p.NBmax * C;
@@ -412,12 +412,17 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
 // always wanted).  When it is set the backward needs no lists (every list of
 // block u is the tokens u bs .. len - 1, read from iota[u bs ..] instead):
 // the workgroups of (z, hkv) 0 write iota[t] = t for their chunk and return.
+// posmap (optional, laid out like block_idx): for every row and slot, the
+// position of the row's token in the list of the slot's block, -1 for slots
+// that are no entry (padding, out of range, future, outside the window, or
+// a repeat of a block the row lists in another slot).
 __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
                                                        const int* __restrict__ idx,
                                                        const int* __restrict__ chunk_pos,
                                                        int* __restrict__ tokens,
                                                        const int* __restrict__ whole,
-                                                       int* __restrict__ iota) {
+                                                       int* __restrict__ iota,
+                                                       int* __restrict__ posmap) {
     if (whole && *whole) {
         if (blockIdx.y == 0)
             for (int t = blockIdx.x * CT + (int)threadIdx.x; t < min(p.Tmax, (int)(blockIdx.x + 1) * CT);
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
         const int r0 = tb + w * q + min(w, rm), r1 = r0 + q + (w < rm ? 1 : 0);
         for (int t = r0; t < r1; ++t)
             for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
-                              [&](int u) { hw[u] += 1; });
+                              [&](int u, int) { hw[u] += 1; });
         __syncthreads();
         for (int u = threadIdx.x; u < NB; u += blockDim.x) {
             int run = cursor[u];
@@ -466,12 +471,21 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
             cursor[u] = run;
         }
         __syncthreads();
-        for (int t = r0; t < r1; ++t)
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last, [&](int u) {
-                const int pos = hw[u];
-                hw[u] = pos + 1;
-                out[pos] = t;
-            });
+        for (int t = r0; t < r1; ++t) {
+            // posmap: every slot of the row gets -1, then the slot standing
+            // for block u its position in u's list (the same lane writes
+            // both, in this order).
+            int* pm = posmap ? posmap + (s.i_base + (int64_t)hkv * p.T + t) * p.S : nullptr;
+            if (pm)
+                for (int si = lane; si < p.S; si += 64) pm[si] = -1;
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
+                              [&](int u, int si) {
+                                  const int pos = hw[u];
+                                  hw[u] = pos + 1;
+                                  out[pos] = t;
+                                  if (pm) pm[si] = pos;
+                              });
+        }
         __syncthreads();
     }
 }
@@ -518,7 +532,8 @@ hipError_t launch_scan_fill(const HostProblem& hp, const int* block_idx, const B
     const bool skip = lists_optional && hp.pair_possible;
     hipLaunchKernelGGL(inv_fill_kernel, dim3(hp.C, hp.ZH), dim3(64 * nw), fill_lds_bytes(hp, nw), st,
                        p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.tokens,
-                       skip ? ws.zh_base + 2 * (hp.ZH + 1) + 3 * hp.ZH : nullptr, ws.iota);
+                       skip ? ws.zh_base + 2 * (hp.ZH + 1) + 3 * hp.ZH : nullptr, ws.iota,
+                       lists_optional && hp.ds_handoff ? ws.posmap : nullptr);
     return hipGetLastError();
 }
 }  // namespace

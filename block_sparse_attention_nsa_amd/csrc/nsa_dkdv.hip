@@ -138,8 +138,11 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // WIN: the problem has a sliding window (keys t - window < j only); the
 // paired launch never has one.  BK: keys of one block (BS, except 16-key
 // blocks, which run on a 32-key tile whose upper 16 keys -- the next
-// block's -- are masked out and never written).
-template <int D, int BS, bool PAIRED, bool WIN, int BK = BS>
+// block's -- are masked out and never written).  DS: the S waves also store
+// dS (bf16) for the dQ kernel that takes it over (G a multiple of 16, so a
+// 16-row half of a step is 16 heads of one token): dsout[entry][key in the
+// block][head], entry = region_base + the row's position in the block's list.
+template <int D, int BS, bool PAIRED, bool WIN, int BK = BS, bool DS = false>
 __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
@@ -147,7 +150,8 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                  const int* __restrict__ offsets, const int* __restrict__ tokens,
                  const int* __restrict__ item_pre, const int* __restrict__ pslot_pre,
                  const int* __restrict__ zh_base, const int* __restrict__ iota, int CR, int pair_on,
-                 float* __restrict__ partials, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+                 float* __restrict__ partials, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                 uint16_t* __restrict__ dsout) {
     using L = RowTile<D>;
     constexpr int NP = BS / 32, KD = D / 32, ND = D / 16, QCH = L::QCH, NI = L::NI;
     constexpr int NJ = (NI + NP - 1) / NP;  // 1 KB row loads per tile for each accumulator (at most)
@@ -197,6 +201,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     // Paired (whole prefixes): block lu's list is the tokens lu bs .. len - 1.
     const int* list = PAIRED ? iota + lu * p.bs : tokens + region_base(p, s, hkv) + off[lu];
     const int R = (off[lu + 1] - off[lu]) * G;
+    const int64_t ds_entry0 = DS ? region_base(p, s, hkv) + off[lu] : 0;
     const int f_begin = it.kitem * CR, f_end = min(R, f_begin + CR);
     const int nsteps = (f_end - f_begin + 31) / 32;
     static_assert(BK == BS || (BK == 16 && BS == 32 && !PAIRED), "a 16-key block on a 32-key tile");
@@ -306,6 +311,25 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                     pk[0][kt] = __builtin_bit_cast(uint4, pack8(pv[kt][0], pv[kt][1]));
                     pk[1][kt] = __builtin_bit_cast(uint4, pack8(dsv[kt][0], dsv[kt][1]));
                 }
+                if constexpr (DS) {
+                    // dS of the step's two 16-row halves (16 heads of one
+                    // token each): lane (g, r) holds heads 4 g .. 4 g + 3 of
+                    // key 32 a + 16 kt + r, 8 contiguous bytes.
+                    const int fr0 = __builtin_amdgcn_readfirstlane(f_end - 32 * (i + 1));
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) {
+                        const int fr = fr0 + 16 * rt;
+                        if (fr < f_begin) continue;  // rows of another item
+                        const int e = fr / G, hh = fr - e * G;
+                        uint16_t* dst = dsout + ((ds_entry0 + e) * BS + 32 * a) * G + hh + 4 * g;
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt) {
+                            const uint4 x = pk[1][kt];
+                            *reinterpret_cast<uint2*>(dst + (int64_t)(16 * kt + r) * G) =
+                                rt == 0 ? make_uint2(x.x, x.y) : make_uint2(x.z, x.w);
+                        }
+                    }
+                }
                 // The accumulator has read the previous step's P / dS.
                 if (i > 0) spin_ge(&freed[a], i, &wait_fail);
 #pragma unroll
@@ -313,7 +337,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt) pbuf[a][x][kt][lane] = pk[x][kt];
             }
-            wait_vm_barrier<0>();
+            // (An S wave issues no loads; with DS its stores may stay in flight.)
+            if constexpr (DS) wait_vm_barrier<60>();
+            else wait_vm_barrier<0>();
         };
         // The accumulators' prologue has two barriers.
         wait_vm_barrier<0>();
@@ -654,7 +680,8 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
             hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, st, hp.dev, (const uint16_t*)q,
                                (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse,
                                delta, ws.offsets, ws.tokens, ws.item_pre, ws.pslot_pre, ws.zh_base,
-                               ws.iota, hp.CR, pair_on, ws.partials, (uint16_t*)dk, (uint16_t*)dv);
+                               ws.iota, hp.CR, pair_on, ws.partials, (uint16_t*)dk, (uint16_t*)dv,
+                               ws.ds);
         };
         if (pair_on) {
             // The paired launch first (it does the work for whole-prefix
@@ -671,6 +698,10 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
                 NSA_DISPATCH_D_BS(hp.dev.D, 32, go(dkdv_kernel<D, 32, false, false, 16>, items, 128));
         } else if (hp.dev.window > 0) {
             NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, true>, items, BS / 16 * 64));
+        } else if (hp.ds_handoff) {
+            // Also stores dS for the dQ kernel that takes it over.
+            NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
+                              go(dkdv_kernel<D, BS, false, false, BS, true>, items, BS / 16 * 64));
         } else {
             NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, false>, items, BS / 16 * 64));
         }

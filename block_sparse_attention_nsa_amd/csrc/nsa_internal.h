@@ -27,6 +27,11 @@ struct HostProblem {
     // the device, possible only without partial slots, for block_size <= 64,
     // bf16, and S * block_size >= the longest sequence.
     bool pair_possible;
+    // dS hand-off: the dK/dV kernel stores dS and the dQ kernel forms dq =
+    // scale dS K from it (bf16, G a multiple of 16, no window, selections
+    // that cannot cover whole causal prefixes: S * block_size < longest
+    // sequence).  The backward then runs dK/dV before dQ.
+    bool ds_handoff;
     // The caller's strides of q, k, v, o, dO, dq, dk, dv when the problem is
     // strided (the device copies hold 32-bit head / token strides).
     int64_t given[8][3];
@@ -47,6 +52,8 @@ struct BwdWorkspace {
     int* iota;           // [Tmax] (pair_possible): iota[t] = t, the lists of a
                          // whole-prefix selection
     float* partials;     // [pslots][bs][D][2]
+    int* posmap;         // (ds_handoff) [block_idx rows][S]: list position of each slot, or -1
+    uint16_t* ds;        // (ds_handoff) [cap][bs][G] bf16: dS of every listed (token, block)
     size_t bytes;
 };
 
@@ -84,6 +91,11 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
                             const void* dO, const float* lse, const float* delta,
                             const BwdWorkspace& ws, void* dk, void* dv, hipStream_t st,
                             int parts = kDkdvAll);
+
+// dQ from the handed-off dS (ds_handoff); runs after the dK/dV block kernel.
+size_t dq_ds_lds_bytes(const HostProblem& hp);
+hipError_t launch_dq_handoff(const HostProblem& hp, const void* k, const int* block_idx,
+                             const BwdWorkspace& ws, void* dq, hipStream_t st);
 
 hipError_t launch_fwd_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
                           const int* block_idx, float* o, float* lse, hipStream_t st);

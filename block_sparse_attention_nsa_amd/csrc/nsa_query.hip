@@ -50,6 +50,11 @@ struct alignas(16) KVStage {
     uint16_t k[JK * D];
     uint16_t v[JK * D];
 };
+// A stage holding K alone (dQ from a handed-off dS needs no V).
+template <int D, int JK>
+struct alignas(16) KStage {
+    uint16_t k[JK * D];
+};
 constexpr int kQStages = 4;  // ring depth
 constexpr int kQAhead = 2;   // jobs between issuing a stage's loads and computing it
 
@@ -272,11 +277,12 @@ __device__ __forceinline__ Job next_job_q(Job c, const uint16_t* ulist, int nU, 
 // its first key's offset to each lane's 32-bit offset, and a lane whose key
 // lies past the sequence (or a job slot past the last job) gets an offset
 // past every descriptor, which loads zeros.
-template <int D, int NW, int JK>
+template <int D, int NW, int JK, bool KONLY = false>
 struct KVLoad {
     using L = RowTile<D>;
-    static constexpr int NI = JK * 2 * D / 1024;
-    static constexpr int NJ = (2 * NI + NW - 1) / NW;  // loads per wave (at most)
+    static constexpr int NI = JK * 2 * D / 1024;      // 1 KB loads per tensor
+    static constexpr int NL = KONLY ? NI : 2 * NI;     // loads per job
+    static constexpr int NJ = (NL + NW - 1) / NW;      // loads per wave (at most)
     static constexpr int RPL = 64 / L::QCH;            // key rows per 1 KB load
     static constexpr uint32_t kOob = 0xFFFFFFF0u;      // past every descriptor's size
     buf_rsrc rk, rv;     // K and V of the (sequence, KV head)
@@ -306,12 +312,13 @@ struct KVLoad {
     // Loads this wave issues per job when it has its full share; kEven: all
     // waves have it.
     static constexpr int kPerWave = NJ;
-    static constexpr bool kEven = (2 * NI) % NW == 0;
-    __device__ bool full_share() const { return jj[NJ - 1] < 2 * NI; }
+    static constexpr bool kEven = NL % NW == 0;
+    __device__ bool full_share() const { return jj[NJ - 1] < NL; }
     // Issued for every job slot, also past the last job (ok == false): those
     // loads all fall out of range and write zeros into a free stage, so a
     // wave always has the same number of loads in flight.
-    __device__ void issue(int j0, bool ok, KVStage<D, JK>& st) const {
+    template <class Stage>
+    __device__ void issue(int j0, bool ok, Stage& st) const {
         const uint32_t ko = (uint32_t)j0 * (uint32_t)kst2, vo = (uint32_t)j0 * (uint32_t)vst2;
         const int lim = ok ? len - j0 : 0;  // rows r < lim of the job exist
         const bool whole = lim >= JK;       // wave-uniform: no row past the sequence
@@ -320,7 +327,9 @@ struct KVLoad {
             const bool isk = jj[j] < NI;
             const uint32_t on = voff[j] + (isk ? ko : vo);
             const uint32_t o = whole || lrow < lim - RPL * (jj[j] % NI) ? on : kOob;
-            if constexpr (kEven) {
+            if constexpr (KONLY) {
+                if (kEven || jj[j] < NI) dma16(rk, reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j], o);
+            } else if constexpr (kEven) {
                 // Every wave has NJ loads: pick K or V without branching, so
                 // the count of loads in flight is the same on every path.
                 uint8_t* dst = isk ? reinterpret_cast<uint8_t*>(st.k) + 1024 * jj[j]
@@ -478,6 +487,99 @@ __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>
     }
     // Loads of job slots past the end finish before the wave leaves.
     wait_vm_barrier<0>();
+}
+
+// Per-wave dS tiles of one job (JK keys x 16 heads, rows of 32 bytes), one
+// per tile of the wave; two of these alternate between consecutive jobs.
+template <int JK, int NW, int RT>
+struct alignas(16) DsBuf {
+    uint16_t v[NW][RT][JK * 16];
+};
+
+// The walk of q_ring for dQ from a handed-off dS: the ring holds K alone,
+// and each wave also stages the dS tiles its tiles need, one job ahead, in
+// two buffers of its own (job j in buffer j % 2).  In its step j a wave
+//   1. issues the dS tiles of job j + 1 (buffer (j + 1) % 2, last read by its
+//      own job j - 1);
+//   2. waits until every wave finished job j + A - NS, then issues its share
+//      of job j + A;
+//   3. waits for its share of job j + 1 and its dS tiles of job j (issued in
+//      step j - 1, before that share), counts landed;
+//   4. waits until all shares of job j landed, computes job j, counts done.
+// issue_ds returns the count of loads it issued (0, NDMA or 2 NDMA), which
+// the wait in 3 leaves in flight with the ring's job j + A.
+template <int D, int BS, int NW, int RT, class IssueDs, class Compute>
+__device__ __forceinline__ void q_ring_ds(const KVLoad<D, NW, JobKeys<BS>::JK, true>& ld,
+                                          const uint16_t* ulist, int nU, int t_last, int lane,
+                                          IssueDs&& issue_ds, Compute&& compute) {
+    constexpr int JK = JobKeys<BS>::JK, NS = kQStages, A = kQAhead, NDMA = JK / 32;
+    using LD = KVLoad<D, NW, JK, true>;
+    using DB = DsBuf<JK, NW, RT>;
+    static_assert(NS == 4 && A == 2 && RT == 2, "the walk below is written for 4 stages, 2 ahead, 2 tiles");
+    __shared__ KStage<D, JK> s0, s1, s2, s3;
+    __shared__ DB d0, d1;
+    __shared__ int landed[NS], done[NS], wait_fail;
+    if (threadIdx.x < NS) {
+        landed[threadIdx.x] = 0;
+        done[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0) wait_fail = 0;
+    __syncthreads();
+    const bool full = ld.full_share();
+    // Everything but the ring's newest job and the newest dS tiles landed.
+    auto own_landed = [&](int nds) {
+        if (LD::kEven && full) {
+            if (nds == 0) wait_vm<LD::kPerWave>();
+            else if (nds == NDMA) wait_vm<LD::kPerWave + NDMA>();
+            else wait_vm<LD::kPerWave + 2 * NDMA>();
+        } else {
+            wait_vm<0>();
+        }
+    };
+    int j = 0;
+    auto step = [&](const Job& cur, const Job& nxt, const Job& iss, const KStage<D, JK>& cs,
+                    KStage<D, JK>& is, const DB& dc, DB& dn, int* land_c, int* land_n,
+                    int* done_c, int* done_i) {
+        const int nds = issue_ds(nxt, dn);
+        const int jf = j + A - NS;
+        if (jf >= 0) spin_ge(done_i, NW * (jf / NS + 1), &wait_fail);
+        ld.issue(iss.j0, iss.ok, is);
+        own_landed(nds);
+        signal(land_n, lane);
+        spin_ge(land_c, NW * (j / NS + 1), &wait_fail);
+        compute(cur, cs, dc);
+        signal(done_c, lane);
+        ++j;
+    };
+    Job jc = first_job<BS>(ulist, nU);
+    Job jn = next_job_q<BS>(jc, ulist, nU, t_last);
+    Job ji = next_job_q<BS>(jn, ulist, nU, t_last);
+    issue_ds(jc, d0);
+    ld.issue(jc.j0, jc.ok, s0);
+    ld.issue(jn.j0, jn.ok, s1);
+    if (LD::kEven && full) wait_vm<LD::kPerWave>(); else wait_vm<0>();
+    signal(&landed[0], lane);
+    auto advance = [&]() {
+        jc = jn;
+        jn = ji;
+        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+    };
+    while (jc.ok) {
+        step(jc, jn, ji, s0, s2, d0, d1, &landed[0], &landed[1], &done[0], &done[2]);
+        advance();
+        if (!jc.ok) break;
+        step(jc, jn, ji, s1, s3, d1, d0, &landed[1], &landed[2], &done[1], &done[3]);
+        advance();
+        if (!jc.ok) break;
+        step(jc, jn, ji, s2, s0, d0, d1, &landed[2], &landed[3], &done[2], &done[0]);
+        advance();
+        if (!jc.ok) break;
+        step(jc, jn, ji, s3, s1, d1, d0, &landed[3], &landed[0], &done[3], &done[1]);
+        advance();
+    }
+    // Loads of job slots past the end finish before the wave leaves.
+    wait_vm<0>();
+    report_wait_timeouts(&wait_fail);
 }
 
 }  // namespace
@@ -907,6 +1009,153 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dQ from the dS that the dK/dV kernel hands off
+// ---------------------------------------------------------------------------
+// The dK/dV kernel forms dS = P (dP - Delta) for every listed (row, key) pair
+// and, for these problems, also stores it (bf16):
+//   ds [entry][key in block][head of the group], entry = region_base of the
+//       (z, hkv) + the (token, block) listing's position in the block's list;
+//   posmap [block_idx row][slot] = that entry for the slot standing for a
+//       listed block (its first occurrence in the row), else -1.
+// Then dQ needs no second pass over S and dP: dq = scale sum over the row's
+// listed blocks of dS K, one product (2 D flops per pair instead of 6 D) and
+// no q, dO, lse or Delta reads.  The walk is the dQ kernel's (16 tiles of 16
+// heads of one token, the union of the workgroup's listed blocks in
+// ascending order, K shared through an LDS ring); per job, each tile whose
+// token lists the block takes its dS tile (staged by buffer-to-LDS loads,
+// read transposed as the B operand) and adds K^T dS^T.  G is a multiple of
+// 16, block_size >= 32, S <= 64 and there is no sliding window.
+template <int D, int BS, int RT, int NW>
+__global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
+                                                        const uint16_t* __restrict__ k,
+                                                        const int* __restrict__ idx,
+                                                        const int* __restrict__ posmap,
+                                                        const uint16_t* __restrict__ ds,
+                                                        uint16_t* __restrict__ dq) {
+    using L = RowTile<D>;
+    constexpr int ND = D / 16, JK = JobKeys<BS>::JK, NKS = JK / 32, NDMA = JK / 32;
+    static_assert(BS >= 32 && JobKeys<BS>::KT == JK, "whole 32-key steps of one block");
+    using DB = DsBuf<JK, NW, RT>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
+    uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
+    int* n_u = reinterpret_cast<int*>(smem + QLds<D, JK>::dynamic_bytes(p.NBmax) - 16);
+
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6),
+              g = lane >> 4, r = lane & 15;
+    const WgCoord wc = wg_coord(p, qg);
+    const Seq s = seq_of(p, wc.z);
+    if (wc.T0 >= s.len) return;
+    const int n_tok = min(qg.TW, s.len - wc.T0);
+    const int t_last = wc.T0 + n_tok - 1;
+    const int NBz = (s.len + BS - 1) / BS;
+    using LD = KVLoad<D, NW, JK, true>;
+    LD ld;
+    const uint16_t* kb = k + head_base(p.lk, s, wc.hkv);
+    ld.init(w, lane, kb, kb, 2 * p.lk.st, 2 * p.lk.st, s.len);
+    uint32_t t_off[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
+
+    // Per tile: its token's block list and list positions (lane x holds slot
+    // x), its first head inside the group, its accumulators.
+    const int* rows = idx_row(p, s, idx, wc.hkv, wc.T0);
+    const int* prows = posmap + (rows - idx);
+    const int64_t ds_base = region_base(p, s, wc.hkv);
+    int u_l[RT], pos_l[RT], h0[RT], tok[RT];
+    bool tokv[RT];
+    f32x4 acc[RT][ND];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        const int tau = w * RT + i;
+        tok[i] = tau / qg.n_ht;
+        tokv[i] = tok[i] < qg.TW && wc.T0 + tok[i] < s.len;
+        h0[i] = 16 * (tau % qg.n_ht);
+        const bool have = tokv[i] && lane < p.S;
+        u_l[i] = have ? rows[tok[i] * p.S + lane] : -1;
+        pos_l[i] = have ? prows[tok[i] * p.S + lane] : -1;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
+
+    // This lane's 16 bytes of a dS tile: key 32 j + lane / 2 of load j,
+    // heads 8 (lane % 2) .. + 7 of the tile.
+    const uint32_t ds_lane = (uint32_t)((lane >> 1) * p.G * 2 + (lane & 1) * 16);
+    // Slot of tile i's token standing for block u, as a lane mask (0: the
+    // token does not list u).
+    auto listing = [&](int i, int u) __attribute__((always_inline)) -> uint64_t {
+        return __ballot(u_l[i] == u && pos_l[i] >= 0);
+    };
+    auto issue_ds = [&](const Job& jb, DB& buf) __attribute__((always_inline)) -> int {
+        if (!jb.ok) return 0;
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            const uint64_t m = listing(i, jb.u);
+            if (!m) continue;
+            const int pos = __builtin_amdgcn_readlane(pos_l[i], (int)__builtin_ctzll(m));
+            const uint16_t* src = ds + ((ds_base + pos) * BS + (jb.j0 - jb.u * BS)) * p.G + h0[i];
+            const buf_rsrc rs = make_rsrc(src, (uint32_t)((JK - 1) * p.G * 2 + 32));
+#pragma unroll
+            for (int jd = 0; jd < NDMA; ++jd)
+                dma16(rs, reinterpret_cast<uint8_t*>(buf.v[w][i]) + 1024 * jd,
+                      ds_lane + (uint32_t)(32 * jd * p.G * 2));
+            n += NDMA;
+        }
+        return n;
+    };
+    // dQ^T += K^T dS^T for the tiles whose token lists the job's block: the
+    // transposed K operand of each 32-key step is read once for both tiles.
+    auto compute = [&](const Job& cur, const KStage<D, JK>& sg, const DB& buf) {
+        bool act[RT];
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            act[i] = listing(i, cur.u) != 0ull;
+            any = any || act[i];
+        }
+        if (!any) return;
+        const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
+#pragma unroll
+        for (int ks_ = 0; ks_ < NKS; ++ks_) {
+            bf16x8 kop[ND];
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt) {
+                const uint8_t* kb0 = ks + t_off[dt] + 32 * ks_ * L::RB;
+                const uint2 k0 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0));
+                const uint2 k1 = lds_read_tr(reinterpret_cast<const uint16_t*>(kb0 + 16 * L::RB));
+                kop[dt] = __builtin_bit_cast(bf16x8, make_uint4(k0.x, k0.y, k1.x, k1.y));
+            }
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                if (!act[i]) continue;
+                // B operand dS^T[keys 32 ks_ + 4 g + e, 32 ks_ + 16 + 4 g + e][head r]:
+                // the key order of the transposed K reads above.
+                const bf16x8 bop = lds_col_operand(buf.v[w][i], 16, 32 * ks_, 32 * ks_ + 16, 0, lane);
+#pragma unroll
+                for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(kop[dt], bop, acc[i][dt]);
+            }
+        }
+    };
+
+    q_ring_ds<D, BS, NW, RT>(ld, ulist, nU, t_last, lane, issue_ds, compute);
+
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+        if (!tokv[i]) continue;
+        const int h = wc.hkv * p.G + h0[i] + r;
+        uint16_t* drow = dq + row_off(p.ldq, s, h, wc.T0 + tok[i]) + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const uint2 pk = make_uint2(pack_bf16x2(acc[i][dt][0] * p.scale, acc[i][dt][1] * p.scale),
+                                        pack_bf16x2(acc[i][dt][2] * p.scale, acc[i][dt][3] * p.scale));
+            *reinterpret_cast<uint2*>(drow + 16 * dt) = pk;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 namespace {
@@ -1032,6 +1281,36 @@ hipError_t launch_dq_bf16(const HostProblem& hp, const void* q, const void* k, c
                        if (win) go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, false, true>);
                        else go(dq_q_kernel<D, BS, kRT_Q, kNW_Q, false, false>);
                    });
+    return hipGetLastError();
+}
+
+// LDS of the hand-off dQ kernel: the K ring, the dS buffers, the counters
+// and the union.
+size_t dq_ds_lds_bytes(const HostProblem& hp) {
+    const size_t JK = hp.dev.bs >= 64 ? 64 : 32;
+    return 4 * JK * hp.dev.D * 2 + 2 * (size_t)kNW_Q * kRT_Q * JK * 32 + 64 + query_dynamic_lds(hp);
+}
+
+hipError_t launch_dq_handoff(const HostProblem& hp, const void* k, const int* block_idx,
+                             const BwdWorkspace& ws, void* dq, hipStream_t st) {
+    const QGeo qg = q_geo(hp, kRT_Q, kNW_Q);
+    const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
+    if (grid == 0) return hipSuccess;
+    const size_t lds = query_dynamic_lds(hp);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kNW_Q * 64), lds, st, hp.dev, qg,
+                           (const uint16_t*)k, block_idx, (const int*)ws.posmap,
+                           (const uint16_t*)ws.ds, (uint16_t*)dq);
+    };
+    const int D = hp.dev.D, BS = hp.dev.bs;
+#define NSA_DQ_DS(D_, BS_) \
+    else if (D == D_ && BS == BS_) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q>);
+    if (false) {}
+    NSA_DQ_DS(32, 32) NSA_DQ_DS(32, 64) NSA_DQ_DS(32, 128)
+    NSA_DQ_DS(64, 32) NSA_DQ_DS(64, 64) NSA_DQ_DS(64, 128)
+    NSA_DQ_DS(128, 32) NSA_DQ_DS(128, 64) NSA_DQ_DS(128, 128)
+    else return hipErrorInvalidValue;
+#undef NSA_DQ_DS
     return hipGetLastError();
 }
 

@@ -133,9 +133,15 @@ size_t nsa_sel_bwd_workspace_bytes(const nsa_sel_problem* p);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, dO and
  * block_idx.  Runs, in order on `stream`: Delta = rowsum(dO * o); the
- * block -> query inversion; the dQ kernel (per query tile, no atomics); the
- * dK/dV kernel (per key block and row chunk, no atomics) and its
- * fixed-order reduction.  Results are deterministic (bitwise repeatable). */
+ * block -> query inversion; the dK/dV kernel (per key block and row chunk,
+ * no atomics) and its fixed-order reduction; the dQ kernel (no atomics).
+ * When the dK/dV kernel hands its dS over to dQ -- bf16, G a multiple of
+ * 16, block_size >= 32, S <= 64, no window and S * block_size < the longest
+ * sequence, so selections that cannot cover whole causal prefixes -- dQ is
+ * dq = scale dS K from that dS (2 D flops per pair) instead of a
+ * recomputation of S and dP per query tile (6 D); the workspace then also
+ * holds dS (bf16, block_size * G per listed (token, block) pair).  Results
+ * are deterministic (bitwise repeatable). */
 nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
                        const void* o, const float* lse, const void* dO,
                        const int32_t* block_idx, const int32_t* cu_seqlens, void* dq, void* dk,
@@ -148,9 +154,11 @@ nsa_status nsa_sel_bwd(const nsa_sel_problem* p, const void* q, const void* k, c
  * device array built into the library instead of a caller buffer.  Nothing
  * is allocated (no hipMalloc, hipFree or allocating library call); each GPU
  * the library runs on holds its own copy of the array until the process
- * ends, its address looked up once per device.  A problem whose backward
- * needs more workspace (nsa_sel_bwd_workspace_bytes() > 64 MiB) is refused
- * with NSA_ERR_WORKSPACE before any HIP call.  The array keeps the last
+ * ends, its address looked up once per device.  When the dS hand-off (see
+ * nsa_sel_bwd) would not fit in the array, dQ recomputes dS instead (results
+ * then agree with nsa_sel_bwd's within the bf16 tolerance, not bitwise).  A
+ * problem that needs more workspace even so is refused with
+ * NSA_ERR_WORKSPACE before any HIP call.  The array keeps the last
  * call's contents; nothing in it needs to start at zero.  All calls on one
  * GPU share that GPU's array: calls that overlap in time on one GPU (other
  * streams, other threads) race and corrupt each other's results -- order
@@ -161,12 +169,15 @@ nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const vo
                                void* dk, void* dv, nsa_stream_t stream);
 
 /* The backward in three stages on one workspace; nsa_sel_bwd is exactly
- * prepare, dq, dkdv in this order.  prepare computes Delta and the block ->
- * query inversion (and the dK/dV work plan) into the workspace; dq and dkdv
+ * prepare, dkdv, dq in this order.  prepare computes Delta and the block ->
+ * query inversion (and the dK/dV work plan) into the workspace; dkdv and dq
  * read them, so they need a workspace prepared for the same problem,
  * block_idx, o and dO (a caller that reuses one block_idx with several
  * q/k/v/dO may also keep the inversion: dkdv uses Delta, so o/dO must match).
- * dkdv writes fp32 partials into the workspace. */
+ * dkdv writes fp32 partials into the workspace, and, for problems whose dQ
+ * takes over the dK/dV kernel's dS (see nsa_sel_bwd), that dS: dq must then
+ * run after dkdv (after nsa_sel_bwd_dkdv_blocks) on the same workspace; for
+ * the other problems dq and dkdv are independent. */
 nsa_status nsa_sel_bwd_prepare(const nsa_sel_problem* p, const void* o, const void* dO,
                                const int32_t* block_idx, const int32_t* cu_seqlens,
                                void* workspace, size_t workspace_bytes, nsa_stream_t stream);

@@ -439,9 +439,9 @@ def test_deterministic_bitwise(name):
 
 @pytest.mark.parametrize("name", ["bf16_T1024", "select_T8192", "causal_B4_T4096", "packed_8seq"])
 def test_staged_backward_equals_one_call(name):
-    """prepare, dq, dkdv_blocks, dkdv_reduce in order equal nsa_sel_bwd bit for
+    """prepare, dkdv_blocks, dkdv_reduce, dq in order equal nsa_sel_bwd bit for
     bit (the T 8192, G 16 workload has lists long enough to be split into fp32
-    partials)."""
+    partials, and its dQ takes over the dK/dV kernel's dS)."""
     w = workloads.make_workload(name)
     d = to_dev(w)
     cu = d.get("cu")
@@ -451,9 +451,9 @@ def test_staged_backward_equals_one_call(name):
                                  w.scale, cu, ms)
     st = nsa.BwdStages(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms)
     st.prepare(o, d["dO"])
-    dq2 = st.dq_stage(d["dO"], lse)
     st.dkdv_blocks(d["dO"], lse)
     dk2, dv2 = st.dkdv_reduce()
+    dq2 = st.dq_stage(d["dO"], lse)
     torch.cuda.synchronize()
     for a, b, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
         assert torch.equal(a, b), n

@@ -2,7 +2,10 @@
 workspace is a fixed device array inside the library) against nsa_sel_bwd on
 the same inputs, through the C ABI: two calls in a row, the second with a
 smaller problem (the array keeps the first call's contents), each bitwise
-equal to nsa_sel_bwd and within the bf16 gate of the float64 oracle."""
+equal to nsa_sel_bwd and within the bf16 gate of the float64 oracle.  With
+16 heads per KV head and sparse lists the dK/dV kernel hands dS over to dQ:
+bitwise equal again while that fits the array, and with dQ recomputing dS
+when it does not (dk, dv bitwise, dq within the gate)."""
 import ctypes
 
 import numpy as np
@@ -58,4 +61,41 @@ def test_noalloc_backward_equals_workspace_backward_twice():
         f = lambda x: x.float().cpu().numpy().astype(np.float64)
         for name, a in (("dq", dq1), ("dk", dk1), ("dv", dv1)):
             assert_close(name, f(a), ref[name], TOL[w.dtype])
+    assert nsa.wait_timeouts() == 0
+
+
+def _workspace_bytes(w, d):
+    cu = d["cu"]
+    ms = w.max_seqlen if w.packed else None
+    p = nsa.make_problem(d["q"], d["k"], d["idx"], w.block_size, w.scale, cu, ms)
+    return int(_lib.load().nsa_sel_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def test_noalloc_with_ds_handoff():
+    cases = [
+        # the hand-off fits the 64 MiB array: bitwise equal
+        (workloads.make_dense(1, 16, 1, 1024, 128, 4, 64, "bf16", "own_first_random", seed=63,
+                              name="noalloc-handoff"), True),
+        # its dS (about 256 MiB) does not: dQ recomputes dS
+        (workloads.make_dense(1, 32, 1, 4096, 32, 16, 64, "bf16", "own_first_random", seed=64,
+                              name="noalloc-handoff-too-big"), False),
+    ]
+    for w, fits in cases:
+        say(f"[{w.name}] B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} S={w.S} bs={w.block_size}")
+        d = to_dev(w)
+        assert (_workspace_bytes(w, d) <= 64 << 20) == fits
+        o, lse = nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale)
+        dq0, dk0, dv0 = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"],
+                                        w.block_size, w.scale)
+        dq1, dk1, dv1 = _noalloc(w, d, o, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(dk0, dk1) and torch.equal(dv0, dv1)
+        f = lambda x: x.float().cpu().numpy().astype(np.float64)
+        if fits:
+            assert torch.equal(dq0, dq1)
+        else:
+            assert_close("dq (hand-off vs recomputed)", f(dq1), f(dq0), TOL[w.dtype])
+        ref = oracle_full(w)
+        for name, a in (("dq", dq1), ("dk", dk1), ("dv", dv1), ("dq (nsa_sel_bwd)", dq0)):
+            assert_close(name, f(a), ref[name.split()[0]], TOL[w.dtype])
     assert nsa.wait_timeouts() == 0
