@@ -3,6 +3,11 @@
     python bench.py [--steps K] [--warmup W]
         [--workload select_T8192|causal_B4_T4096|packed_8seq|bf16_T1024]
 
+Without --workload the line's headline is select_T8192 (B1 Hq32 Hkv2 T8192
+bs64 S16, with the CPU oracle baseline) and "also" holds the same figures for
+the other D128 workloads, causal_B4_T4096 and packed_8seq, timed after it in
+the same process; with --workload only that one is timed.
+
 A step is one pass of the whole hot path over one batch of synthetic input:
 nsa_sel_fwd, then the backward's stages (Delta + block->query inversion +
 plan, the dK/dV block kernel, the dK/dV partial reduction, dQ).  Inputs are
@@ -34,12 +39,17 @@ PEAK_HBM_GBS = 8000.0
 
 # Workloads the benchmark runs (the f32 one is a parity case only).
 BENCH_WORKLOADS = ("select_T8192", "causal_B4_T4096", "packed_8seq", "bf16_T1024")
+HEADLINE = "select_T8192"
+ALSO = ("causal_B4_T4096", "packed_8seq")
 # Algorithmic flops per (row, key) pair of each timed stage, in units of D:
-# fwd S and PV; dq recomputes S and dP and forms dS K; dkdv recomputes S and
-# dP and forms dV and dK.
+# fwd S and PV; dq recomputes S and dP and forms dS K (or, when the dK/dV
+# kernel hands its dS over, forms dS K alone); dkdv recomputes S and dP and
+# forms dV and dK.
 STAGE_FLOPS_PER_PAIR_D = {"fwd": 4, "dq": 6, "dkdv": 8}
+DQ_HANDOFF_FLOPS_PER_PAIR_D = 2
 # The one kernel each of these stages launches (bf16 path).
 STAGE_KERNEL = {"fwd": "fwd_q_kernel", "dq": "dq_q_kernel", "dkdv": "dkdv_kernel"}
+DQ_HANDOFF_KERNEL = "dq_ds_kernel"
 
 
 def log(*a):
@@ -140,44 +150,18 @@ def cpu_baseline(w, n_tokens: int, window: int = 0, sink=None):
             "sample": f"{what} (N={n} pairs), float64 fwd+bwd"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="select_T8192", choices=BENCH_WORKLOADS)
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="tokens per (entry, head) of the CPU oracle sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--window", type=int, default=0,
-                    help="sliding window of this many keys (0: none); a variant, not the metric's workload")
-    ap.add_argument("--sink", action="store_true",
-                    help="per-head attention-sink logits (forward with sink, dsink stage timed too)")
-    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
-                    help="after the timed steps, convert a bf16 tensor of this many MiB to "
-                         "float32 once (a kernel of known traffic for scaling counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on exactly one GPU: the path has no multi-GPU mode "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(name, args, dev, cpu_leg: bool):
+    """Times K steps of one workload; returns its part of the JSON line."""
     import torch
 
     import block_sparse_attention_nsa_amd as nsa
     import workloads
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    w = workloads.make_workload(args.workload, seed=args.seed)
+    w = workloads.make_workload(name, seed=args.seed)
     G = w.Hq // w.Hkv
     N = useful_pairs(w.block_idx, G, w.block_size, row_groups(w), args.window)
     f_fwd, f_bwd = 4.0 * w.D * N, 10.0 * w.D * N
-    log(f"[bench] {args.workload}: {workloads.WORKLOADS[args.workload]}; N = {N} pairs, "
+    log(f"[bench] {name}: {workloads.WORKLOADS[name]}; N = {N} pairs, "
         f"F_fwd = {f_fwd:.4g}, F_bwd = {f_bwd:.4g}")
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -247,15 +231,20 @@ def main():
     log(f"[bench] ms/step {ms_step:.3f}; stages (ms): " +
         ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()))
 
+    # The dominant kernel and its algorithmic flops per launch.
+    kernel_of = dict(STAGE_KERNEL)
+    flops_d = dict(STAGE_FLOPS_PER_PAIR_D)
+    if stages.ds_handoff:
+        kernel_of["dq"], flops_d["dq"] = DQ_HANDOFF_KERNEL, DQ_HANDOFF_FLOPS_PER_PAIR_D
     dom = max(("fwd", "dq", "dkdv"), key=lambda n: stage_ms[n])
-    achieved = STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N / (stage_ms[dom] * 1e-3) / 1e12
+    achieved = flops_d[dom] * w.D * N / (stage_ms[dom] * 1e-3) / 1e12
     from block_sparse_attention_nsa_amd.traffic import source_hash
-    kern = STAGE_KERNEL[dom]
+    kern = kernel_of[dom]
     src = source_hash(kern)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(kern, args.workload, src), "kernel": kern,
-                "flops_per_launch": STAGE_FLOPS_PER_PAIR_D[dom] * w.D * N,
+                "traffic": stored_traffic(kern, name, src), "kernel": kern,
+                "flops_per_launch": flops_d[dom] * w.D * N,
                 "launch_ms": round(stage_ms[dom], 4)}
 
     if args.calibrate_copy_mb:
@@ -269,7 +258,7 @@ def main():
         del src_t, dst_t
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_leg:
         log(f"[bench] CPU oracle sample ({args.cpu_tokens} tokens per head) ...")
         cpu = cpu_baseline(w, args.cpu_tokens, args.window,
                            None if sink is None else sink.cpu().numpy())
@@ -277,11 +266,11 @@ def main():
             f"on {cpu['cores']} threads")
 
     if w.packed:
-        config = {"workload": args.workload, "description": workloads.WORKLOADS[args.workload],
+        config = {"workload": name, "description": workloads.WORKLOADS[name],
                   "n_seqs": w.n_seqs, "total_tokens": w.T, "max_seqlen": w.max_seqlen,
                   "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "S": w.S}
     else:
-        config = {"workload": args.workload, "description": workloads.WORKLOADS[args.workload], "B": w.B,
+        config = {"workload": name, "description": workloads.WORKLOADS[name], "B": w.B,
                   "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size,
                   "S": w.S}
     config["useful_pairs"] = N
@@ -311,9 +300,59 @@ def main():
         "step_ms_events": step_stats,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "git": git_sha(),
+        "ds_handoff": bool(stages.ds_handoff),
         "kernel_source_hash": src,
     }
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, choices=BENCH_WORKLOADS,
+                    help="time only this workload (default: select_T8192, then the other D128 ones)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens per (entry, head) of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window of this many keys (0: none); a variant, not the metric's workload")
+    ap.add_argument("--sink", action="store_true",
+                    help="per-head attention-sink logits (forward with sink, dsink stage timed too)")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the timed steps, convert a bf16 tensor of this many MiB to "
+                         "float32 once (a kernel of known traffic for scaling counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU: the path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_nsa_amd as nsa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    name = args.workload or HEADLINE
+    out = run_workload(name, args, dev, cpu_leg=not args.no_cpu_baseline)
+    if args.workload is None:
+        out["also"] = []
+        for other in ALSO:
+            torch.cuda.empty_cache()
+            r = run_workload(other, args, dev, cpu_leg=False)
+            out["also"].append({k: r[k] for k in ("config", "value", "ms_per_step", "frac_of_peak",
+                                                   "fwd_tflops", "bwd_tflops", "bwd_frac_of_peak",
+                                                   "stage_ms", "step_ms_events", "roofline",
+                                                   "ds_handoff")})
+    out["git"] = nsa.build_git()
+    if out["git"] == "unknown":
+        out["git"] = git_sha()
     print(json.dumps(out), flush=True)
 
 

@@ -34,6 +34,8 @@ __all__ = [
     "make_problem",
     "set_strides",
     "wait_timeouts",
+    "ds_handoff",
+    "build_git",
     "selection_attn",
     "SelectionAttn",
 ]
@@ -167,6 +169,20 @@ def bwd_workspace_bytes(p: _lib.Problem) -> int:
     return int(n)
 
 
+def ds_handoff(p: _lib.Problem) -> bool:
+    """Whether the backward of this problem hands dS from dK/dV over to dQ
+    (nsa_sel_bwd_ds_handoff)."""
+    r = _lib.load().nsa_sel_bwd_ds_handoff(p)
+    if r < 0:
+        raise _lib.NsaError("nsa_sel_bwd_ds_handoff", _lib.NSA_ERR_INVALID_ARG, _lib.last_error())
+    return bool(r)
+
+
+def build_git() -> str:
+    """The commit the loaded library was built from (nsa_build_git)."""
+    return _lib.load().nsa_build_git().decode()
+
+
 def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqlens=None,
                 max_seqlen=None, workspace=None, dq=None, dk=None, dv=None, sink=None, window=0):
     """dq, dk, dv = backward (nsa_sel_bwd); with sink logits (lse from the
@@ -220,6 +236,7 @@ class BwdStages:
         self.dq, self.dk, self.dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         set_strides(self.p, q=q, k=k, v=v, dq=self.dq, dk=self.dk, dv=self.dv)
         self.lib = _lib.load()
+        self.ds_handoff = ds_handoff(self.p)
 
     def prepare(self, o, dO):
         set_strides(self.p, o=o, dO=dO)

@@ -29,6 +29,8 @@ EXPORTS = (
     "nsa_sel_fwd_sink",
     "nsa_sel_bwd_dsink",
     "nsa_sel_wait_timeouts",
+    "nsa_sel_bwd_ds_handoff",
+    "nsa_build_git",
     "nsa_status_string",
     "nsa_last_error",
 )
@@ -115,6 +117,10 @@ def load():
     lib.nsa_sel_bwd_dsink.restype = st
     lib.nsa_sel_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
     lib.nsa_sel_wait_timeouts.restype = st
+    lib.nsa_sel_bwd_ds_handoff.argtypes = [P]
+    lib.nsa_sel_bwd_ds_handoff.restype = ctypes.c_int32
+    lib.nsa_build_git.argtypes = []
+    lib.nsa_build_git.restype = ctypes.c_char_p
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []

@@ -49,15 +49,33 @@ def _hipcc() -> str:
     return "hipcc"
 
 
+def _git_commit() -> str:
+    """Short commit of the checkout, "+dirty" if the library's sources or
+    header differ from it; "unknown" outside a git checkout."""
+    try:
+        sha = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True, timeout=30)
+        if sha.returncode != 0 or not sha.stdout.strip():
+            return "unknown"
+        dirty = subprocess.run(["git", "status", "--porcelain", "--", CSRC, INCLUDE], cwd=ROOT,
+                               capture_output=True, text=True, timeout=30).stdout.strip()
+        return sha.stdout.strip() + ("+dirty" if dirty else "")
+    except (OSError, subprocess.SubprocessError):
+        return "unknown"
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     hipcc = _hipcc()
+    commit = _git_commit()
     procs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
         objs.append(obj)
         extra = [] if src in AGPR_SOURCES else VGPR_FORM
+        if src == "nsa_api.hip":
+            extra = extra + [f'-DNSA_BUILD_GIT="{commit}"']
         cmd = [hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -426,6 +426,23 @@ const char* nsa_status_string(nsa_status s) {
 
 const char* nsa_last_error(void) { return g_last_error.c_str(); }
 
+// Set by the build (the commit of the sources compiled).
+#ifndef NSA_BUILD_GIT
+#define NSA_BUILD_GIT "unknown"
+#endif
+const char* nsa_build_git(void) { return NSA_BUILD_GIT; }
+
+int32_t nsa_sel_bwd_ds_handoff(const nsa_sel_problem* p) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    if (!p) {
+        fail(NSA_ERR_INVALID_ARG, "problem pointer is NULL");
+        return -1;
+    }
+    if (make_problem(p, hp) != NSA_OK) return -1;
+    return hp.ds_handoff ? 1 : 0;
+}
+
 nsa_status nsa_sel_wait_timeouts(uint64_t* count) {
     g_last_error.clear();
     if (!count) return fail(NSA_ERR_INVALID_ARG, "count is NULL");

@@ -36,6 +36,8 @@ _COMMON = ("nsa_device.h", "nsa_internal.h", "nsa_api.hip")
 KERNEL_SOURCES = {
     "fwd_q_kernel": ("nsa_query.hip",) + _COMMON,
     "dq_q_kernel": ("nsa_query.hip",) + _COMMON,
+    # reads the dS the dK/dV kernel stores and the inversion's slot positions
+    "dq_ds_kernel": ("nsa_query.hip", "nsa_dkdv.hip", "nsa_common.hip") + _COMMON,
     "dkdv_kernel": ("nsa_dkdv.hip", "nsa_common.hip") + _COMMON,
 }
 

@@ -276,6 +276,15 @@ size_t nsa_sel_invert_tokens_capacity(const nsa_sel_problem* p);
  * device (a blocking device-to-host copy of the counters). */
 nsa_status nsa_sel_wait_timeouts(uint64_t* count);
 
+/* Whether nsa_sel_bwd hands dS from the dK/dV kernel over to dQ for this
+ * problem (the conditions stated at nsa_sel_bwd): 1 yes, 0 no, -1 the
+ * problem is invalid (see nsa_last_error()).  Host only, no HIP call. */
+int32_t nsa_sel_bwd_ds_handoff(const nsa_sel_problem* p);
+
+/* The git commit the library was built from ("unknown" outside a git
+ * checkout; "+dirty" when its sources had uncommitted changes). */
+const char* nsa_build_git(void);
+
 /* Text of a status code, and the detail of the calling thread's last
  * error (empty string if none). */
 const char* nsa_status_string(nsa_status s);

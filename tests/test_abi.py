@@ -252,3 +252,26 @@ def test_noalloc_backward_checks_before_any_hip_call():
     st = lib.nsa_sel_bwd_noalloc(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                  FAKE, None)
     assert st == _lib.NSA_ERR_WORKSPACE and str(64 << 20) in _lib.last_error()
+
+
+def test_ds_handoff_query():
+    """nsa_sel_bwd_ds_handoff states when dK/dV hands dS over to dQ: bf16,
+    16-head groups, block_size >= 32, S <= 64, no window, and lists that
+    cannot cover whole causal prefixes (S * block_size < length)."""
+    lib = _lib.load()
+    q = lambda **kw: lib.nsa_sel_bwd_ds_handoff(_prob(**kw))
+    cfg2 = dict(dtype=1, D=128, block_size=64, Hq=32, Hkv=2, T=8192, B=1, S=16)
+    assert q(**cfg2) == 1, _lib.last_error()
+    assert q(**{**cfg2, "Hq": 64}) == 1                      # G = 32
+    assert q(**{**cfg2, "S": 128}) == 0                      # whole prefixes possible
+    assert q(**{**cfg2, "dtype": 0, "D": 64}) == 0           # f32 path
+    assert q(**{**cfg2, "Hq": 6}) == 0                       # G = 3
+    assert q(**{**cfg2, "block_size": 16, "S": 64}) == 0     # 16-key blocks
+    assert q(**{**cfg2, "S": 65}) == 0                       # more than 64 slots
+    assert q(**{**cfg2, "window": 512}) == 0
+    assert q(**{**cfg2, "Hq": 33}) == -1 and _lib.last_error()  # invalid problem
+
+
+def test_build_git_reported():
+    s = _lib.load().nsa_build_git().decode()
+    assert s == "unknown" or re.fullmatch(r"[0-9a-f]{4,40}(\+dirty)?", s), s
