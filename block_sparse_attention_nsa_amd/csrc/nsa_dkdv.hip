@@ -138,11 +138,13 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 // WIN: the problem has a sliding window (keys t - window < j only); the
 // paired launch never has one.  BK: keys of one block (BS, except 16-key
 // blocks, which run on a 32-key tile whose upper 16 keys -- the next
-// block's -- are masked out and never written).  DS: the S waves also store
-// dS (bf16) for the dQ kernel that takes it over (G a multiple of 16, so a
-// 16-row half of a step is 16 heads of one token): dsout[entry][key in the
-// block][head], entry = region_base + the row's position in the block's list.
-template <int D, int BS, bool PAIRED, bool WIN, int BK = BS, bool DS = false>
+// block's -- are masked out and never written).  DS != 0: the S waves also
+// store dS (bf16) for the dQ kernel that takes it over, dsout[entry][key in
+// the block][head], entry = region_base + the row's position in the block's
+// list; DS = 1 for G a multiple of 16 (a 16-row half of a step is 16 heads of
+// one token), DS = 2 for G = 4 or 8 (the four rows a lane holds are four
+// heads of one token).
+template <int D, int BS, bool PAIRED, bool WIN, int BK = BS, int DS = 0>
 __global__ __launch_bounds__(BS / 16 * 64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
@@ -202,6 +204,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     const int* list = PAIRED ? iota + lu * p.bs : tokens + region_base(p, s, hkv) + off[lu];
     const int R = (off[lu + 1] - off[lu]) * G;
     const int64_t ds_entry0 = DS ? region_base(p, s, hkv) + off[lu] : 0;
+    const int gsh = G == 4 ? 2 : 3;
     const int f_begin = it.kitem * CR, f_end = min(R, f_begin + CR);
     const int nsteps = (f_end - f_begin + 31) / 32;
     static_assert(BK == BS || (BK == 16 && BS == 32 && !PAIRED), "a 16-key block on a 32-key tile");
@@ -312,16 +315,27 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                     pk[1][kt] = __builtin_bit_cast(uint4, pack8(dsv[kt][0], dsv[kt][1]));
                 }
                 if constexpr (DS) {
-                    // dS of the step's two 16-row halves (16 heads of one
-                    // token each): lane (g, r) holds heads 4 g .. 4 g + 3 of
-                    // key 32 a + 16 kt + r, 8 contiguous bytes.
+                    // dS of the step's rows: lane (g, r) holds list rows
+                    // fl .. fl + 3 (fl = the step's first row + 16 rt + 4 g)
+                    // of key 32 a + 16 kt + r -- with G a multiple of 4, four
+                    // heads of one entry, 8 contiguous bytes.
                     const int fr0 = __builtin_amdgcn_readfirstlane(f_end - 32 * (i + 1));
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt) {
-                        const int fr = fr0 + 16 * rt;
-                        if (fr < f_begin) continue;  // rows of another item
-                        const int e = fr / G, hh = fr - e * G;
-                        uint16_t* dst = dsout + ((ds_entry0 + e) * BS + 32 * a) * G + hh + 4 * g;
+                        const int fr = fr0 + 16 * rt, fl = fr + 4 * g;
+                        uint16_t* dst;
+                        if constexpr (DS == 1) {
+                            // G a multiple of 16: a 16-row half is one entry
+                            // (wave-uniform).
+                            if (fr < f_begin) continue;  // rows of another item
+                            const int e = fr / G;
+                            dst = dsout + ((ds_entry0 + e) * BS + 32 * a) * G + (fr - e * G) + 4 * g;
+                        } else {
+                            // G = 4 or 8: entries differ across the lanes.
+                            if (fl < f_begin) continue;
+                            const int e = fl >> gsh;
+                            dst = dsout + ((ds_entry0 + e) * BS + 32 * a) * G + (fl - e * G);
+                        }
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt) {
                             const uint4 x = pk[1][kt];
@@ -701,7 +715,8 @@ hipError_t launch_dkdv_bf16(const HostProblem& hp, const void* q, const void* k,
         } else if (hp.ds_handoff) {
             // Also stores dS for the dQ kernel that takes it over.
             NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs,
-                              go(dkdv_kernel<D, BS, false, false, BS, true>, items, BS / 16 * 64));
+                              if (hp.dev.G % 16 == 0) go(dkdv_kernel<D, BS, false, false, BS, 1>, items, BS / 16 * 64);
+                              else go(dkdv_kernel<D, BS, false, false, BS, 2>, items, BS / 16 * 64));
         } else {
             NSA_DISPATCH_D_BS(hp.dev.D, hp.dev.bs, go(dkdv_kernel<D, BS, false, false>, items, BS / 16 * 64));
         }

@@ -1019,13 +1019,23 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
 //       listed block (its first occurrence in the row), else -1.
 // Then dQ needs no second pass over S and dP: dq = scale sum over the row's
 // listed blocks of dS K, one product (2 D flops per pair instead of 6 D) and
-// no q, dO, lse or Delta reads.  The walk is the dQ kernel's (16 tiles of 16
-// heads of one token, the union of the workgroup's listed blocks in
-// ascending order, K shared through an LDS ring); per job, each tile whose
-// token lists the block takes its dS tile (staged by buffer-to-LDS loads,
-// read transposed as the B operand) and adds K^T dS^T.  G is a multiple of
-// 16, block_size >= 32, S <= 64 and there is no sliding window.
-template <int D, int BS, int RT, int NW>
+// no q, dO, lse or Delta reads.  The walk is the dQ kernel's (16-row tiles,
+// the union of the workgroup's listed blocks in ascending order, K shared
+// through an LDS ring); per job, each tile one of whose tokens lists the
+// block takes its dS tile (staged by buffer-to-LDS loads, zeros for the
+// tile's tokens that do not list it, read transposed as the B operand) and
+// adds K^T dS^T.  TPT = tokens per tile: 1 (16 heads of one token, G a
+// multiple of 16), 2 (G = 8) or 4 (G = 4).  dS tile in LDS, 32 bytes per
+// key: [key][16 tile rows] for TPT <= 2; for TPT = 4 [key pair][token]
+// [key of the pair][4 heads], so that one 16-byte load holds two keys of
+// one token (8 contiguous bytes per key in ds).  block_size >= 32, S <= 64,
+// no sliding window, and a (z, hkv) region of ds spans < 2^31 bytes.
+// Byte of (key, heads 4 col4 .. + 3) in a TPT = 4 dS tile.
+__device__ __forceinline__ uint32_t ds_tile_byte(int key, int col4) {
+    return (uint32_t)((((key >> 1) * 4 + col4) * 16) + (key & 1) * 8);
+}
+
+template <int D, int BS, int RT, int NW, int TPT>
 __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
                                                         const uint16_t* __restrict__ k,
                                                         const int* __restrict__ idx,
@@ -1035,7 +1045,9 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
     using L = RowTile<D>;
     constexpr int ND = D / 16, JK = JobKeys<BS>::JK, NKS = JK / 32, NDMA = JK / 32;
     static_assert(BS >= 32 && JobKeys<BS>::KT == JK, "whole 32-key steps of one block");
+    static_assert(TPT == 1 || TPT == 2 || TPT == 4, "tokens per tile");
     using DB = DsBuf<JK, NW, RT>;
+    constexpr uint32_t kOob = 0xFFFFFFF0u;  // past the region descriptor (2^31 bytes): loads zeros
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned long long* umask = reinterpret_cast<unsigned long long*>(smem);
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
@@ -1057,62 +1069,103 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);
 
-    // Per tile: its token's block list and list positions (lane x holds slot
-    // x), its first head inside the group, its accumulators.
+    // Per tile and token: the token's block list and list positions (lane x
+    // holds slot x); per tile its first head inside the group and its
+    // accumulators.
     const int* rows = idx_row(p, s, idx, wc.hkv, wc.T0);
     const int* prows = posmap + (rows - idx);
-    const int64_t ds_base = region_base(p, s, wc.hkv);
-    int u_l[RT], pos_l[RT], h0[RT], tok[RT];
-    bool tokv[RT];
+    int u_l[RT][TPT], pos_l[RT][TPT], h0[RT];
     f32x4 acc[RT][ND];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         const int tau = w * RT + i;
-        tok[i] = tau / qg.n_ht;
-        tokv[i] = tok[i] < qg.TW && wc.T0 + tok[i] < s.len;
-        h0[i] = 16 * (tau % qg.n_ht);
-        const bool have = tokv[i] && lane < p.S;
-        u_l[i] = have ? rows[tok[i] * p.S + lane] : -1;
-        pos_l[i] = have ? prows[tok[i] * p.S + lane] : -1;
+        h0[i] = TPT == 1 ? 16 * (tau % qg.n_ht) : 0;
+#pragma unroll
+        for (int a = 0; a < TPT; ++a) {
+            const int tok = TPT == 1 ? tau / qg.n_ht : tau * TPT + a;
+            const bool have = tok < qg.TW && wc.T0 + tok < s.len && lane < p.S;
+            u_l[i][a] = have ? rows[tok * p.S + lane] : -1;
+            pos_l[i][a] = have ? prows[tok * p.S + lane] : -1;
+        }
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
 
-    // This lane's 16 bytes of a dS tile: key 32 j + lane / 2 of load j,
-    // heads 8 (lane % 2) .. + 7 of the tile.
-    const uint32_t ds_lane = (uint32_t)((lane >> 1) * p.G * 2 + (lane & 1) * 16);
-    // Slot of tile i's token standing for block u, as a lane mask (0: the
-    // token does not list u).
-    auto listing = [&](int i, int u) __attribute__((always_inline)) -> uint64_t {
-        return __ballot(u_l[i] == u && pos_l[i] >= 0);
+    // One descriptor over the (z, hkv) region of ds; a lane's offset selects
+    // its token's entry.  Lane l of 1 KB load jd fills tile bytes 1024 jd +
+    // 16 l: key 32 jd + l / 2, heads h0 + 8 (l % 2) (TPT 1); key 32 jd + l / 2
+    // of token l % 2 (TPT 2); keys 32 jd + 2 (l / 4) + {0, 1} of token l % 4
+    // (TPT 4).
+    const buf_rsrc rs = make_rsrc(ds + region_base(p, s, wc.hkv) * BS * p.G, 0x80000000u);
+    const int my_tok = TPT == 1 ? 0 : (lane & (TPT - 1));
+    const int my_key = TPT == 4 ? 2 * (lane >> 2) : (lane >> 1);
+    const int my_head = TPT == 1 ? 8 * (lane & 1) : 0;
+    // Entry of tile i's token a for block u (-1: it does not list u); all
+    // wave-uniform.
+    auto listing = [&](int i, int a, int u) __attribute__((always_inline)) -> uint64_t {
+        return __ballot(u_l[i][a] == u && pos_l[i][a] >= 0);
     };
+    auto entry = [&](int i, int a, int u) __attribute__((always_inline)) -> int {
+        const uint64_t m = listing(i, a, u);
+        return m ? __builtin_amdgcn_readlane(pos_l[i][a], (int)__builtin_ctzll(m)) : -1;
+    };
+    // One token per tile: a descriptor per dS tile, fixed lane offsets.
+    const int64_t ds_base = region_base(p, s, wc.hkv);
+    const uint32_t lane_off = (uint32_t)((my_key * p.G + my_head) * 2);
     auto issue_ds = [&](const Job& jb, DB& buf) __attribute__((always_inline)) -> int {
         if (!jb.ok) return 0;
+        const int kofs = jb.j0 - jb.u * BS;
         int n = 0;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            const uint64_t m = listing(i, jb.u);
-            if (!m) continue;
-            const int pos = __builtin_amdgcn_readlane(pos_l[i], (int)__builtin_ctzll(m));
-            const uint16_t* src = ds + ((ds_base + pos) * BS + (jb.j0 - jb.u * BS)) * p.G + h0[i];
-            const buf_rsrc rs = make_rsrc(src, (uint32_t)((JK - 1) * p.G * 2 + 32));
+            if constexpr (TPT == 1) {
+                const uint64_t m = listing(i, 0, jb.u);
+                if (!m) continue;
+                const int e0 = __builtin_amdgcn_readlane(pos_l[i][0], (int)__builtin_ctzll(m));
+                const buf_rsrc rt = make_rsrc(ds + ((ds_base + e0) * BS + kofs) * p.G + h0[i],
+                                              (uint32_t)((JK - 1) * p.G * 2 + 32));
 #pragma unroll
-            for (int jd = 0; jd < NDMA; ++jd)
-                dma16(rs, reinterpret_cast<uint8_t*>(buf.v[w][i]) + 1024 * jd,
-                      ds_lane + (uint32_t)(32 * jd * p.G * 2));
+                for (int jd = 0; jd < NDMA; ++jd)
+                    dma16(rt, reinterpret_cast<uint8_t*>(buf.v[w][i]) + 1024 * jd,
+                          lane_off + (uint32_t)(32 * jd * p.G * 2));
+                n += NDMA;
+                continue;
+            }
+            int e[TPT];
+            bool any = false;
+#pragma unroll
+            for (int a = 0; a < TPT; ++a) {
+                e[a] = entry(i, a, jb.u);
+                any = any || e[a] >= 0;
+            }
+            if (!any) continue;
+            int mine = e[0];
+#pragma unroll
+            for (int a = 1; a < TPT; ++a) mine = my_tok == a ? e[a] : mine;
+#pragma unroll
+            for (int jd = 0; jd < NDMA; ++jd) {
+                const uint32_t off =
+                    mine < 0 ? kOob
+                             : (uint32_t)(((mine * BS + kofs + 32 * jd + my_key) * p.G + h0[i] + my_head) * 2);
+                dma16(rs, reinterpret_cast<uint8_t*>(buf.v[w][i]) + 1024 * jd, off);
+            }
             n += NDMA;
         }
         return n;
     };
-    // dQ^T += K^T dS^T for the tiles whose token lists the job's block: the
-    // transposed K operand of each 32-key step is read once for both tiles.
+    // dQ^T += K^T dS^T for the tiles one of whose tokens lists the job's
+    // block: the transposed K operand of each 32-key step is read once for
+    // both tiles.
+    const int q4 = r >> 2, c4 = r & 3;  // (TPT = 4 tile reads)
     auto compute = [&](const Job& cur, const KStage<D, JK>& sg, const DB& buf) {
         bool act[RT];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            act[i] = listing(i, cur.u) != 0ull;
+            act[i] = false;
+#pragma unroll
+            for (int a = 0; a < TPT; ++a) act[i] = act[i] || listing(i, a, cur.u) != 0ull;
             any = any || act[i];
         }
         if (!any) return;
@@ -1130,9 +1183,18 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
 #pragma unroll
             for (int i = 0; i < RT; ++i) {
                 if (!act[i]) continue;
-                // B operand dS^T[keys 32 ks_ + 4 g + e, 32 ks_ + 16 + 4 g + e][head r]:
+                // B operand dS^T[keys 32 ks_ + 4 g + e, 32 ks_ + 16 + 4 g + e][row r]:
                 // the key order of the transposed K reads above.
-                const bf16x8 bop = lds_col_operand(buf.v[w][i], 16, 32 * ks_, 32 * ks_ + 16, 0, lane);
+                bf16x8 bop;
+                if constexpr (TPT == 4) {
+                    const uint8_t* tb = reinterpret_cast<const uint8_t*>(buf.v[w][i]);
+                    const int klo = 32 * ks_ + 4 * g + q4;
+                    const uint2 lo = lds_read_tr(reinterpret_cast<const uint16_t*>(tb + ds_tile_byte(klo, c4)));
+                    const uint2 hi = lds_read_tr(reinterpret_cast<const uint16_t*>(tb + ds_tile_byte(klo + 16, c4)));
+                    bop = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                } else {
+                    bop = lds_col_operand(buf.v[w][i], 16, 32 * ks_, 32 * ks_ + 16, 0, lane);
+                }
 #pragma unroll
                 for (int dt = 0; dt < ND; ++dt) acc[i][dt] = mfma(kop[dt], bop, acc[i][dt]);
             }
@@ -1143,9 +1205,20 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-        if (!tokv[i]) continue;
-        const int h = wc.hkv * p.G + h0[i] + r;
-        uint16_t* drow = dq + row_off(p.ldq, s, h, wc.T0 + tok[i]) + 4 * g;
+        int h, t;
+        if constexpr (TPT == 1) {
+            // 16 heads of one token (the tile's head range lies inside G)
+            const int tok = (w * RT + i) / qg.n_ht;
+            if (tok >= qg.TW || wc.T0 + tok >= s.len) continue;
+            h = wc.hkv * p.G + h0[i] + r;
+            t = wc.T0 + tok;
+        } else {
+            const TileRow trw = tile_row(p, qg, wc.hkv, wc.T0, s.len, w * RT + i, r);
+            if (!trw.valid) continue;
+            h = trw.h;
+            t = trw.t;
+        }
+        uint16_t* drow = dq + row_off(p.ldq, s, h, t) + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
             const uint2 pk = make_uint2(pack_bf16x2(acc[i][dt][0] * p.scale, acc[i][dt][1] * p.scale),
@@ -1302,9 +1375,15 @@ hipError_t launch_dq_handoff(const HostProblem& hp, const void* k, const int* bl
                            (const uint16_t*)k, block_idx, (const int*)ws.posmap,
                            (const uint16_t*)ws.ds, (uint16_t*)dq);
     };
-    const int D = hp.dev.D, BS = hp.dev.bs;
-#define NSA_DQ_DS(D_, BS_) \
-    else if (D == D_ && BS == BS_) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q>);
+    const int D = hp.dev.D, BS = hp.dev.bs, G = hp.dev.G;
+    const int tpt = G % 16 == 0 ? 1 : G == 8 ? 2 : G == 4 ? 4 : 0;
+#define NSA_DQ_DS(D_, BS_)                                                          \
+    else if (D == D_ && BS == BS_) {                                                \
+        if (tpt == 1) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 1>);                   \
+        else if (tpt == 2) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 2>);              \
+        else if (tpt == 4) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 4>);              \
+        else return hipErrorInvalidValue;                                           \
+    }
     if (false) {}
     NSA_DQ_DS(32, 32) NSA_DQ_DS(32, 64) NSA_DQ_DS(32, 128)
     NSA_DQ_DS(64, 32) NSA_DQ_DS(64, 64) NSA_DQ_DS(64, 128)

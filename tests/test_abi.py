@@ -256,8 +256,9 @@ def test_noalloc_backward_checks_before_any_hip_call():
 
 def test_ds_handoff_query():
     """nsa_sel_bwd_ds_handoff states when dK/dV hands dS over to dQ: bf16,
-    16-head groups, block_size >= 32, S <= 64, no window, and lists that
-    cannot cover whole causal prefixes (S * block_size < length)."""
+    G = 4, 8 or a multiple of 16, block_size >= 32, S <= 64, no window,
+    lists that cannot cover whole causal prefixes (S * block_size < length)
+    and a per-(batch, KV head) dS region below 2^31 bytes."""
     lib = _lib.load()
     q = lambda **kw: lib.nsa_sel_bwd_ds_handoff(_prob(**kw))
     cfg2 = dict(dtype=1, D=128, block_size=64, Hq=32, Hkv=2, T=8192, B=1, S=16)
@@ -266,6 +267,13 @@ def test_ds_handoff_query():
     assert q(**{**cfg2, "S": 128}) == 0                      # whole prefixes possible
     assert q(**{**cfg2, "dtype": 0, "D": 64}) == 0           # f32 path
     assert q(**{**cfg2, "Hq": 6}) == 0                       # G = 3
+    assert q(**{**cfg2, "Hq": 8}) == 1                       # G = 4
+    assert q(**{**cfg2, "Hq": 16}) == 1                      # G = 8
+    assert q(**{**cfg2, "Hq": 4}) == 0                       # G = 2
+    assert q(**{**cfg2, "Hq": 24}) == 0                      # G = 12
+    # dS region of one (batch, KV head): T * S * block_size * G * 2 bytes
+    assert q(**{**cfg2, "T": (1 << 16) - 64}) == 1
+    assert q(**{**cfg2, "T": 1 << 16}) == 0
     assert q(**{**cfg2, "block_size": 16, "S": 64}) == 0     # 16-key blocks
     assert q(**{**cfg2, "S": 65}) == 0                       # more than 64 slots
     assert q(**{**cfg2, "window": 512}) == 0
