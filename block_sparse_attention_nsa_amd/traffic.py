@@ -124,6 +124,66 @@ def stats_table(path: str, header: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+SIMDS = 1024            # 256 CUs x 4 SIMDs
+CLOCK_GHZ = 2.4         # peak engine clock the MFMA peak is quoted at
+
+
+def stats_avg_ns(path: str, pattern: str) -> float:
+    """Summed average duration (ns) of the kernels a regex matches in a
+    kernel_stats.csv (a stage that launches two instantiations per step)."""
+    t = 0.0
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if re.search(pattern, r["Name"]):
+                t += float(r["AverageNs"])
+    return t if t > 0 else float("nan")
+
+
+def sq_table(paths, kernels, header: str, stats: str = None) -> str:
+    """SQ counters of one workload's passes (run_counter_collection.csv each)
+    as per-launch whole-device totals for each kernel regex, their shares of
+    SQ_WAVE_CYCLES, and the MFMA-busy share of all SIMD cycles at the peak
+    clock (kernel time from a kernel_stats.csv of an unprofiled-counter run
+    if given, else from the counter dispatches' own timestamps)."""
+    tot = {k: {} for k in kernels}
+    launches = {k: {} for k in kernels}
+    dur = {k: {} for k in kernels}
+    for path in paths:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                for k in kernels:
+                    if not re.search(k, row["Kernel_Name"]):
+                        continue
+                    c = row["Counter_Name"]
+                    tot[k][c] = tot[k].get(c, 0.0) + float(row["Counter_Value"])
+                    launches[k].setdefault(c, set()).add((path, row["Dispatch_Id"]))
+                    if "End_Timestamp" in row:
+                        dur[k][(path, row["Dispatch_Id"])] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    counters = sorted({c for k in kernels for c in tot[k]})
+    per = {k: {c: tot[k][c] / max(1, len(launches[k].get(c, ()))) for c in tot[k]} for k in kernels}
+    avg_ns = {k: (sum(dur[k].values()) / len(dur[k]) if dur[k] else float("nan")) for k in kernels}
+    if stats:
+        avg_ns = {k: stats_avg_ns(stats, k) for k in kernels}
+    w = max(14, *(len(k) + 2 for k in kernels))
+    lines = [header.rstrip("\n"), f"{'counter':30s}" + "".join(f"{k:>{w}s}" for k in kernels)]
+    for c in counters:
+        lines.append(f"{c:30s}" + "".join(f"{per[k].get(c, float('nan')):>{w}.4g}" for k in kernels))
+    lines.append("")
+    lines.append("shares of SQ_WAVE_CYCLES (resident wave time):")
+    for c in counters:
+        if c.startswith(("SQ_ACTIVE_INST", "SQ_WAIT")):
+            lines.append(f"{c:30s}" + "".join(
+                f"{per[k].get(c, float('nan')) / per[k].get('SQ_WAVE_CYCLES', float('nan')):>{w}.2f}"
+                for k in kernels))
+    lines.append("")
+    lines.append(f"{'kernel time per launch (us)':30s}" + "".join(f"{avg_ns[k] / 1e3:>{w}.1f}" for k in kernels))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+        lines.append(f"{'MFMA busy share of SIMD cycles':30s}" + "".join(
+            f"{per[k].get('SQ_VALU_MFMA_BUSY_CYCLES', float('nan')) / (SIMDS * avg_ns[k] * CLOCK_GHZ):>{w}.3f}"
+            for k in kernels))
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--stats", help="format this kernel_stats.csv into --out instead (with "
@@ -135,7 +195,21 @@ def main() -> None:
     ap.add_argument("--write", help="run_counter_collection.csv with WRITE_SIZE")
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", default="", help="the profiling commands, recorded in the output")
+    ap.add_argument("--sq", nargs="+", help="format these SQ counter passes (run_counter_collection.csv "
+                                            "each) for the --kernels into --out instead")
+    ap.add_argument("--kernels", default="fwd_q_kernel,dq_q_kernel,dq_ds_kernel,dkdv_kernel",
+                    help="comma-separated kernel regexes (--sq)")
     a = ap.parse_args()
+    if a.sq:
+        ks = [k for k in a.kernels.split(",") if k]
+        head = (f"# rocprofv3 SQ counters, per launch (whole device), workload {a.workload}\n"
+                f"# command: {a.command}\n"
+                f"# kernel sources hash: {source_hash()}\n")
+        text = sq_table(a.sq, ks, head, a.stats)
+        with open(a.out, "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
     if a.stats:
         head = (f"# rocprofv3 kernel statistics, workload {a.workload}\n"
                 f"# command: {a.command}\n"
