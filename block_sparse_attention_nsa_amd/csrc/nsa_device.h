@@ -110,6 +110,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 // two values per instruction (NaN stays NaN).
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
@@ -257,6 +258,8 @@ static __device__ unsigned int g_wait_timeouts;
 // vector-memory wait.
 __device__ __forceinline__ void spin_ge(const int* ctr, int target, int* fail) {
     const uint32_t a = lds_addr(ctr);
+    // (Not unrolled: eight copies per call site bloated the ring loops.)
+#pragma nounroll
     for (int it = 0; it < (1 << 18); ++it) {
         int v;
         asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");

@@ -339,8 +339,12 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt) {
                             const uint4 x = pk[1][kt];
-                            *reinterpret_cast<uint2*>(dst + (int64_t)(16 * kt + r) * G) =
-                                rt == 0 ? make_uint2(x.x, x.y) : make_uint2(x.z, x.w);
+                            // Non-temporal: dS is read once, by the dQ kernel
+                            // after the reduce, and would otherwise push the
+                            // fp32 partials and the q / dO rows out of the
+                            // caches.
+                            const u32x2 v = rt == 0 ? u32x2{x.x, x.y} : u32x2{x.z, x.w};
+                            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(dst + (int64_t)(16 * kt + r) * G));
                         }
                     }
                 }
