@@ -146,7 +146,7 @@ def sq_table(paths, kernels, header: str, stats: str = None) -> str:
     clock (kernel time from a kernel_stats.csv of an unprofiled-counter run
     if given, else from the counter dispatches' own timestamps)."""
     tot = {k: {} for k in kernels}
-    launches = {k: {} for k in kernels}
+    launches = {k: {} for k in kernels}  # counter -> {kernel name: dispatches}
     dur = {k: {} for k in kernels}
     for path in paths:
         with open(path) as f:
@@ -156,12 +156,18 @@ def sq_table(paths, kernels, header: str, stats: str = None) -> str:
                         continue
                     c = row["Counter_Name"]
                     tot[k][c] = tot[k].get(c, 0.0) + float(row["Counter_Value"])
-                    launches[k].setdefault(c, set()).add((path, row["Dispatch_Id"]))
-                    if "End_Timestamp" in row:
-                        dur[k][(path, row["Dispatch_Id"])] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+                    launches[k].setdefault(c, {}).setdefault(row["Kernel_Name"], set()).add(row["Dispatch_Id"])
+                    if "End_Timestamp" in row and path == paths[0]:
+                        dur[k][row["Dispatch_Id"]] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
     counters = sorted({c for k in kernels for c in tot[k]})
-    per = {k: {c: tot[k][c] / max(1, len(launches[k].get(c, ()))) for c in tot[k]} for k in kernels}
-    avg_ns = {k: (sum(dur[k].values()) / len(dur[k]) if dur[k] else float("nan")) for k in kernels}
+    # Per stage launch: a stage may launch two instantiations per step (the
+    # paired dK/dV kernel and the per-block one, which then exits at once),
+    # so totals are divided by the most-launched instantiation's count.
+    per = {k: {c: tot[k][c] / max(1, max((len(v) for v in launches[k].get(c, {}).values()), default=1))
+               for c in tot[k]} for k in kernels}
+    avg_ns = {k: (sum(dur[k].values()) / max(1, max((len(v) for c in launches[k]
+                                                       for v in launches[k][c].values()), default=1))
+                  if dur[k] else float("nan")) for k in kernels}
     if stats:
         avg_ns = {k: stats_avg_ns(stats, k) for k in kernels}
     w = max(14, *(len(k) + 2 for k in kernels))
