@@ -99,3 +99,61 @@ def test_noalloc_with_ds_handoff():
         for name, a in (("dq", dq1), ("dk", dk1), ("dv", dv1), ("dq (nsa_sel_bwd)", dq0)):
             assert_close(name, f(a), ref[name.split()[0]], TOL[w.dtype])
     assert nsa.wait_timeouts() == 0
+
+
+def test_noalloc_backward_under_graph_capture():
+    """The callers this entry point is for: forward (preallocated outputs) and
+    nsa_sel_bwd_noalloc captured into one HIP graph and replayed three
+    times, with other eager work and a synchronisation between replays;
+    every replay's o, lse, dq, dk, dv must equal the eager results bitwise.
+    Covers the hand-off (16 heads per KV head, sparse lists) and a packed
+    4-head problem.  The first call on the device (the scratch address
+    lookup) happens before the capture."""
+    cases = [
+        workloads.make_dense(1, 16, 1, 1024, 128, 4, 64, "bf16", "own_first_random", seed=65,
+                             name="graph-handoff"),
+        workloads.make_thd([300, 0, 77, 160], 8, 2, 64, 5, 32, "bf16", "own_first_random",
+                           seed=66, name="graph-packed"),
+    ]
+    for w in cases:
+        say(f"[{w.name}] graph capture: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D}")
+        d = to_dev(w)
+        ms = w.max_seqlen if w.packed else None
+        o = torch.empty_like(d["q"])
+        lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32,
+                          device=d["q"].device)
+        nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, d["cu"], ms,
+                        out=o, lse=lse)
+        dq0, dk0, dv0 = _noalloc(w, d, o, lse)
+        torch.cuda.synchronize()
+        ref = [x.clone() for x in (o, lse, dq0, dk0, dv0)]
+
+        cu, p = d["cu"], None
+        p = nsa.make_problem(d["q"], d["k"], d["idx"], w.block_size, w.scale, cu, ms)
+        dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
+        nsa.set_strides(p, q=d["q"], k=d["k"], v=d["v"], o=o, dO=d["dO"], dq=dq, dk=dk, dv=dv)
+        lib = _lib.load()
+        ptr = lambda t: None if t is None else t.data_ptr()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms,
+                                out=o, lse=lse)
+                st = lib.nsa_sel_bwd_noalloc(
+                    ctypes.byref(p), ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(o), ptr(lse),
+                    ptr(d["dO"]), ptr(d["idx"]), ptr(cu), ptr(dq), ptr(dk), ptr(dv),
+                    torch.cuda.current_stream().cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        _lib.check("nsa_sel_bwd_noalloc (captured)", st)
+        for rep in range(3):
+            for x in (o, lse, dq, dk, dv):
+                x.fill_(7.0)                      # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), (o, lse, dq, dk, dv), ref):
+                assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
+        say(f"  3 replays bitwise equal to the eager call")
+    assert nsa.wait_timeouts() == 0
