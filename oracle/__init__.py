@@ -18,6 +18,10 @@ Where the method's source pages are silent the oracle takes these readings:
     future block adds nothing; an empty row gives o = 0, lse = -inf, dq = 0;
   * scale defaults to 1/sqrt(D); lse is natural-log and includes the scale;
   * an optional sliding window W (keys t - W < j <= t), a mask on keys only;
+  * dense problems may have Tk >= T keys (k/v [B, Hkv, Tk, D]): the queries
+    are the last T key positions (bottom-right causal alignment, one of the
+    backward flavours page 3 lists), query t at position t + Tk - T, which
+    replaces t in the causal and window limits;
   * an optional attention sink (page 3 names a dSink backward step, nothing
     more): a per-head logit, no scale, in every row's softmax denominator
     with no value; lse includes it, dq/dk/dv keep their formulas with that
@@ -60,13 +64,13 @@ def _load():
     ip = ctypes.POINTER(ctypes.c_int32)
     lp = ctypes.POINTER(ctypes.c_int64)
     i, d, i64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
-    shape = [i, i, i, i, i, i, i, d, dp, i]
+    shape = [i, i, i, i, i, i, i, d, dp, i, i]
     lib.nsa_oracle_fwd_rows.argtypes = shape + [dp, dp, dp, ip, i64, lp, dp, dp]
     lib.nsa_oracle_bwd_rows.argtypes = shape + [dp, dp, dp, dp, ip, i64, lp, dp, dp, dp]
     lib.nsa_oracle_dkdv_keys.argtypes = shape + [dp, dp, dp, dp, ip, dp, dp, i64, lp, dp, dp]
-    lib.nsa_oracle_invert.argtypes = [i, i, i, i, i, i, ip, ip, ip, i64]
+    lib.nsa_oracle_invert.argtypes = [i, i, i, i, i, i, i, ip, ip, ip, i64]
     lib.nsa_oracle_invert.restype = i64
-    lib.nsa_oracle_count_pairs.argtypes = [i, i, i, i, i, i, ip]
+    lib.nsa_oracle_count_pairs.argtypes = [i, i, i, i, i, i, i, ip]
     lib.nsa_oracle_count_pairs.restype = i64
     lib.nsa_oracle_num_threads.restype = i
     _lib = lib
@@ -93,11 +97,11 @@ def _shape(q, k, idx, block_size, scale, sink=None, window=0):
     """The C shape arguments; sink (per-head logits) is passed as a pointer
     to a float64 copy that the returned tuple keeps alive."""
     B, Hq, T, D = q.shape
-    Hkv = k.shape[1]
+    Hkv, Tk = k.shape[1], k.shape[2]
     S = idx.shape[-1]
     if scale is None:
         scale = D ** -0.5
-    if k.shape != (B, Hkv, T, D) or idx.shape != (B, Hkv, T, S) or Hq % Hkv:
+    if k.shape != (B, Hkv, Tk, D) or Tk < T or idx.shape != (B, Hkv, T, S) or Hq % Hkv:
         raise ValueError("inconsistent shapes")
     sk = None if sink is None else _f64(sink).reshape(-1)
     if sk is not None and sk.shape != (Hq,):
@@ -105,7 +109,7 @@ def _shape(q, k, idx, block_size, scale, sink=None, window=0):
     ptr = None if sk is None else _ptr(sk, ctypes.c_double)
     if window is None or window < 0:
         raise ValueError("window must be >= 0 (0: none)")
-    return _Shape((B, Hq, Hkv, T, D, S, int(block_size), float(scale), ptr, int(window)), sk)
+    return _Shape((B, Hq, Hkv, T, D, S, int(block_size), float(scale), ptr, int(window), Tk), sk)
 
 
 class _Shape(tuple):
@@ -156,7 +160,7 @@ def bwd_rows(q, k, v, dO, block_idx, block_size, rows=None, scale=None, want_dq=
 
 def dkdv_keys(q, k, v, dO, block_idx, block_size, row_lse, row_delta, keys=None, scale=None,
               window=0):
-    """dk, dv of the listed flat keys ((b*Hkv + hkv)*T + j); all keys if None.
+    """dk, dv of the listed flat keys ((b*Hkv + hkv)*Tk + j); all keys if None.
     row_lse/row_delta: every row, shaped or flat [B*Hq*T]."""
     q, k, v, dO, idx = _f64(q), _f64(k), _f64(v), _f64(dO), _i32(block_idx)
     sh = _shape(q, k, idx, block_size, scale, None, window)
@@ -186,11 +190,11 @@ def fwd(q, k, v, block_idx, block_size, scale=None, sink=None, window=0):
 def bwd(q, k, v, dO, block_idx, block_size, scale=None, sink=None, window=0):
     """Dense backward: (dq, dk, dv, lse, delta); lse includes the sink if any."""
     B, Hq, T, D = np.shape(q)
-    Hkv = np.shape(k)[1]
+    Hkv, Tk = np.shape(k)[1], np.shape(k)[2]
     lse, delta, dq = bwd_rows(q, k, v, dO, block_idx, block_size, None, scale, sink=sink,
                               window=window)
     dk, dv = dkdv_keys(q, k, v, dO, block_idx, block_size, lse, delta, None, scale, window)
-    return (dq.reshape(B, Hq, T, D), dk.reshape(B, Hkv, T, D), dv.reshape(B, Hkv, T, D),
+    return (dq.reshape(B, Hq, T, D), dk.reshape(B, Hkv, Tk, D), dv.reshape(B, Hkv, Tk, D),
             lse.reshape(B, Hq, T), delta.reshape(B, Hq, T))
 
 
@@ -209,29 +213,35 @@ def dsink(sink, lse, delta, head_axis: int):
     return -(p_sink * delta).sum(axis=axes)
 
 
-def invert(block_idx, block_size, window: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+def invert(block_idx, block_size, window: int = 0, Tk: Optional[int] = None
+           ) -> Tuple[np.ndarray, np.ndarray]:
     """Brute-force block -> token lists: for block u the ascending tokens
-    t >= u*bs that list u (with a window W, only those t whose window reaches
-    a key of u: (u+1)*bs - 1 > t - W).  Returns (counts [B,Hkv,NB], tokens)
-    with the lists concatenated in (b, hkv, u) order."""
+    whose key position p = t + Tk - T is >= u*bs and that list u (with a
+    window W, only those whose window reaches a key of u: (u+1)*bs - 1 >
+    p - W).  Tk defaults to T.  Returns (counts [B,Hkv,NB], tokens) with the
+    lists concatenated in (b, hkv, u) order, NB = ceil(Tk / bs)."""
     idx = _i32(block_idx)
     B, Hkv, T, S = idx.shape
-    NB = -(-T // block_size)
+    Tk = T if Tk is None else int(Tk)
+    NB = -(-Tk // block_size)
     counts = np.zeros((B, Hkv, NB), dtype=np.int32)
     cap = max(1, B * Hkv * T * min(S, NB))
     tokens = np.zeros(cap, dtype=np.int32)
-    n = _load().nsa_oracle_invert(B, Hkv, T, S, int(block_size), int(window), _ptr(idx, ctypes.c_int32),
-                                  _ptr(counts, ctypes.c_int32), _ptr(tokens, ctypes.c_int32), cap)
+    n = _load().nsa_oracle_invert(B, Hkv, T, Tk, S, int(block_size), int(window),
+                                  _ptr(idx, ctypes.c_int32), _ptr(counts, ctypes.c_int32),
+                                  _ptr(tokens, ctypes.c_int32), cap)
     if n < 0:
         raise RuntimeError("oracle invert: capacity exceeded")
     return counts, tokens[:n].copy()
 
 
-def count_pairs(block_idx, Hq: int, block_size: int) -> int:
-    """Useful (query-head row, key) pair count N = sum over rows of |A|."""
+def count_pairs(block_idx, Hq: int, block_size: int, Tk: Optional[int] = None) -> int:
+    """Useful (query-head row, key) pair count N = sum over rows of |A|
+    (Tk keys per group, default T)."""
     idx = _i32(block_idx)
     B, Hkv, T, S = idx.shape
-    return int(_load().nsa_oracle_count_pairs(B, Hq, Hkv, T, S, int(block_size),
+    Tk = T if Tk is None else int(Tk)
+    return int(_load().nsa_oracle_count_pairs(B, Hq, Hkv, T, Tk, S, int(block_size),
                                               _ptr(idx, ctypes.c_int32)))
 
 

@@ -33,6 +33,14 @@
  * rows of head h, is -sum_rows exp(sink[h] - lse) Delta (computed in
  * oracle/__init__.py).  sink == NULL means no sink.
  *
+ * Bottom-right causal alignment (the pages list it among the backward's
+ * flavours, nothing more; the reading taken): a dense problem may have Tk >=
+ * T keys per (batch entry, KV head); the T queries are then the last T
+ * positions of the key range, query t at key position t + (Tk - T), so
+ * causality reads j <= t + (Tk - T) and the key set is capped at j < Tk
+ * (Tk = T: the usual causal mask).  Below, "t" in a key comparison means
+ * that position.
+ *
  * Optional sliding window (the pages list sliding-window masks among the
  * backward's flavours; the reading taken): window W >= 1 further limits A to
  * the keys j with t - W < j <= t (W = 0: no limit).  It is a mask on the
@@ -40,7 +48,7 @@
  * unchanged.
  *
  * Layout (dense, contiguous, row-major): q, o, dO, dq [B][Hq][T][D];
- * k, v, dk, dv [B][Hkv][T][D]; block_idx [B][Hkv][T][S] int32; lse, delta
+ * k, v, dk, dv [B][Hkv][Tk][D]; block_idx [B][Hkv][T][S] int32; lse, delta
  * [B][Hq][T].  Packed variable-length batches are handled by the Python side
  * as one dense B=1 call per sequence (no key crosses a sequence boundary).
  *
@@ -61,9 +69,13 @@ typedef struct {
     double scale;
     const double* sink; /* [Hq] or NULL */
     int window;         /* 0: none */
+    int Tk;             /* keys per (batch entry, KV head), >= T */
 } shape_t;
 
-static int n_blocks(const shape_t* sh) { return (sh->T + sh->bs - 1) / sh->bs; }
+/* Key position of query t (bottom-right alignment). */
+static int kpos(const shape_t* sh, int t) { return t + (sh->Tk - sh->T); }
+
+static int n_blocks(const shape_t* sh) { return (sh->Tk + sh->bs - 1) / sh->bs; }
 
 static const int32_t* idx_row(const shape_t* sh, const int32_t* idx, int b, int hkv, int t) {
     return idx + (((int64_t)b * sh->Hkv + hkv) * sh->T + t) * sh->S;
@@ -74,7 +86,7 @@ static const double* qrow(const shape_t* sh, const double* x, int b, int h, int 
 }
 
 static const double* krow(const shape_t* sh, const double* x, int b, int hkv, int j) {
-    return x + (((int64_t)b * sh->Hkv + hkv) * sh->T + j) * sh->D;
+    return x + (((int64_t)b * sh->Hkv + hkv) * sh->Tk + j) * sh->D;
 }
 
 static double dot(const double* a, const double* b, int D) {
@@ -93,11 +105,11 @@ static int row_lists_block(const int32_t* row, int S, int u) {
 
 /* Ascending list of the keys in A(b,h,t); returns its size. */
 static int selected_keys(const shape_t* sh, const int32_t* row, int t, int* keys) {
-    int NB = n_blocks(sh), n = 0;
+    int NB = n_blocks(sh), n = 0, tp = kpos(sh, t);
     for (int u = 0; u < NB; ++u) {
         if (!row_lists_block(row, sh->S, u)) continue;
-        for (int j = u * sh->bs; j < (u + 1) * sh->bs && j < sh->T && j <= t; ++j)
-            if (sh->window <= 0 || j > t - sh->window) keys[n++] = j;
+        for (int j = u * sh->bs; j < (u + 1) * sh->bs && j < sh->Tk && j <= tp; ++j)
+            if (sh->window <= 0 || j > tp - sh->window) keys[n++] = j;
     }
     return n;
 }
@@ -175,8 +187,9 @@ static void dkdv_key(const shape_t* sh, const double* q, const double* k, const 
     const double* kj = krow(sh, k, b, hkv, j);
     const double* vj = krow(sh, v, b, hkv, j);
     for (int d = 0; d < D; ++d) dk_out[d] = dv_out[d] = 0.0;
-    for (int t = j; t < sh->T; ++t) {
-        if (sh->window > 0 && t >= j + sh->window) break;  /* key j left row t's window */
+    int t0 = j - (sh->Tk - sh->T);  /* the first query whose position reaches j */
+    for (int t = t0 < 0 ? 0 : t0; t < sh->T; ++t) {
+        if (sh->window > 0 && kpos(sh, t) >= j + sh->window) break;  /* key j left row t's window */
         if (!row_lists_block(idx_row(sh, idx, b, hkv, t), sh->S, u)) continue;
         for (int g = 0; g < G; ++g) {
             int h = hkv * G + g;
@@ -195,13 +208,15 @@ static void dkdv_key(const shape_t* sh, const double* q, const double* k, const 
 
 static int shape_ok(const shape_t* sh) {
     if (sh->B < 0 || sh->T < 0 || sh->D <= 0 || sh->S <= 0 || sh->bs <= 0) return 0;
+    if (sh->Tk < sh->T) return 0;
     if (sh->Hkv <= 0 || sh->Hq <= 0 || sh->Hq % sh->Hkv) return 0;
     return 1;
 }
 
-#define SHAPE_ARGS \
-    int B, int Hq, int Hkv, int T, int D, int S, int bs, double scale, const double* sink, int window
-#define MAKE_SHAPE shape_t sh = {B, Hq, Hkv, T, D, S, bs, scale, sink, window}
+#define SHAPE_ARGS                                                                            \
+    int B, int Hq, int Hkv, int T, int D, int S, int bs, double scale, const double* sink, \
+        int window, int Tk
+#define MAKE_SHAPE shape_t sh = {B, Hq, Hkv, T, D, S, bs, scale, sink, window, Tk}
 
 int nsa_oracle_num_threads(void) {
 #ifdef _OPENMP
@@ -268,7 +283,7 @@ int nsa_oracle_bwd_rows(SHAPE_ARGS, const double* q, const double* k, const doub
     return err;
 }
 
-/* dk, dv of the listed keys (flat (b*Hkv + hkv)*T + j); keys == NULL means
+/* dk, dv of the listed keys (flat (b*Hkv + hkv)*Tk + j); keys == NULL means
  * every key.  row_lse / row_delta must hold every row [B][Hq][T] (from
  * nsa_oracle_bwd_rows over all rows).  Outputs are [n_keys][D]. */
 int nsa_oracle_dkdv_keys(SHAPE_ARGS, const double* q, const double* k, const double* v,
@@ -280,7 +295,7 @@ int nsa_oracle_dkdv_keys(SHAPE_ARGS, const double* q, const double* k, const dou
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t i = 0; i < n_keys; ++i) {
         int64_t r = keys ? keys[i] : i;
-        int j = (int)(r % T), hkv = (int)((r / T) % Hkv), b = (int)(r / ((int64_t)T * Hkv));
+        int j = (int)(r % Tk), hkv = (int)((r / Tk) % Hkv), b = (int)(r / ((int64_t)Tk * Hkv));
         dkdv_key(&sh, q, k, v, dO, idx, row_lse, row_delta, b, hkv, j, dk_out + i * D,
                  dv_out + i * D);
     }
@@ -290,7 +305,7 @@ int nsa_oracle_dkdv_keys(SHAPE_ARGS, const double* q, const double* k, const dou
 /* Full forward: o [B][Hq][T][D], lse [B][Hq][T]. */
 int nsa_oracle_fwd(SHAPE_ARGS, const double* q, const double* k, const double* v,
                    const int32_t* idx, double* o, double* lse) {
-    return nsa_oracle_fwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, window, q, k, v, idx,
+    return nsa_oracle_fwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, window, Tk, q, k, v, idx,
                                (int64_t)B * Hq * T, NULL, o, lse);
 }
 
@@ -299,33 +314,35 @@ int nsa_oracle_fwd(SHAPE_ARGS, const double* q, const double* k, const double* v
 int nsa_oracle_bwd(SHAPE_ARGS, const double* q, const double* k, const double* v,
                    const double* dO, const int32_t* idx, double* dq, double* dk, double* dv,
                    double* lse, double* delta) {
-    int rc = nsa_oracle_bwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, window, q, k, v, dO, idx,
-                                 (int64_t)B * Hq * T, NULL, lse, delta, dq);
+    int rc = nsa_oracle_bwd_rows(B, Hq, Hkv, T, D, S, bs, scale, sink, window, Tk, q, k, v, dO,
+                                 idx, (int64_t)B * Hq * T, NULL, lse, delta, dq);
     if (rc) return rc;
-    return nsa_oracle_dkdv_keys(B, Hq, Hkv, T, D, S, bs, scale, sink, window, q, k, v, dO, idx, lse, delta,
-                                (int64_t)B * Hkv * T, NULL, dk, dv);
+    return nsa_oracle_dkdv_keys(B, Hq, Hkv, T, D, S, bs, scale, sink, window, Tk, q, k, v, dO, idx,
+                                lse, delta, (int64_t)B * Hkv * Tk, NULL, dk, dv);
 }
 
 /* Block -> query inversion, brute force.  For every (b, hkv, u) in order, the
- * ascending tokens t whose key set A meets block u: t lists u and t >= u*bs
- * (a listed block that starts after t adds no key, so it is not an entry);
+ * ascending tokens t whose key set A meets block u: t lists u and its key
+ * position t + Tk - T >= u*bs (a listed block that starts after it adds no
+ * key, so it is not an entry);
  * each token appears once however often it lists u.  counts is
  * [B][Hkv][NB]; tokens receives the lists back to back in that order (its
  * capacity is cap entries).  Returns the total entry count, or -1 if cap is
  * too small. */
-int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, int window, const int32_t* idx,
-                          int32_t* counts, int32_t* tokens, int64_t cap) {
-    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL, window};
+int64_t nsa_oracle_invert(int B, int Hkv, int T, int Tk, int S, int bs, int window,
+                          const int32_t* idx, int32_t* counts, int32_t* tokens, int64_t cap) {
+    shape_t sh = {B, Hkv, Hkv, T, 1, S, bs, 1.0, NULL, window, Tk};
     int NB = n_blocks(&sh);
     int64_t n = 0;
     for (int b = 0; b < B; ++b)
         for (int hkv = 0; hkv < Hkv; ++hkv)
             for (int u = 0; u < NB; ++u) {
                 int32_t c = 0;
-                for (int t = u * bs; t < T; ++t) {
+                for (int t = 0; t < T; ++t) {
+                    if (kpos(&sh, t) < u * bs) continue;
                     if (!row_lists_block(idx_row(&sh, idx, b, hkv, t), S, u)) continue;
                     /* with a window: only rows whose window reaches a key of u */
-                    if (window > 0 && (u + 1) * bs - 1 <= t - window) continue;
+                    if (window > 0 && (u + 1) * bs - 1 <= kpos(&sh, t) - window) continue;
                     if (n >= cap) return -1;
                     tokens[n++] = t;
                     ++c;
@@ -336,8 +353,9 @@ int64_t nsa_oracle_invert(int B, int Hkv, int T, int S, int bs, int window, cons
 }
 
 /* Number of useful (query-head row, key) pairs: sum over rows of |A|. */
-int64_t nsa_oracle_count_pairs(int B, int Hq, int Hkv, int T, int S, int bs, const int32_t* idx) {
-    shape_t sh = {B, Hq, Hkv, T, 1, S, bs, 1.0, NULL, 0};
+int64_t nsa_oracle_count_pairs(int B, int Hq, int Hkv, int T, int Tk, int S, int bs,
+                               const int32_t* idx) {
+    shape_t sh = {B, Hq, Hkv, T, 1, S, bs, 1.0, NULL, 0, Tk};
     if (!shape_ok(&sh)) return -1;
     int G = Hq / Hkv;
     int* keys = (int*)malloc(sizeof(int) * (size_t)S * bs);

@@ -17,17 +17,19 @@ import test_oracle_pins as pins
 import test_oracle_sink as sink_pins
 import test_oracle_subsets as subset_pins
 import test_oracle_window as window_pins
+import test_oracle_bottom_right as br_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "nsa_oracle.c")
 
 MUTANTS = {
     "dq drops scale": ("dq_out[d] += sh->scale * dS * kj[d];", "dq_out[d] += dS * kj[d];"),
     "dS sign": ("double dS = P[a] * (dP[a] - delta);", "double dS = P[a] * (dP[a] + delta);"),
-    "causal strict": ("j < sh->T && j <= t;", "j < sh->T && j < t;"),
+    "causal strict": ("j < sh->Tk && j <= tp;", "j < sh->Tk && j < tp;"),
     "block start off by one": ("for (int j = u * sh->bs; j <", "for (int j = u * sh->bs + 1; j <"),
     "dk uses dO": ("dk_out[d] += sh->scale * dS * q_r[d];", "dk_out[d] += sh->scale * dS * do_r[d];"),
     "dv uses dS": ("dv_out[d] += Pj * do_r[d];", "dv_out[d] += dS * do_r[d];"),
-    "dkdv skips diagonal": ("for (int t = j; t < sh->T; ++t)", "for (int t = j + 1; t < sh->T; ++t)"),
+    "dkdv skips diagonal": ("for (int t = t0 < 0 ? 0 : t0; t < sh->T; ++t)",
+                            "for (int t = (t0 < 0 ? 0 : t0) + 1; t < sh->T; ++t)"),
     "delta drops P": ("delta += P[a] * dP[a];", "delta += dP[a];"),
     "head map transposed": ("int G = sh->Hq / sh->Hkv, hkv = h / G, D = sh->D;\n    const double* K",
                             "int G = sh->Hq / sh->Hkv, hkv = h % sh->Hkv, D = sh->D;\n    const double* K"),
@@ -37,11 +39,15 @@ MUTANTS = {
                  "const double* V = krow(sh, k, b, hkv, 0);\n    int n = selected_keys"),
     "sink left out of the sum": ("double sum = sh->sink ? exp(sk - m) : 0.0;", "double sum = 0.0;"),
     "sink ignored on empty rows": ("if (n == 0) return sk;", "if (n == 0) return -INFINITY;"),
-    "window off by one": ("j > t - sh->window) keys[n++] = j;", "j >= t - sh->window) keys[n++] = j;"),
-    "dkdv ignores the window": ("if (sh->window > 0 && t >= j + sh->window) break;", ";"),
+    "window off by one": ("j > tp - sh->window) keys[n++] = j;", "j >= tp - sh->window) keys[n++] = j;"),
+    "dkdv ignores the window": ("if (sh->window > 0 && kpos(sh, t) >= j + sh->window) break;", ";"),
     # the subset calls: a listed row / key computed as if the list were absent
     "row list ignored": ("int64_t r = rows ? rows[i] : i;", "int64_t r = i;"),
     "key list ignored": ("int64_t r = keys ? keys[i] : i;", "int64_t r = i;"),
+    "bottom-right offset dropped": ("static int kpos(const shape_t* sh, int t) { return t + (sh->Tk - sh->T); }",
+                                    "static int kpos(const shape_t* sh, int t) { return t; }"),
+    "dkdv rows start at the key": ("int t0 = j - (sh->Tk - sh->T);", "int t0 = j;"),
+    "keys capped at the query count": ("j < sh->Tk && j <= tp;", "j < sh->T && j <= tp;"),
 }
 
 
@@ -76,6 +82,8 @@ CHECKS = [
     lambda: window_pins.test_window_dense_autograd(41, 2, 4, 2, 40, 8, 4, 5, 7),
     lambda: subset_pins.test_row_and_key_subsets_equal_full_call(),
     lambda: subset_pins.test_packed_batch_equals_block_diagonal_autograd(subset_pins.PACKED[0]),
+    lambda: br_pins.test_bottom_right_dense_autograd(*br_pins.BR_CASES[0]),
+    lambda: br_pins.test_bottom_right_finite_differences(),
 ]
 
 
