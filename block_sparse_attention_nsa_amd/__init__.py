@@ -77,7 +77,9 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, block_idx: torch.Tensor, bloc
                  scale: Optional[float] = None, cu_seqlens: Optional[torch.Tensor] = None,
                  max_seqlen: Optional[int] = None, window: int = 0) -> _lib.Problem:
     """The nsa_sel_problem describing these tensors (contiguous layouts until
-    set_strides records the actual strides)."""
+    set_strides records the actual strides).  Dense k may hold more tokens
+    than q (Tk >= T): the queries are then the last T key positions
+    (bottom-right causal alignment)."""
     if q.dtype not in _DTYPES:
         raise TypeError(f"q dtype {q.dtype} is not float32 or bfloat16")
     p = _lib.Problem()
@@ -87,6 +89,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, block_idx: torch.Tensor, bloc
         p.layout = _lib.NSA_DENSE
         p.B, p.Hq, p.T, p.D = q.shape
         p.Hkv = k.shape[1]
+        p.Tk = k.shape[2]
         p.S = block_idx.shape[-1]
         p.n_seqs, p.max_seqlen = 0, 0
     else:
@@ -117,7 +120,7 @@ def _check_tensors(q, k, v, block_idx, cu_seqlens, p: _lib.Problem):
     if block_idx.dtype != torch.int32 or not block_idx.is_contiguous():
         raise TypeError("block_idx must be a contiguous int32 tensor")
     dense = cu_seqlens is None
-    want_k = (p.B, p.Hkv, p.T, p.D) if dense else (p.T, p.Hkv, p.D)
+    want_k = (p.B, p.Hkv, p.Tk, p.D) if dense else (p.T, p.Hkv, p.D)
     want_i = (p.B, p.Hkv, p.T, p.S) if dense else (p.Hkv, p.T, p.S)
     if tuple(k.shape) != want_k or tuple(block_idx.shape) != want_i:
         raise ValueError(f"shape mismatch: k {tuple(k.shape)} (want {want_k}), "
@@ -302,8 +305,8 @@ def nsa_sel_invert(q, k, block_idx, block_size, cu_seqlens=None, max_seqlen=None
     lib = _lib.load()
     cap = int(lib.nsa_sel_invert_tokens_capacity(p))
     Z = p.B if cu_seqlens is None else p.n_seqs
-    tmax = p.T if cu_seqlens is None else p.max_seqlen
-    nb = -(-tmax // p.block_size)
+    kmax = (p.Tk or p.T) if cu_seqlens is None else p.max_seqlen  # keys: blocks are key blocks
+    nb = -(-kmax // p.block_size)
     offsets = torch.empty((Z, p.Hkv, nb + 1), dtype=torch.int32, device=block_idx.device)
     tokens = torch.empty(max(cap, 1), dtype=torch.int32, device=block_idx.device)
     nbytes = bwd_workspace_bytes(p)

@@ -61,6 +61,7 @@ class Problem(ctypes.Structure):
         ("stride_dq", ctypes.c_int64 * 3),
         ("stride_dk", ctypes.c_int64 * 3),
         ("stride_dv", ctypes.c_int64 * 3),
+        ("Tk", ctypes.c_int32),
     ]
 
 

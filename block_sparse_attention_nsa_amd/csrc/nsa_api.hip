@@ -51,6 +51,12 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     if (!isfinite(p->scale)) return fail(NSA_ERR_INVALID_ARG, "scale is not finite");
     if (p->window < 0) return fail(NSA_ERR_INVALID_ARG, "window=%d is negative (0: none)", p->window);
     int Tmax = p->T, Z = p->B;
+    // Keys per (z, hkv): dense problems may have more keys than queries.
+    if (p->Tk < 0) return fail(NSA_ERR_INVALID_ARG, "Tk=%d must be >= 0 (0: T)", p->Tk);
+    if (packed && p->Tk != 0 && p->Tk != p->T)
+        return fail(NSA_ERR_INVALID_ARG, "packed inputs need Tk = 0 or T (got %d)", p->Tk);
+    const int Tk = p->Tk == 0 ? p->T : p->Tk;
+    if (!packed && Tk < p->T) return fail(NSA_ERR_INVALID_ARG, "Tk=%d is below T=%d", Tk, p->T);
     if (packed) {
         if (p->B != 1) return fail(NSA_ERR_INVALID_ARG, "packed inputs need B == 1 (got %d)", p->B);
         if (p->n_seqs < 0) return fail(NSA_ERR_INVALID_ARG, "n_seqs=%d must be >= 0", p->n_seqs);
@@ -71,13 +77,18 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
         if (p->D != 16 && p->D != 32 && p->D != 64 && p->D != 128)
             return fail(NSA_ERR_UNSUPPORTED, "f32 needs D in {16, 32, 64, 128} (got %d)", p->D);
     }
-    const int64_t NBmax = ((int64_t)Tmax + p->block_size - 1) / p->block_size;
+    // Blocks of the keys (the queries' positions end where the keys end).
+    const int64_t Kmax = packed ? Tmax : Tk;
+    const int64_t NBmax = (Kmax + p->block_size - 1) / p->block_size;
     if (NBmax > 8192) return fail(NSA_ERR_UNSUPPORTED, "ceil(max length / block_size) = %lld exceeds 8192", (long long)NBmax);
     const int G = p->Hq / p->Hkv;
     if ((int64_t)Tmax * G > (1ll << 30)) return fail(NSA_ERR_UNSUPPORTED, "max length * G exceeds 2^30 rows");
     if ((int64_t)p->Hq * p->T * p->D >= (1ll << 31))
         return fail(NSA_ERR_UNSUPPORTED, "Hq * T * D = %lld elements per batch entry exceeds 2^31 - 1",
                     (long long)p->Hq * p->T * p->D);
+    if ((int64_t)p->Hkv * Tk * p->D >= (1ll << 31))
+        return fail(NSA_ERR_UNSUPPORTED, "Hkv * Tk * D = %lld elements per batch entry exceeds 2^31 - 1",
+                    (long long)p->Hkv * Tk * p->D);
     const int64_t ZH = (int64_t)Z * p->Hkv;
     if (ZH > 8192) return fail(NSA_ERR_UNSUPPORTED, "(batch or sequences) * Hkv = %lld exceeds 8192", (long long)ZH);
     const int64_t idx_rows = (int64_t)p->B * p->Hkv * p->T;
@@ -91,15 +102,15 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
         return fail(NSA_ERR_INVALID_ARG, "strided=%d is not 0 or 1", p->strided);
 
     nsa::Problem& d = hp.dev;
-    d.B = p->B; d.T = p->T; d.Hq = p->Hq; d.Hkv = p->Hkv; d.G = G; d.D = p->D; d.S = p->S;
+    d.B = p->B; d.T = p->T; d.Tk = Tk; d.Hq = p->Hq; d.Hkv = p->Hkv; d.G = G; d.D = p->D; d.S = p->S;
     d.bs = p->block_size; d.Z = Z; d.packed = packed ? 1 : 0; d.Tmax = Tmax; d.NBmax = (int)NBmax;
     d.Smin = (int)Smin; d.scale = p->scale; d.scale_log2 = p->scale * nsa::kLog2e; d.cu = nullptr;
     d.sink = nullptr;
     d.window = p->window;
     // Element strides (batch entry, head, token) of the eight tensors.
     {
-        const int64_t D = p->D, T = p->T;
-        auto dflt = [&](int64_t H) {
+        const int64_t D = p->D;
+        auto dflt = [&](int64_t H, int64_t T) {
             // (32-bit head / token strides: check_qk bounds them before any use)
             return packed ? nsa::TLayout{0, (int32_t)D, (int32_t)(H * D)}
                           : nsa::TLayout{H * T * D, (int32_t)(T * D), (int32_t)D};
@@ -114,14 +125,14 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
                                  p->stride_do, p->stride_dq, p->stride_dk, p->stride_dv};
         for (int i = 0; i < 8; ++i)
             for (int j = 0; j < 3; ++j) hp.given[i][j] = st ? src[i][j] : 0;
-        d.lq = st ? given(p->stride_q) : dflt(p->Hq);
-        d.lo = st ? given(p->stride_o) : dflt(p->Hq);
-        d.ldo = st ? given(p->stride_do) : dflt(p->Hq);
-        d.ldq = st ? given(p->stride_dq) : dflt(p->Hq);
-        d.lk = st ? given(p->stride_k) : dflt(p->Hkv);
-        d.lv = st ? given(p->stride_v) : dflt(p->Hkv);
-        d.ldk = st ? given(p->stride_dk) : dflt(p->Hkv);
-        d.ldv = st ? given(p->stride_dv) : dflt(p->Hkv);
+        d.lq = st ? given(p->stride_q) : dflt(p->Hq, p->T);
+        d.lo = st ? given(p->stride_o) : dflt(p->Hq, p->T);
+        d.ldo = st ? given(p->stride_do) : dflt(p->Hq, p->T);
+        d.ldq = st ? given(p->stride_dq) : dflt(p->Hq, p->T);
+        d.lk = st ? given(p->stride_k) : dflt(p->Hkv, Tk);
+        d.lv = st ? given(p->stride_v) : dflt(p->Hkv, Tk);
+        d.ldk = st ? given(p->stride_dk) : dflt(p->Hkv, Tk);
+        d.ldv = st ? given(p->stride_dv) : dflt(p->Hkv, Tk);
     }
     hp.dtype = p->dtype;
     hp.ZH = (int)ZH;
@@ -146,8 +157,10 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     hp.items_ub = ZH * NBmax + (rows_ub + hp.CR - 1) / hp.CR;
     if (hp.items_ub > (1ll << 31) - 1) return fail(NSA_ERR_UNSUPPORTED, "too many dK/dV work items");
     hp.pslots = (p->dtype == NSA_BF16 && (int64_t)Tmax * G > hp.CR) ? hp.items_ub : 0;
+    // (Block pairs assume a block's list starts at its own first token:
+    // queries and keys aligned, Tk = T.)
     hp.pair_possible = p->dtype == NSA_BF16 && hp.pslots == 0 && p->block_size <= 64 && p->window == 0 &&
-                       (int64_t)p->S * p->block_size >= Tmax && ZH > 0 && NBmax > 0;
+                       (int64_t)p->S * p->block_size >= Tmax && ZH > 0 && NBmax > 0 && Tk == p->T;
     // dS hand-off: the dQ kernel's tiles hold 16 heads of one token, or all
     // heads of 2 or 4 tokens; one 32-bit offset spans a (z, hkv) region of dS.
     hp.ds_handoff = p->dtype == NSA_BF16 && (G % 16 == 0 || G == 8 || G == 4) && p->window == 0 &&
@@ -236,7 +249,7 @@ nsa_status check_qk(const nsa::HostProblem& hp, Which w, const void* ptr) {
     const nsa::Problem& d = hp.dev;
     const char* name = kWhichName[w];
     const bool qlike = w == kQ || w == kO || w == kDO || w == kDQ;
-    const int64_t nb = d.packed ? 1 : d.B, nh = qlike ? d.Hq : d.Hkv, nt = d.T, D = d.D;
+    const int64_t nb = d.packed ? 1 : d.B, nh = qlike ? d.Hq : d.Hkv, nt = qlike ? d.T : d.Tk, D = d.D;
     if (nb * nh * nt == 0) return NSA_OK;
     if (!ptr) return fail(NSA_ERR_INVALID_ARG, "%s is NULL", name);
     const bool bf16 = hp.dtype == NSA_BF16;
@@ -280,7 +293,7 @@ struct Sizes {
 };
 Sizes sizes_of(const nsa::HostProblem& hp) {
     const nsa::Problem& d = hp.dev;
-    return {(int64_t)d.B * d.Hq * d.T * d.D, (int64_t)d.B * d.Hkv * d.T * d.D,
+    return {(int64_t)d.B * d.Hq * d.T * d.D, (int64_t)d.B * d.Hkv * d.Tk * d.D,
             (int64_t)d.B * d.Hkv * d.T * d.S, (int64_t)d.B * d.Hq * d.T};
 }
 

@@ -140,25 +140,27 @@ hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, fl
 // of the row is written before it is read, so `last` needs no clearing
 // between rows; plain LDS writes and reads replace atomics, and distinct
 // blocks never contend for one word.
-__device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int t, int W) {
-    return u >= 0 && u < NBz && u * bs <= t && (W <= 0 || (u + 1) * bs > t - W + 1);
+// (tp: the row's key position, token + qoff)
+__device__ __forceinline__ bool entry_ok(int u, int NBz, int bs, int tp, int W) {
+    return u >= 0 && u < NBz && u * bs <= tp && (W <= 0 || (u + 1) * bs > tp - W + 1);
 }
 
-// Calls f(u, si) once per distinct valid entry u of row (S entries, token
-// t), from the lane holding the representative entry si (lane si % 64).
+// Calls f(u, si) once per distinct valid entry u of row (S entries, key
+// position tp), from the lane holding the representative entry si (lane si
+// % 64).
 // Rows of up to 65535 entries (positions fit 16 bits).
 template <typename F>
-__device__ __forceinline__ void for_each_distinct(const int* row, int S, int NBz, int bs, int t,
+__device__ __forceinline__ void for_each_distinct(const int* row, int S, int NBz, int bs, int tp,
                                                   int W, int lane, volatile uint16_t* last, F&& f) {
     for (int s0 = 0; s0 < S; s0 += 64) {
         const int si = s0 + lane;
         const int u = si < S ? row[si] : -1;
-        if (entry_ok(u, NBz, bs, t, W)) last[u] = (uint16_t)si;
+        if (entry_ok(u, NBz, bs, tp, W)) last[u] = (uint16_t)si;
     }
     for (int s0 = 0; s0 < S; s0 += 64) {
         const int si = s0 + lane;
         const int u = si < S ? row[si] : -1;
-        if (entry_ok(u, NBz, bs, t, W) && last[u] == (uint16_t)si) f(u, si);
+        if (entry_ok(u, NBz, bs, tp, W) && last[u] == (uint16_t)si) f(u, si);
     }
 }
 
@@ -192,7 +194,7 @@ __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, con
     int* rows = sm + p.NBmax + kInvWaves * NBH;              // [kRowStage]
     const int z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
-    const int NBz = (s.len + p.bs - 1) / p.bs;
+    const int NBz = (s.klen + p.bs - 1) / p.bs;
     for (int u = threadIdx.x; u < p.NBmax; u += blockDim.x) hist[u] = 0;
     const int t_end = min(c * CT + CT, s.len);
     const int per = max(1, kRowStage / p.S);
@@ -202,7 +204,7 @@ __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, con
         stage_rows(p, s, idx, hkv, tb, te, rows);
         __syncthreads();
         for (int t = tb + w; t < te; t += kInvWaves)
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t + s.qoff, p.window, lane, last,
                               [&](int u, int) { atomicAdd(&hist[u], 1); });
     }
     __syncthreads();
@@ -346,13 +348,15 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(Problem p, int C, int CR,
     __syncthreads();
     for (int u = threadIdx.x; u <= NB; u += blockDim.x) off[u] = u < NB ? vals[u] : total;
     __syncthreads();
-    const int len = seq_of(p, zh / p.Hkv).len;
+    const Seq sq = seq_of(p, zh / p.Hkv);
+    const int len = sq.klen;  // keys: every block inside them gets an item below
     // Whole causal prefixes: a row's listed blocks can only be blocks at or
     // before its own, so every row lists all of them exactly when every block
-    // u inside the sequence is listed by all len - u bs tokens from u bs on.
+    // u of the keys is listed by every token whose key position t + qoff
+    // reaches it: len - u bs tokens from u bs on when queries and keys align.
     int short_list = 0;
     for (int u = threadIdx.x; u < NB; u += blockDim.x)
-        if (u * p.bs < len && off[u + 1] - off[u] != len - u * p.bs) short_list = 1;
+        if (u * p.bs < len && off[u + 1] - off[u] != sq.len - max(0, u * p.bs - sq.qoff)) short_list = 1;
     const int zh_full = !__syncthreads_or(short_list);
     for (int u = threadIdx.x; u < NB; u += blockDim.x) {
         const int rows = (off[u + 1] - off[u]) * p.G;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
     const int c = blockIdx.x, zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
     if (c * CT >= s.len) return;  // chunk past a short sequence's end
-    const int NBz = (s.len + p.bs - 1) / p.bs;
+    const int NBz = (s.klen + p.bs - 1) / p.bs;
     const int* cp = chunk_pos + (int64_t)zh * NB * C;
     for (int u = threadIdx.x; u < NB; u += blockDim.x) cursor[u] = cp[(int64_t)u * C + c];
     int* out = tokens + region_base(p, s, hkv);
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
         const int n = te - tb, q = n / NW, rm = n % NW;
         const int r0 = tb + w * q + min(w, rm), r1 = r0 + q + (w < rm ? 1 : 0);
         for (int t = r0; t < r1; ++t)
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t + s.qoff, p.window, lane, last,
                               [&](int u, int) { hw[u] += 1; });
         __syncthreads();
         for (int u = threadIdx.x; u < NB; u += blockDim.x) {
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(512) void inv_fill_kernel(Problem p, int CT, int C,
             int* pm = posmap ? posmap + (s.i_base + (int64_t)hkv * p.T + t) * p.S : nullptr;
             if (pm)
                 for (int si = lane; si < p.S; si += 64) pm[si] = -1;
-            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t, p.window, lane, last,
+            for_each_distinct(rows + (t - tb) * p.S, p.S, NBz, p.bs, t + s.qoff, p.window, lane, last,
                               [&](int u, int si) {
                                   const int pos = hw[u];
                                   hw[u] = pos + 1;
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(64 * kChkWaves) void check_idx_kernel(Problem p, co
     volatile uint16_t* last = lastbuf + w * p.NBmax;
     const int zh = blockIdx.y, z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
-    const int NBz = (s.len + p.bs - 1) / p.bs;
+    const int NBz = (s.klen + p.bs - 1) / p.bs;
     unsigned long long c[4] = {0ull, 0ull, 0ull, 0ull};
     const int t0 = blockIdx.x * kChkRows, t1 = min(s.len, t0 + kChkRows);
     for (int t = t0 + w; t < t1; t += kChkWaves) {
@@ -620,7 +624,7 @@ __global__ __launch_bounds__(64 * kChkWaves) void check_idx_kernel(Problem p, co
                 ++c[1];
             } else {
                 ++inr;
-                if ((int64_t)u * p.bs > t) ++c[2];
+                if ((int64_t)u * p.bs > t + s.qoff) ++c[2];
                 last[u] = (uint16_t)si;
             }
         }

@@ -33,10 +33,11 @@ struct TLayout {
 // Everything a kernel needs to know about the problem (passed by value).
 struct Problem {
     int B, T, Hq, Hkv, G, D, S, bs;
+    int Tk;       // dense: keys per (batch entry, KV head), >= T (queries are the last T positions)
     int Z;        // batch entries (dense) or sequences (packed)
     int packed;   // 1 when cu is a cumulative-length array
-    int Tmax;     // longest sequence (T for dense)
-    int NBmax;    // ceil(Tmax / bs)
+    int Tmax;     // longest sequence of queries (T for dense)
+    int NBmax;    // key blocks of the longest sequence (dense: ceil(Tk / bs))
     int Smin;     // min(S, NBmax): distinct usable entries per row, at most
     float scale;  // softmax scale
     float scale_log2;  // scale * log2(e): scores in the base-2 domain
@@ -53,7 +54,9 @@ struct Problem {
 // stays inside the T-token arrays whatever cu holds.  block_idx rows and
 // lse / delta entries are counted in their own (contiguous) arrays.
 struct Seq {
-    int start, len;
+    int start, len;    // first token (packed) and number of queries
+    int klen;          // keys (dense: Tk; packed: len)
+    int qoff;          // key position of query 0: query t is at t + qoff (klen - len)
     int zb;            // batch entry of the dense layouts (0 when packed)
     int64_t i_base;    // block_idx row of (hkv, t) = i_base + hkv*T + t
     int64_t l_base;    // lse/delta index of (h, t)  = l_base + h*T + t
@@ -67,12 +70,16 @@ __device__ __forceinline__ Seq seq_of(const Problem& p, int z) {
         b = min(max(b, a), p.T);
         s.start = a;
         s.len = min(b - a, p.Tmax);
+        s.klen = s.len;
+        s.qoff = 0;
         s.zb = 0;
         s.i_base = a;
         s.l_base = a;
     } else {
         s.start = 0;
         s.len = p.T;
+        s.klen = p.Tk;
+        s.qoff = p.Tk - p.T;
         s.zb = z;
         s.i_base = (int64_t)z * p.Hkv * p.T;
         s.l_base = (int64_t)z * p.Hq * p.T;

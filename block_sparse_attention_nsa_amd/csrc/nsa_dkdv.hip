@@ -197,7 +197,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
     }
     const int z = it.zh / p.Hkv, hkv = it.zh % p.Hkv, u = it.u;
     const Seq s = seq_of(p, z);
-    if (PAIRED && u * BS >= s.len) return;  // pair past a short sequence's end
+    if (PAIRED && u * BS >= s.klen) return;  // pair past a short sequence's end
     const int lu = PAIRED ? 2 * u : u;      // the list walked: block lu's
     const int* off = offsets + (int64_t)it.zh * (NB + 1);
     // Paired (whole prefixes): block lu's list is the tokens lu bs .. len - 1.
@@ -221,7 +221,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
-            const bool in = 16 * kt < BK && key < s.len;
+            const bool in = 16 * kt < BK && key < s.klen;
             const uint16_t* kr = k + row_off(p.lk, s, hkv, in ? key : 0) + 8 * g;
             const uint16_t* vr = v + row_off(p.lv, s, hkv, in ? key : 0) + 8 * g;
 #pragma unroll
@@ -288,8 +288,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     const int x0 = f0 + 16 * rt + 4 * g;
-                    const int tv[4] = {x0 >= 0 ? tt[rt].x : -1, x0 + 1 >= 0 ? tt[rt].y : -1,
-                                       x0 + 2 >= 0 ? tt[rt].z : -1, x0 + 3 >= 0 ? tt[rt].w : -1};
+                    // (key positions of the rows' tokens; -1: no row)
+                    const int tv[4] = {x0 >= 0 ? tt[rt].x + s.qoff : -1, x0 + 1 >= 0 ? tt[rt].y + s.qoff : -1,
+                                       x0 + 2 >= 0 ? tt[rt].z + s.qoff : -1, x0 + 3 >= 0 ? tt[rt].w + s.qoff : -1};
                     const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
                                          -ll[rt].w * kLog2e};
                     const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
@@ -555,7 +556,7 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int key = kbase + 16 * kt + r;
-            if (16 * kt >= BK || key >= s.len) continue;
+            if (16 * kt >= BK || key >= s.klen) continue;
             uint16_t* dkr = dk + row_off(p.ldk, s, hkv, key) + 4 * g;
             uint16_t* dvr = dv + row_off(p.ldv, s, hkv, key) + 4 * g;
 #pragma unroll
@@ -607,7 +608,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
     const int zh = bu / NB, u = bu % NB;
     const int z = zh / p.Hkv, hkv = zh % p.Hkv;
     const Seq s = seq_of(p, z);
-    if (u * BK >= s.len) return;
+    if (u * BK >= s.klen) return;
     const int* ip = item_pre + (int64_t)zh * (NB + 1);
     const int n = ip[u + 1] - ip[u];
     if (n == 1) return;
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(
         const int x = pos[q] % E4;
         const int ln = x % 64, tile = x / (64 * ND);
         key[q] = u * BK + 16 * tile + (ln & 15);
-        on[q] = pos[q] < e_end && 16 * tile < BK && key[q] < s.len;
+        on[q] = pos[q] < e_end && 16 * tile < BK && key[q] < s.klen;
     }
     float4 acc[kP];
 #pragma unroll

@@ -19,22 +19,25 @@ __device__ __forceinline__ int seq_of_token(const Problem& p, int tok) {
 
 // Row r of the q-like tensor -> (z, h, t).  Dense rows are (b, h, t); packed
 // rows are (token, h).
+// Flat row r of a [B, H, T, ..] (dense; T = Tn) or [Ttot, H, ..] (packed)
+// tensor -> (entry, head, token).
 __device__ __forceinline__ void decode_qrow(const Problem& p, int64_t r, int H, int& z, int& h,
-                                            int& t) {
+                                            int& t, int Tn) {
     if (p.packed) {
         int tok = (int)(r / H);
         h = (int)(r % H);
         z = seq_of_token(p, tok);
         t = tok - min(max(p.cu[z], 0), p.T);
     } else {
-        t = (int)(r % p.T);
-        h = (int)((r / p.T) % H);
-        z = (int)(r / ((int64_t)p.T * H));
+        t = (int)(r % Tn);
+        h = (int)((r / Tn) % H);
+        z = (int)(r / ((int64_t)Tn * H));
     }
 }
 
-__device__ __forceinline__ bool slot_valid(const int* row, int si, int u, int NBz, int bs, int t) {
-    if (u < 0 || u >= NBz || u * bs > t) return false;
+// (tp: the query's key position)
+__device__ __forceinline__ bool slot_valid(const int* row, int si, int u, int NBz, int bs, int tp) {
+    if (u < 0 || u >= NBz || u * bs > tp) return false;
     for (int s2 = 0; s2 < si; ++s2)
         if (row[s2] == u) return false;
     return true;
@@ -50,10 +53,10 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
     int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= nrows) return;
     int z, h, t;
-    decode_qrow(p, r, p.Hq, z, h, t);
+    decode_qrow(p, r, p.Hq, z, h, t, p.T);
     const Seq s = seq_of(p, z);
     if (t < 0 || t >= s.len) return;
-    const int hkv = h / p.G, NBz = (s.len + p.bs - 1) / p.bs;
+    const int hkv = h / p.G, NBz = (s.klen + p.bs - 1) / p.bs, tp = t + s.qoff;
     const int* row = idx_row(p, s, idx, hkv, t);
     float qv[D], acc[D];
     const float* qr = q + row_off(p.lq, s, h, t);
@@ -64,10 +67,10 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(Problem p, const float* __
     float m = -__builtin_huge_valf(), l = 0.f;
     for (int si = 0; si < p.S; ++si) {
         const int u = row[si];
-        if (!slot_valid(row, si, u, NBz, p.bs, t)) continue;
-        const int j1 = min((u + 1) * p.bs, t + 1);
-        // Sliding window: keys t - window < j only.
-        const int j0 = p.window > 0 ? max(u * p.bs, t - p.window + 1) : u * p.bs;
+        if (!slot_valid(row, si, u, NBz, p.bs, tp)) continue;
+        const int j1 = min((u + 1) * p.bs, tp + 1);
+        // Sliding window: keys tp - window < j only.
+        const int j0 = p.window > 0 ? max(u * p.bs, tp - p.window + 1) : u * p.bs;
         for (int j = j0; j < j1; ++j) {
             const float* kr = k + row_off(p.lk, s, hkv, j);
             const float* vr = v + row_off(p.lv, s, hkv, j);
@@ -105,10 +108,10 @@ __global__ __launch_bounds__(128) void dq_f32_kernel(Problem p, const float* __r
     int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= nrows) return;
     int z, h, t;
-    decode_qrow(p, r, p.Hq, z, h, t);
+    decode_qrow(p, r, p.Hq, z, h, t, p.T);
     const Seq s = seq_of(p, z);
     if (t < 0 || t >= s.len) return;
-    const int hkv = h / p.G, NBz = (s.len + p.bs - 1) / p.bs;
+    const int hkv = h / p.G, NBz = (s.klen + p.bs - 1) / p.bs, tp = t + s.qoff;
     const int* row = idx_row(p, s, idx, hkv, t);
     const int64_t lo = l_off(p, s, h, t);
     const float* qr = q + row_off(p.lq, s, h, t);
@@ -122,10 +125,10 @@ __global__ __launch_bounds__(128) void dq_f32_kernel(Problem p, const float* __r
     const float lse2 = lse[lo] * kLog2e, dl = delta[lo];
     for (int si = 0; si < p.S; ++si) {
         const int u = row[si];
-        if (!slot_valid(row, si, u, NBz, p.bs, t)) continue;
-        const int j1 = min((u + 1) * p.bs, t + 1);
-        // Sliding window: keys t - window < j only.
-        const int j0 = p.window > 0 ? max(u * p.bs, t - p.window + 1) : u * p.bs;
+        if (!slot_valid(row, si, u, NBz, p.bs, tp)) continue;
+        const int j1 = min((u + 1) * p.bs, tp + 1);
+        // Sliding window: keys tp - window < j only.
+        const int j0 = p.window > 0 ? max(u * p.bs, tp - p.window + 1) : u * p.bs;
         for (int j = j0; j < j1; ++j) {
             const float* kr = k + row_off(p.lk, s, hkv, j);
             const float* vr = v + row_off(p.lv, s, hkv, j);
@@ -153,9 +156,9 @@ __global__ __launch_bounds__(128) void dkdv_f32_kernel(
     int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= nkeys) return;
     int z, hkv, j;
-    decode_qrow(p, r, p.Hkv, z, hkv, j);
+    decode_qrow(p, r, p.Hkv, z, hkv, j, p.Tk);
     const Seq s = seq_of(p, z);
-    if (j < 0 || j >= s.len) return;
+    if (j < 0 || j >= s.klen) return;
     const int u = j / p.bs;
     const int zh = z * p.Hkv + hkv;
     const int* off = offsets + (int64_t)zh * (p.NBmax + 1);
@@ -171,8 +174,8 @@ __global__ __launch_bounds__(128) void dkdv_f32_kernel(
         av[d] = 0.f;
     }
     for (int e = 0; e < cnt; ++e) {
-        const int t = list[e];
-        if (j > t || (p.window > 0 && t - p.window >= j)) continue;
+        const int t = list[e], tp = t + s.qoff;
+        if (j > tp || (p.window > 0 && tp - p.window >= j)) continue;
         for (int gg = 0; gg < p.G; ++gg) {
             const int h = hkv * p.G + gg;
             const int64_t lo = l_off(p, s, h, t);
@@ -235,7 +238,8 @@ hipError_t launch_dq_f32(const HostProblem& hp, const float* q, const float* k, 
 hipError_t launch_dkdv_f32(const HostProblem& hp, const float* q, const float* k, const float* v,
                            const float* dO, const float* lse, const float* delta,
                            const BwdWorkspace& ws, float* dk, float* dv, hipStream_t st) {
-    const int64_t n = (int64_t)hp.dev.B * hp.dev.Hkv * hp.dev.T;
+    // keys: [B, Hkv, Tk] (dense) or [Ttot, Hkv] (packed, Tk = T)
+    const int64_t n = (int64_t)hp.dev.B * hp.dev.Hkv * hp.dev.Tk;
     if (n == 0) return hipSuccess;
     dim3 grid((unsigned)((n + 127) / 128));
     NSA_DISPATCH_D_F32(hp.dev.D, hipLaunchKernelGGL((dkdv_f32_kernel<D>), grid, dim3(128), 0, st,

@@ -214,8 +214,9 @@ __device__ int wg_union(const Problem& p, const Seq& s, const int* __restrict__ 
         const int a = e / p.S, u = rows[e];
         // (With a sliding window, only blocks reaching into token T0 + a's
         // window: the others are masked entirely, so they are not walked.)
-        if (u >= 0 && u < NBz && u * p.bs <= T0 + a &&
-            (p.window <= 0 || (u + 1) * p.bs > T0 + a - p.window + 1))
+        const int tp = T0 + a + s.qoff;  // the token's key position
+        if (u >= 0 && u < NBz && u * p.bs <= tp &&
+            (p.window <= 0 || (u + 1) * p.bs > tp - p.window + 1))
             atomicOr(&umask[u], 1ull << a);
     }
     __syncthreads();
@@ -608,12 +609,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     const Seq s = seq_of(p, wc.z);
     if (wc.T0 >= s.len) return;
     const int n_tok = min(qg.TW, s.len - wc.T0);
-    const int t_last = wc.T0 + n_tok - 1;
-    const int NBz = (s.len + BS - 1) / BS;
+    const int t_last = wc.T0 + n_tok - 1 + s.qoff;  // key position of the last query
+    const int NBz = (s.klen + BS - 1) / BS;
+    const int qoff = s.qoff;
     using LD = KVLoad<D, NW, JK>;
     LD ld;
     ld.init(w, lane, k + head_base(p.lk, s, wc.hkv), v + head_base(p.lv, s, wc.hkv),
-            2 * p.lk.st, 2 * p.lv.st, s.len);
+            2 * p.lk.st, 2 * p.lv.st, s.klen);
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
@@ -670,8 +672,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         // No mask when every token of the tile lists the block, the slice
         // ends before the tile's first token, and all rows exist.
         const bool full = KT == JK && ((bm & tmask[i]) == tmask[i]) &&
-                          (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
-                          tr[i].valid && (!WIN || cur.j0 > tr[i].t - p.window);
+                          (cur.j0 + JK - 1 <= tr[i].t + qoff - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
+                          tr[i].valid && (!WIN || cur.j0 > tr[i].t + qoff - p.window);
         float mloc = kNegInfQ;
         if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
 #pragma unroll
@@ -682,9 +684,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
             const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
             // Key 16 kt + 4 g + e is masked past lim; compared as
             // 16 kt + e > lim - 4 g so the left side is a constant.
-            const int lim = (sel ? tr[i].t - cur.j0 : -1) - 4 * g;
+            const int lim = (sel ? tr[i].t + qoff - cur.j0 : -1) - 4 * g;
             // Sliding window: keys below t - window + 1 too (same form).
-            const int lo = WIN ? tr[i].t - p.window + 1 - cur.j0 - 4 * g : 0;
+            const int lo = WIN ? tr[i].t + qoff - p.window + 1 - cur.j0 - 4 * g : 0;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -864,12 +866,13 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     const Seq s = seq_of(p, wc.z);
     if (wc.T0 >= s.len) return;
     const int n_tok = min(qg.TW, s.len - wc.T0);
-    const int t_last = wc.T0 + n_tok - 1;
-    const int NBz = (s.len + BS - 1) / BS;
+    const int t_last = wc.T0 + n_tok - 1 + s.qoff;  // key position of the last query
+    const int NBz = (s.klen + BS - 1) / BS;
+    const int qoff = s.qoff;
     using LD = KVLoad<D, NW, JK>;
     LD ld;
     ld.init(w, lane, k + head_base(p.lk, s, wc.hkv), v + head_base(p.lv, s, wc.hkv),
-            2 * p.lk.st, 2 * p.lv.st, s.len);
+            2 * p.lk.st, 2 * p.lv.st, s.klen);
     uint32_t a_off[KD], t_off[ND];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) a_off[kk] = L::a_off(lane, kk);
@@ -910,13 +913,13 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     auto dscore = [&](int i, f32x4 (&sc)[NKT], const f32x4 (&dp)[NKT], const Job& cur, uint64_t bm,
                       bf16x8 (&dsb)[NKS]) __attribute__((always_inline)) {
         const bool full = KT == JK && ((bm & tmask[i]) == tmask[i]) &&
-                          (cur.j0 + JK - 1 <= tr[i].t - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
-                          tr[i].valid && (!WIN || cur.j0 > tr[i].t - p.window);
+                          (cur.j0 + JK - 1 <= tr[i].t + qoff - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
+                          tr[i].valid && (!WIN || cur.j0 > tr[i].t + qoff - p.window);
         if (!__builtin_amdgcn_readfirstlane((int)__all(full))) {
             const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
             // Key 16 kt + 4 g + e is masked past lim (constant left side).
-            const int lim = (sel ? tr[i].t - cur.j0 : -1) - 4 * g;
-            const int lo = WIN ? tr[i].t - p.window + 1 - cur.j0 - 4 * g : 0;
+            const int lim = (sel ? tr[i].t + qoff - cur.j0 : -1) - 4 * g;
+            const int lo = WIN ? tr[i].t + qoff - p.window + 1 - cur.j0 - 4 * g : 0;
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -1059,12 +1062,12 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
     const Seq s = seq_of(p, wc.z);
     if (wc.T0 >= s.len) return;
     const int n_tok = min(qg.TW, s.len - wc.T0);
-    const int t_last = wc.T0 + n_tok - 1;
-    const int NBz = (s.len + BS - 1) / BS;
+    const int t_last = wc.T0 + n_tok - 1 + s.qoff;  // key position of the last query
+    const int NBz = (s.klen + BS - 1) / BS;
     using LD = KVLoad<D, NW, JK, true>;
     LD ld;
     const uint16_t* kb = k + head_base(p.lk, s, wc.hkv);
-    ld.init(w, lane, kb, kb, 2 * p.lk.st, 2 * p.lk.st, s.len);
+    ld.init(w, lane, kb, kb, 2 * p.lk.st, 2 * p.lk.st, s.klen);
     uint32_t t_off[ND];
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) t_off[dt] = L::t_off(lane, dt);

@@ -115,6 +115,14 @@ typedef struct nsa_sel_problem {
     int32_t strided;
     int64_t stride_q[3], stride_k[3], stride_v[3], stride_o[3];
     int64_t stride_do[3], stride_dq[3], stride_dk[3], stride_dv[3];
+    /* Dense only: keys per (batch entry, KV head), >= T; 0 means T.  With
+     * Tk > T the T queries are the last T positions of the key range
+     * (bottom-right causal alignment, a backward flavour page 3 of the
+     * reference text lists): query t sees keys j <= t + Tk - T, block
+     * numbers in block_idx count blocks of the Tk keys, and k, v, dk, dv are
+     * [B, Hkv, Tk, D] (default strides from Tk).  Packed problems need 0 or
+     * T (queries and keys share the cumulative lengths). */
+    int32_t Tk;
 } nsa_sel_problem;
 
 typedef struct hipStream_t_opaque* nsa_stream_t; /* a hipStream_t; NULL = null stream */

@@ -283,3 +283,28 @@ def test_ds_handoff_query():
 def test_build_git_reported():
     s = _lib.load().nsa_build_git().decode()
     assert s == "unknown" or re.fullmatch(r"[0-9a-f]{4,40}(\+dirty)?", s), s
+
+
+def test_key_length_checks():
+    """Tk (keys per (batch entry, KV head)) must be 0 (= T) or >= T for dense
+    problems and 0 or T for packed ones; k-like tensors span Tk rows."""
+    lib = _lib.load()
+    ok = _prob(dtype=1, D=64, block_size=32, Hq=4, Hkv=2, T=100, S=4)
+    ok.Tk = 300
+    assert lib.nsa_sel_bwd_workspace_bytes(ok) > 0, _lib.last_error()
+    bad = _prob(dtype=1, D=64, block_size=32, Hq=4, Hkv=2, T=100, S=4)
+    bad.Tk = 99
+    assert _fwd(bad) == _lib.NSA_ERR_INVALID_ARG and "Tk" in _lib.last_error()
+    neg = _prob(dtype=1, D=64, block_size=32, Hq=4, Hkv=2, T=100, S=4)
+    neg.Tk = -1
+    assert _fwd(neg) == _lib.NSA_ERR_INVALID_ARG
+    packed = _prob(layout=1, dtype=1, D=64, block_size=32, Hq=4, Hkv=2, T=100, S=4, n_seqs=1,
+                   max_seqlen=100)
+    packed.Tk = 200
+    assert _fwd(packed, cu=FAKE) == _lib.NSA_ERR_INVALID_ARG and "Tk" in _lib.last_error()
+    packed.Tk = 100
+    assert lib.nsa_sel_bwd_workspace_bytes(packed) > 0, _lib.last_error()
+    # key blocks: 8192 blocks of keys at most, whatever the query count
+    many = _prob(dtype=1, D=64, block_size=32, Hq=4, Hkv=2, T=10, S=4)
+    many.Tk = 32 * 8192 + 1
+    assert lib.nsa_sel_bwd_workspace_bytes(many) == 0 and "8192" in _lib.last_error()

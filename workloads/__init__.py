@@ -114,8 +114,8 @@ def _block_idx(rng, recipe: str, n_heads: int, T: int, bs: int, S: int) -> np.nd
 
 @dataclasses.dataclass
 class Workload:
-    """One seeded draw.  Dense: q/dO [B,Hq,T,D], k/v [B,Hkv,T,D],
-    block_idx [B,Hkv,T,S].  Packed (cu_seqlens set): q/dO [Ttot,Hq,D],
+    """One seeded draw.  Dense: q/dO [B,Hq,T,D], k/v [B,Hkv,Tk,D] (Tk >= T;
+    the queries are the last T key positions), block_idx [B,Hkv,T,S].  Packed (cu_seqlens set): q/dO [Ttot,Hq,D],
     k/v [Ttot,Hkv,D], block_idx [Hkv,Ttot,S] with sequence-local indices."""
     name: str
     dtype: str  # "f32" or "bf16"
@@ -153,14 +153,19 @@ def _normal(rng, shape, dtype: str) -> np.ndarray:
 
 
 def make_dense(B, Hq, Hkv, T, D, S, block_size, dtype="bf16", recipe="own_random",
-               seed=0, name="dense", block_idx=None) -> Workload:
-    """Dense [B,H,T,D] draw in the order q, k, v, block_idx, dO."""
+               seed=0, name="dense", block_idx=None, Tk=None) -> Workload:
+    """Dense [B,H,T,D] draw in the order q, k, v, block_idx, dO.  With Tk > T
+    the keys are [B,Hkv,Tk,D] and the block lists are the recipe's lists of
+    the last T of Tk positions."""
     rng = np.random.default_rng(seed)
+    Tk = T if Tk is None else int(Tk)
     q = _normal(rng, (B, Hq, T, D), dtype)
-    k = _normal(rng, (B, Hkv, T, D), dtype)
-    v = _normal(rng, (B, Hkv, T, D), dtype)
+    k = _normal(rng, (B, Hkv, Tk, D), dtype)
+    v = _normal(rng, (B, Hkv, Tk, D), dtype)
     if block_idx is None:
-        idx = np.stack([_block_idx(rng, recipe, Hkv, T, block_size, S) for _ in range(B)])
+        idx = np.stack([_block_idx(rng, recipe, Hkv, Tk, block_size, S)[:, Tk - T:]
+                        for _ in range(B)])
+        idx = np.ascontiguousarray(idx)
     else:
         idx = np.ascontiguousarray(block_idx, dtype=np.int32)
     dO = _normal(rng, (B, Hq, T, D), dtype)
