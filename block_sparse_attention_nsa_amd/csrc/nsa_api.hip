@@ -163,8 +163,10 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
                        (int64_t)p->S * p->block_size >= Tmax && ZH > 0 && NBmax > 0 && Tk == p->T;
     // dS hand-off: the dQ kernel's tiles hold 16 heads of one token, or all
     // heads of 2 or 4 tokens; one 32-bit offset spans a (z, hkv) region of dS.
+    // (Lists that can cover whole key prefixes recompute dS: measured faster
+    // on a dense causal problem than moving their dS through memory.)
     hp.ds_handoff = p->dtype == NSA_BF16 && (G % 16 == 0 || G == 8 || G == 4) && p->window == 0 &&
-                    p->block_size >= 32 && p->S <= 64 && (int64_t)p->S * p->block_size < Tmax &&
+                    p->block_size >= 32 && p->S <= 64 && (int64_t)p->S * p->block_size < Kmax &&
                     (int64_t)Tmax * Smin * p->block_size * G * 2 < (1ll << 31);
     if (hp.ds_handoff && nsa::dq_ds_lds_bytes(hp) > 163840) hp.ds_handoff = false;
     if (nsa::invert_lds_bytes(hp) > 163840)

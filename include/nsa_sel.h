@@ -143,9 +143,10 @@ size_t nsa_sel_bwd_workspace_bytes(const nsa_sel_problem* p);
  * block_idx.  Runs, in order on `stream`: Delta = rowsum(dO * o); the
  * block -> query inversion; the dK/dV kernel (per key block and row chunk,
  * no atomics) and its fixed-order reduction; the dQ kernel (no atomics).
- * When the dK/dV kernel hands its dS over to dQ -- bf16, G a multiple of
- * 16, block_size >= 32, S <= 64, no window and S * block_size < the longest
- * sequence, so selections that cannot cover whole causal prefixes -- dQ is
+ * When the dK/dV kernel hands its dS over to dQ -- bf16, G = 4, 8 or a
+ * multiple of 16, block_size >= 32, S <= 64, no window and S * block_size
+ * below the longest key range, so selections that cannot cover whole causal
+ * prefixes -- dQ is
  * dq = scale dS K from that dS (2 D flops per pair) instead of a
  * recomputation of S and dP per query tile (6 D); the workspace then also
  * holds dS (bf16, block_size * G per listed (token, block) pair).  Results

@@ -46,10 +46,14 @@ def test_bottom_right_bf16(case):
 
 
 def test_bottom_right_decoding_query():
-    """One query at the end of 1024 keys (16 heads per KV head: the hand-off
-    path) and of 999 keys (4 heads: the recomputing dQ)."""
-    for Hq, Tk in ((32, 1024), (8, 999)):
-        w = _br(f"br-decode-{Hq}", 2, Hq, 2, 1, Tk, 128, 8, 64, seed=92)
+    """One query at the end of 1024 keys (16 heads per KV head, 8 blocks of 16:
+    the hand-off path) and of 999 keys (4 heads, lists that can cover the
+    whole prefix: the recomputing dQ)."""
+    for Hq, Tk, S, handoff in ((32, 1024, 8, True), (8, 999, 16, False)):
+        w = _br(f"br-decode-{Hq}", 2, Hq, 2, 1, Tk, 128, S, 64, seed=92)
+        d = to_dev(w)
+        p = nsa.make_problem(d["q"], d["k"], d["idx"], w.block_size, w.scale)
+        assert nsa.ds_handoff(p) == handoff
         _full_parity(w)
 
 
