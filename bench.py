@@ -11,7 +11,8 @@ the same process; with --workload only that one is timed.
 A step is one pass of the whole hot path over one batch of synthetic input:
 nsa_sel_fwd, then the backward's stages (Delta + block->query inversion +
 plan, the dK/dV block kernel, the dK/dV partial reduction, dQ).  Inputs are
-resident in HBM before timing.
+resident in HBM before timing.  By default the inversion runs on a second
+stream beside the forward and the reduction beside dQ (--serial: one stream).
 The metric is useful TFLOP/s: F_fwd = 4*D*N and F_bwd = 10*D*N with N the
 exact number of (query-head row, key) pairs the block lists select (counted
 here from block_idx), per step, over the wall time of K steps bracketed by
@@ -173,14 +174,51 @@ def run_workload(name, args, dev, cpu_leg: bool):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
     stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms, window=args.window)
-    names = ("fwd", "prepare", "dkdv", "dkdv_reduce", "dq") + (("dsink",) if args.sink else ())
+    serial = args.serial or args.sink
+    names = (("fwd", "prepare", "dkdv", "dkdv_reduce", "dq") + (("dsink",) if args.sink else ())
+             if serial else ("fwd", "prepare_lists", "prepare_delta", "dkdv", "dkdv_reduce", "dq"))
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
     sink = None
     if args.sink:
         sink = torch.from_numpy(np.random.default_rng(args.seed + 1).normal(0.0, 1.0, w.Hq)
                                 .astype(np.float32)).to(dev)
         dsink = torch.empty_like(sink)
 
+    def step_overlapped(evs=None):
+        # Two streams, default priority.  The inversion needs only block_idx:
+        # it runs on the side stream during the forward (after the previous
+        # step's dK/dV and dQ have read the lists it overwrites).  The dK/dV
+        # reduce and dQ read and write disjoint data: the reduce runs on the
+        # side stream beside dQ.
+        ev = (lambda i: evs[i].record()) if evs is not None else (lambda i: None)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            ev(1)
+            stages.prepare_lists()
+            ev(2)
+        ev(0)
+        nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse,
+                        window=args.window)
+        ev(3)
+        stages.prepare_delta(o, dO)
+        ev(4)
+        main.wait_stream(side)
+        stages.dkdv_blocks(dO, lse)
+        ev(5)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            ev(6)
+            stages.dkdv_reduce()
+            ev(7)
+        stages.dq_stage(dO, lse)
+        ev(8)
+        main.wait_stream(side)
+        ev(9)
+
     def step(evs=None):
+        if not serial:
+            return step_overlapped(evs)
         if evs is not None:
             evs[0].record()
         nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse, sink=sink,
@@ -207,7 +245,8 @@ def run_workload(name, args, dev, cpu_leg: bool):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    n_ev = len(names) + 1 if serial else 10
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -216,18 +255,24 @@ def run_workload(name, args, dev, cpu_leg: bool):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = {n: 0.0 for n in names}
+    # (event pairs of each stage; overlapped: the side stream's stages run
+    # beside the main stream's, so the stage times overlap)
+    pairs = ({n: (j, j + 1) for j, n in enumerate(names)} if serial else
+             {"fwd": (0, 3), "prepare_lists": (1, 2), "prepare_delta": (3, 4), "dkdv": (4, 5),
+              "dkdv_reduce": (6, 7), "dq": (5, 8)})
     for evs in events:
-        for j, n in enumerate(names):
-            stage_ms[n] += evs[j].elapsed_time(evs[j + 1])
+        for n, (a, b) in pairs.items():
+            stage_ms[n] += evs[a].elapsed_time(evs[b])
     stage_ms = {n: v / args.steps for n, v in stage_ms.items()}
     # Whole-step times from the launch stream's events (first to last).
-    per_step = sorted(evs[0].elapsed_time(evs[len(names)]) for evs in events)
+    last = len(names) if serial else 9
+    per_step = sorted(evs[0].elapsed_time(evs[last]) for evs in events)
     step_stats = {"median": round(float(np.median(per_step)), 4), "min": round(per_step[0], 4),
                   "max": round(per_step[-1], 4)}
     ms_step = wall * 1e3 / args.steps
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    bwd_ms = stage_ms["prepare"] + stage_ms["dq"] + stage_ms["dkdv"] + stage_ms["dkdv_reduce"] + \
-        stage_ms.get("dsink", 0.0)
+    # The backward's share of the step: everything after the forward.
+    bwd_ms = ms_step - stage_ms["fwd"]
     log(f"[bench] ms/step {ms_step:.3f}; stages (ms): " +
         ", ".join(f"{n} {v:.3f}" for n, v in stage_ms.items()))
 
@@ -296,6 +341,8 @@ def run_workload(name, args, dev, cpu_leg: bool):
         "fwd_tflops": round(f_fwd / (stage_ms["fwd"] * 1e-3) / 1e12, 3),
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 3),
         "bwd_frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "schedule": "serial" if serial else "overlapped (inversion beside the forward, "
+                                            "dK/dV reduce beside dQ; two streams)",
         "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "step_ms_events": step_stats,
         "roofline": roofline,
@@ -321,6 +368,9 @@ def main():
                     help="sliding window of this many keys (0: none); a variant, not the metric's workload")
     ap.add_argument("--sink", action="store_true",
                     help="per-head attention-sink logits (forward with sink, dsink stage timed too)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run every stage on one stream (default: the inversion beside the "
+                         "forward and the dK/dV reduce beside dQ, on a second stream)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed steps, convert a bf16 tensor of this many MiB to "
                          "float32 once (a kernel of known traffic for scaling counters)")
@@ -348,7 +398,7 @@ def main():
             r = run_workload(other, args, dev, cpu_leg=False)
             out["also"].append({k: r[k] for k in ("config", "value", "ms_per_step", "frac_of_peak",
                                                    "fwd_tflops", "bwd_tflops", "bwd_frac_of_peak",
-                                                   "stage_ms", "step_ms_events", "roofline",
+                                                   "stage_ms", "step_ms_events", "roofline", "schedule",
                                                    "ds_handoff")})
     out["git"] = nsa.build_git()
     if out["git"] == "unknown":

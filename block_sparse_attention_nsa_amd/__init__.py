@@ -247,6 +247,21 @@ class BwdStages:
                                           _ptr(self.cu), _ptr(self.ws), self.ws.numel(), _stream())
         _lib.check("nsa_sel_bwd_prepare", st)
 
+    def prepare_lists(self):
+        """The inversion and dK/dV plan alone (nsa_sel_bwd_prepare_lists):
+        needs only block_idx, so it may run during the forward."""
+        st = self.lib.nsa_sel_bwd_prepare_lists(self.p, _ptr(self.idx), _ptr(self.cu),
+                                                _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_prepare_lists", st)
+
+    def prepare_delta(self, o, dO):
+        """Delta alone (nsa_sel_bwd_prepare_delta); with prepare_lists it
+        equals prepare."""
+        set_strides(self.p, o=o, dO=dO)
+        st = self.lib.nsa_sel_bwd_prepare_delta(self.p, _ptr(o), _ptr(dO), _ptr(self.cu),
+                                                _ptr(self.ws), self.ws.numel(), _stream())
+        _lib.check("nsa_sel_bwd_prepare_delta", st)
+
     def dq_stage(self, dO, lse):
         set_strides(self.p, dO=dO)
         st = self.lib.nsa_sel_bwd_dq(self.p, _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(dO),

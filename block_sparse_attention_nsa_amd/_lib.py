@@ -18,6 +18,8 @@ EXPORTS = (
     "nsa_sel_bwd_noalloc",
     "nsa_sel_bwd_workspace_bytes",
     "nsa_sel_bwd_prepare",
+    "nsa_sel_bwd_prepare_lists",
+    "nsa_sel_bwd_prepare_delta",
     "nsa_sel_bwd_dq",
     "nsa_sel_bwd_dkdv",
     "nsa_sel_bwd_dkdv_blocks",
@@ -96,6 +98,10 @@ def load():
     lib.nsa_sel_bwd_workspace_bytes.restype = sz
     lib.nsa_sel_bwd_prepare.argtypes = [P, vp, vp, ip, ip, vp, sz, vp]
     lib.nsa_sel_bwd_prepare.restype = st
+    lib.nsa_sel_bwd_prepare_lists.argtypes = [P, ip, ip, vp, sz, vp]
+    lib.nsa_sel_bwd_prepare_lists.restype = st
+    lib.nsa_sel_bwd_prepare_delta.argtypes = [P, vp, vp, ip, vp, sz, vp]
+    lib.nsa_sel_bwd_prepare_delta.restype = st
     lib.nsa_sel_bwd_dq.argtypes = [P, vp, vp, vp, vp, fp, ip, ip, vp, vp, sz, vp]
     lib.nsa_sel_bwd_dq.restype = st
     lib.nsa_sel_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, fp, ip, vp, vp, vp, sz, vp]

@@ -666,6 +666,36 @@ nsa_status nsa_sel_bwd_prepare(const nsa_sel_problem* p, const void* o, const vo
     return run_prepare(hp, a, reinterpret_cast<hipStream_t>(stream));
 }
 
+nsa_status nsa_sel_bwd_prepare_lists(const nsa_sel_problem* p, const int32_t* block_idx,
+                                     const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{kAbsent, kAbsent, kAbsent, kAbsent, kAbsent, kAbsent, kAbsent,
+                    kAbsent, (const float*)kAbsent, block_idx, cu_seqlens, workspace, workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    const nsa::BwdWorkspace ws = carve(hp, workspace);
+    NSA_HIP(nsa::launch_prepare_lists(hp, block_idx, ws, reinterpret_cast<hipStream_t>(stream)),
+            "inversion launch");
+    return NSA_OK;
+}
+
+nsa_status nsa_sel_bwd_prepare_delta(const nsa_sel_problem* p, const void* o, const void* dO,
+                                     const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, nsa_stream_t stream) {
+    g_last_error.clear();
+    nsa::HostProblem hp;
+    const BwdArgs a{kAbsent, kAbsent, kAbsent, o,       dO,      kAbsent, kAbsent,
+                    kAbsent, (const float*)kAbsent, (const int32_t*)kAbsent, cu_seqlens, workspace,
+                    workspace_bytes};
+    NSA_TRY(check_bwd(p, a, hp));
+    if (sizes_of(hp).q == 0) return NSA_OK;
+    const nsa::BwdWorkspace ws = carve(hp, workspace);
+    NSA_HIP(nsa::launch_delta(hp, o, dO, ws.delta, reinterpret_cast<hipStream_t>(stream)), "delta launch");
+    return NSA_OK;
+}
+
 nsa_status nsa_sel_bwd_dq(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
                           const void* dO, const float* lse, const int32_t* block_idx,
                           const int32_t* cu_seqlens, void* dq, void* workspace,

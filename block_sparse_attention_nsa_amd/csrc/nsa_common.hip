@@ -665,6 +665,17 @@ hipError_t launch_invert(const HostProblem& hp, const int* block_idx, const BwdW
     return launch_scan_fill(hp, block_idx, ws, st, false);
 }
 
+// The prepare stage without Delta: the inversion and the dK/dV plan (as the
+// backward needs them, lists optional for whole-prefix selections).
+hipError_t launch_prepare_lists(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
+                                hipStream_t st) {
+    const Problem& p = hp.dev;
+    if (hp.ZH == 0 || hp.C == 0) return hipSuccess;
+    hipLaunchKernelGGL(inv_count_kernel, dim3(hp.C, hp.ZH), dim3(64 * kInvWaves), count_lds_bytes(p),
+                       st, p, hp.CT, hp.C, block_idx, ws.chunk_pos, ws.ticket);
+    return launch_scan_fill(hp, block_idx, ws, st, true);
+}
+
 hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, const int* block_idx,
                           const BwdWorkspace& ws, hipStream_t st) {
     const Problem& p = hp.dev;

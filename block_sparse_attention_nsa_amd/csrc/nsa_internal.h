@@ -75,6 +75,8 @@ hipError_t launch_check_idx(const HostProblem& hp, const int* block_idx, unsigne
 // Delta, the inversion and the dK/dV work plan, as the backward's prepare
 // stage runs them (for bf16 the Delta rows and the inversion counts share one
 // launch; the last scan workgroup writes the plan).
+hipError_t launch_prepare_lists(const HostProblem& hp, const int* block_idx, const BwdWorkspace& ws,
+                                hipStream_t st);
 hipError_t launch_prepare(const HostProblem& hp, const void* o, const void* dO, const int* block_idx,
                           const BwdWorkspace& ws, hipStream_t st);
 

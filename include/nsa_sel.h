@@ -186,10 +186,25 @@ nsa_status nsa_sel_bwd_noalloc(const nsa_sel_problem* p, const void* q, const vo
  * dkdv writes fp32 partials into the workspace, and, for problems whose dQ
  * takes over the dK/dV kernel's dS (see nsa_sel_bwd), that dS: dq must then
  * run after dkdv (after nsa_sel_bwd_dkdv_blocks) on the same workspace; for
- * the other problems dq and dkdv are independent. */
+ * the other problems dq and dkdv are independent.  dq and
+ * nsa_sel_bwd_dkdv_reduce are always independent of each other (they read
+ * and write disjoint data), so after _blocks they may run concurrently. */
 nsa_status nsa_sel_bwd_prepare(const nsa_sel_problem* p, const void* o, const void* dO,
                                const int32_t* block_idx, const int32_t* cu_seqlens,
                                void* workspace, size_t workspace_bytes, nsa_stream_t stream);
+
+/* nsa_sel_bwd_prepare in its two independent parts, same workspace:
+ * _lists computes the block -> query inversion and the dK/dV work plan from
+ * block_idx alone (so it may run before or during the forward), _delta
+ * computes Delta from o and dO.  They write disjoint parts of the
+ * workspace: calling both, in either order or concurrently on two streams,
+ * equals nsa_sel_bwd_prepare (bitwise). */
+nsa_status nsa_sel_bwd_prepare_lists(const nsa_sel_problem* p, const int32_t* block_idx,
+                                     const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, nsa_stream_t stream);
+nsa_status nsa_sel_bwd_prepare_delta(const nsa_sel_problem* p, const void* o, const void* dO,
+                                     const int32_t* cu_seqlens, void* workspace,
+                                     size_t workspace_bytes, nsa_stream_t stream);
 nsa_status nsa_sel_bwd_dq(const nsa_sel_problem* p, const void* q, const void* k, const void* v,
                           const void* dO, const float* lse, const int32_t* block_idx,
                           const int32_t* cu_seqlens, void* dq, void* workspace,

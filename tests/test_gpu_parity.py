@@ -459,6 +459,42 @@ def test_staged_backward_equals_one_call(name):
         assert torch.equal(a, b), n
 
 
+@pytest.mark.parametrize("name", ["select_T8192", "causal_B4_T4096", "packed_8seq"])
+def test_two_stream_schedule_equals_one_call(name):
+    """The inversion on a second stream beside the forward, and the dK/dV
+    reduce beside dQ, equal nsa_sel_bwd bit for bit, over three steps that
+    reuse one workspace (the order the two-stream step of the benchmark uses)."""
+    w = workloads.make_workload(name)
+    d = to_dev(w)
+    cu = d.get("cu")
+    ms = w.max_seqlen if w.packed else None
+    o, lse = nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms)
+    dq, dk, dv = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"], w.block_size,
+                                 w.scale, cu, ms)
+    torch.cuda.synchronize()
+    st = nsa.BwdStages(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    for it in range(3):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            st.prepare_lists()
+        nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms,
+                        out=o2, lse=lse2)
+        st.prepare_delta(o2, d["dO"])
+        main.wait_stream(side)
+        st.dkdv_blocks(d["dO"], lse2)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            dk2, dv2 = st.dkdv_reduce()
+        dq2 = st.dq_stage(d["dO"], lse2)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for a, b, n in ((o, o2, "o"), (lse, lse2, "lse"), (dq, dq2, "dq"), (dk, dk2, "dk"),
+                        (dv, dv2, "dv")):
+            assert torch.equal(a, b), f"step {it}: {n}"
+
+
 def test_runs_on_caller_stream():
     """All work is queued on the caller's (non-default) stream."""
     w = workloads.make_workload("bf16_T1024")
