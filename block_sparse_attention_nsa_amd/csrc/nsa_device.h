@@ -298,6 +298,34 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 
+// Wave-uniform tests of a per-lane condition, decided on the scalar unit
+// (ballot against exec: no vector compare / select / readfirstlane chain).
+__device__ __forceinline__ bool wave_all(bool c) {
+    return __builtin_amdgcn_ballot_w64(c) == __builtin_amdgcn_read_exec();
+}
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0ull; }
+// A value the caller knows to be wave-uniform, moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Float max as the bare instruction.  fmaxf obliges the compiler to quiet a
+// signalling NaN first, i.e. an extra v_max_f32 x, x on every operand it
+// cannot prove canonical (all permlane results, every loop-carried value);
+// the scores these kernels take the max of are never NaN.
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 (one C-layout column),
 // with gfx950's lane-half swaps (v_permlane32_swap exchanges lanes 32..63 of
 // one operand with lanes 0..31 of the other, v_permlane16_swap the odd rows
@@ -306,10 +334,10 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
 __device__ __forceinline__ float col_max4(float v) {
     const uint32_t u = __float_as_uint(v);
     const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const float m = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const uint32_t um = __float_as_uint(m);
     const auto b = __builtin_amdgcn_permlane16_swap(um, um, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float col_sum4(float v) {
     const uint32_t u = __float_as_uint(v);

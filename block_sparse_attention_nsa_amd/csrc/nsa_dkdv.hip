@@ -25,6 +25,7 @@
 // the call and its gradients; the backward formulas are the exact gradient of
 // the masked softmax attention, as stated in include/nsa_sel.h.
 #include <algorithm>
+#include <type_traits>
 
 #include "nsa_internal.h"
 
@@ -284,31 +285,53 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                 // Row x of the step is list row f_end - 32 (i + 1) + x; rows
                 // below the chunk take token -1 (no key passes the mask).
                 const int f0 = f_end - 32 * (i + 1) - f_begin;
-                float pv[2][2][4], dsv[2][2][4];
+                int tv[2][4];  // key positions of the rows' tokens; -1: no row
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     const int x0 = f0 + 16 * rt + 4 * g;
-                    // (key positions of the rows' tokens; -1: no row)
-                    const int tv[4] = {x0 >= 0 ? tt[rt].x + s.qoff : -1, x0 + 1 >= 0 ? tt[rt].y + s.qoff : -1,
-                                       x0 + 2 >= 0 ? tt[rt].z + s.qoff : -1, x0 + 3 >= 0 ? tt[rt].w + s.qoff : -1};
-                    const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
-                                         -ll[rt].w * kLog2e};
-                    const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
+                    tv[rt][0] = x0 >= 0 ? tt[rt].x + s.qoff : -1;
+                    tv[rt][1] = x0 + 1 >= 0 ? tt[rt].y + s.qoff : -1;
+                    tv[rt][2] = x0 + 2 >= 0 ? tt[rt].z + s.qoff : -1;
+                    tv[rt][3] = x0 + 3 >= 0 ? tt[rt].w + s.qoff : -1;
+                }
+                float pv[2][2][4], dsv[2][2][4];
+                auto p_ds = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt) {
-                        const int key = kbase + 16 * kt + r;
+                    for (int rt = 0; rt < 2; ++rt) {
+                        const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
+                                             -ll[rt].w * kLog2e};
+                        const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
 #pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) {
-                            const float e = fast_exp2(fmaf(sc[rt][kt][i4], c2, nl[i4]));
-                            const bool vis = 16 * kt < BK &&
-                                             (WIN ? key <= tv[i4] && key + p.window > tv[i4]
-                                                  : key <= tv[i4]);
-                            const float P = vis ? e : 0.f;
-                            pv[kt][rt][i4] = P;
-                            dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
+                        for (int kt = 0; kt < 2; ++kt) {
+                            const int key = kbase + 16 * kt + r;
+#pragma unroll
+                            for (int i4 = 0; i4 < 4; ++i4) {
+                                const float e = fast_exp2(fmaf(sc[rt][kt][i4], c2, nl[i4]));
+                                float P = e;
+                                if constexpr (decltype(masked)::value) {
+                                    const bool vis = 16 * kt < BK &&
+                                                     (WIN ? key <= tv[rt][i4] && key + p.window > tv[rt][i4]
+                                                          : key <= tv[rt][i4]);
+                                    P = vis ? e : 0.f;
+                                }
+                                pv[kt][rt][i4] = P;
+                                dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
+                            }
                         }
                     }
+                };
+                // Every row of the step exists and sees all of the pair's keys
+                // (away from the diagonal and the list's end): no selects.
+                int tmin = min(min(min(tv[0][0], tv[0][1]), min(tv[0][2], tv[0][3])),
+                               min(min(tv[1][0], tv[1][1]), min(tv[1][2], tv[1][3])));
+                bool open = BK >= 32 && tmin >= kbase + 31;
+                if constexpr (WIN) {
+                    const int tmax = max(max(max(tv[0][0], tv[0][1]), max(tv[0][2], tv[0][3])),
+                                         max(max(tv[1][0], tv[1][1]), max(tv[1][2], tv[1][3])));
+                    open = open && kbase + p.window > tmax;
                 }
+                if (wave_all(open)) p_ds(std::false_type{});
+                else p_ds(std::true_type{});
                 uint4 pk[2][2];
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {

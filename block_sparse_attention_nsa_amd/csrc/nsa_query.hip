@@ -604,7 +604,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     uint16_t* ulist = reinterpret_cast<uint16_t*>(umask + p.NBmax);
     int* n_u = reinterpret_cast<int*>(smem + QLds<D, JK>::dynamic_bytes(p.NBmax) - 16);
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6),
+              g = lane >> 4, r = lane & 15;
     const WgCoord wc = wg_coord(p, qg);
     const Seq s = seq_of(p, wc.z);
     if (wc.T0 >= s.len) return;
@@ -627,12 +628,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     uint64_t tmask[RT];
     bf16x8 qf[RT][KD];
     f32x4 acc[RT][ND];
-    float m_run[RT], l_run[RT];
+    // Running max and sum per row; mc = the max in base-2 units, or 0 while
+    // the row has seen no key (the exponent's offset, updated with m_run).
+    float m_run[RT], l_run[RT], mc[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
         const int tau = w * RT + i;
         tr[i] = tile_row(p, qg, wc.hkv, wc.T0, s.len, tau, r);
-        tmask[i] = tile_tokens(p, qg, tau);
+        tmask[i] = uniform64(tile_tokens(p, qg, tau));
         const uint16_t* qrow = q + row_off(p.lq, s, tr[i].h, tr[i].t) + 8 * g;
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk)
@@ -641,6 +644,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         for (int dt = 0; dt < ND; ++dt) acc[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_run[i] = kNegInfQ;
         l_run[i] = 0.f;
+        mc[i] = 0.f;
     }
     const int nU = wg_union(p, s, idx, wc.hkv, wc.T0, n_tok, NBz, umask, ulist, n_u);
     const float c2 = p.scale_log2;
@@ -674,13 +678,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         const bool full = KT == JK && ((bm & tmask[i]) == tmask[i]) &&
                           (cur.j0 + JK - 1 <= tr[i].t + qoff - (tr[i].tok - (int)__builtin_ctzll(tmask[i]))) &&
                           tr[i].valid && (!WIN || cur.j0 > tr[i].t + qoff - p.window);
-        float mloc = kNegInfQ;
-        if (__builtin_amdgcn_readfirstlane((int)__all(full))) {
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, sc[kt][e]);
-        } else {
+        // The mask overwrites masked scores in place (the no-mask path then
+        // needs no copies of the scores where the two paths meet).
+        if (!wave_all(full)) {
             const bool sel = tr[i].valid && ((bm >> tr[i].tok) & 1ull);
             // Key 16 kt + 4 g + e is masked past lim; compared as
             // 16 kt + e > lim - 4 g so the left side is a constant.
@@ -690,32 +690,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < 4; ++e)
                     if (16 * kt >= KT || 16 * kt + e > lim || (WIN && 16 * kt + e < lo))
                         sc[kt][e] = kNegInfQ;
-                    mloc = fmaxf(mloc, sc[kt][e]);
-                }
         }
+        // Row max of the lane's 4 NKT scores: a v_max3 chain.
+        float mloc = vmax3(sc[0][0], sc[0][1], sc[0][2]);
+#pragma unroll
+        for (int x = 3; x + 1 < 4 * NKT; x += 2) mloc = vmax3(mloc, sc[x / 4][x % 4], sc[(x + 1) / 4][(x + 1) % 4]);
+        if constexpr ((4 * NKT) % 2 == 0) mloc = vmax(mloc, sc[NKT - 1][3]);
         const float mblk = col_max4(mloc);
         const bool grow = mblk * c2 > m_run[i] * c2 + kLazyQ;
-        if (__builtin_amdgcn_readfirstlane((int)__any(grow))) {
+        if (wave_any(grow)) {
             const float m_new = grow ? mblk : m_run[i];
             const float alpha = grow ? fast_exp2((m_run[i] - m_new) * c2) : 1.f;
 #pragma unroll
             for (int dt = 0; dt < ND; ++dt) acc[i][dt] *= alpha;
             l_run[i] *= alpha;
             m_run[i] = m_new;
+            mc[i] = m_new == kNegInfQ ? 0.f : m_new * c2;
         }
-        const float mc = m_run[i] == kNegInfQ ? 0.f : m_run[i] * c2;
-        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+        float lsum[4];
 #pragma unroll
         for (int ks_ = 0; ks_ < NKS; ++ks_) {
             float p0[4], p1[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                p0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, -mc));
-                p1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, -mc));
-                lsum[e] += p0[e] + p1[e];
+                p0[e] = fast_exp2(fmaf(sc[2 * ks_][e], c2, -mc[i]));
+                p1[e] = fast_exp2(fmaf(sc[2 * ks_ + 1][e], c2, -mc[i]));
+                lsum[e] = ks_ == 0 ? p0[e] + p1[e] : lsum[e] + (p0[e] + p1[e]);
             }
             pb[ks_] = pack8(p0, p1);
         }
@@ -729,10 +732,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
-        const uint64_t bm = umask[cur.u];
+        const uint64_t bm = uniform64(umask[cur.u]);
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            if (!__builtin_amdgcn_readfirstlane((int)((bm & tmask[i]) != 0ull))) continue;
+            if ((bm & tmask[i]) == 0ull) continue;
             f32x4 sc[NKT];
             {
                 KOps ka;
@@ -777,11 +780,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         static_assert(RT == 2, "two tiles per wave");
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
-        const uint64_t bm = umask[cur.u];
+        const uint64_t bm = uniform64(umask[cur.u]);
         // Neither tile's tokens list the block (or both tiles are idle: past
         // the workgroup's tokens when G < 4): nothing to compute.  Loads and
         // barriers happen outside, so leaving early is safe.
-        if (!__builtin_amdgcn_readfirstlane((int)((bm & (tmask[0] | tmask[1])) != 0ull))) return;
+        if ((bm & (tmask[0] | tmask[1])) == 0ull) return;
         f32x4 sc0[NKT], sc1[NKT];
         {
             KOps ka;
