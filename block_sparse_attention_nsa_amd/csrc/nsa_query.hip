@@ -220,13 +220,23 @@ __device__ int wg_union(const Problem& p, const Seq& s, const int* __restrict__ 
             atomicOr(&umask[u], 1ull << a);
     }
     __syncthreads();
+    // The listed blocks in ascending order, and their token masks moved to
+    // the same positions (umask[i] = the mask of block ulist[i]), so a walk
+    // reads a job's block and mask from one position.  In place: a
+    // position never exceeds its block, and each 64-block chunk's masks are
+    // read before any lane writes.
     if (tid < 64) {
         int n = 0;
         for (int base = 0; base < NBz; base += 64) {
             const int u = base + tid;
-            const bool nz = u < NBz && umask[u] != 0ull;
+            const uint64_t m = u < NBz ? umask[u] : 0ull;
+            const bool nz = m != 0ull;
             const uint64_t bal = __ballot(nz);
-            if (nz) ulist[n + __popcll(bal & ((1ull << tid) - 1ull))] = (uint16_t)u;
+            if (nz) {
+                const int pos = n + __popcll(bal & ((1ull << tid) - 1ull));
+                ulist[pos] = (uint16_t)u;
+                umask[pos] = m;
+            }
             n += __popcll(bal);
         }
         if (tid == 0) *n_out = n;
@@ -236,23 +246,33 @@ __device__ int wg_union(const Problem& p, const Seq& s, const int* __restrict__ 
 }
 
 // The workgroup's walk: JK-key jobs (block ulist[iu], slice sb), slices that
-// start after the last token skipped.  All values wave-uniform.
+// start after the last token skipped.  All values wave-uniform.  bm: the
+// tokens of the workgroup that list the block (umask[iu]), read with the
+// block for the jobs a wave computes (MASK), so the job's first operand
+// reads need no LDS round trip of their own.
 struct Job {
     int iu, sb, u, j0;
     bool ok;
+    uint64_t bm;
 };
-template <int BS>
-__device__ __forceinline__ Job first_job(const uint16_t* ulist, int nU) {
+struct UnionList {
+    const uint16_t* ulist;
+    const unsigned long long* umask;
+    int nU;
+};
+template <int BS, bool MASK = false>
+__device__ __forceinline__ Job first_job(const UnionList& ul) {
     Job j;
     j.iu = 0;
     j.sb = 0;
-    j.ok = nU > 0;
-    j.u = j.ok ? __builtin_amdgcn_readfirstlane(ulist[0]) : 0;
+    j.ok = ul.nU > 0;
+    j.u = j.ok ? __builtin_amdgcn_readfirstlane(ul.ulist[0]) : 0;
+    j.bm = MASK && j.ok ? uniform64(ul.umask[0]) : 0ull;
     j.j0 = j.u * BS;
     return j;
 }
-template <int BS>
-__device__ __forceinline__ Job next_job_q(Job c, const uint16_t* ulist, int nU, int t_last) {
+template <int BS, bool MASK = false>
+__device__ __forceinline__ Job next_job_q(Job c, const UnionList& ul, int t_last) {
     constexpr int JK = JobKeys<BS>::JK;
     if (!c.ok) return c;
     if (c.sb + 1 < BS / JK && c.j0 + JK <= t_last) {
@@ -260,13 +280,14 @@ __device__ __forceinline__ Job next_job_q(Job c, const uint16_t* ulist, int nU, 
         c.j0 += JK;
         return c;
     }
-    if (c.iu + 1 >= nU) {
+    if (c.iu + 1 >= ul.nU) {
         c.ok = false;
         return c;
     }
     ++c.iu;
     c.sb = 0;
-    c.u = __builtin_amdgcn_readfirstlane(ulist[c.iu]);
+    c.u = __builtin_amdgcn_readfirstlane(ul.ulist[c.iu]);
+    if constexpr (MASK) c.bm = uniform64(ul.umask[c.iu]);
     c.j0 = c.u * BS;
     return c;
 }
@@ -368,9 +389,8 @@ __device__ __forceinline__ void wait_vm() {
 // by waves at or ahead of it), so the walk ends.  Counts are cumulative: the
 // u-th use of a stage is complete at NW * (u + 1).
 template <int D, int BS, int NW, class Compute>
-__device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
-                                       const uint16_t* ulist, int nU, int t_last, int lane,
-                                       Compute&& compute) {
+__device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld, const UnionList& ul,
+                                       int t_last, int lane, Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK, NS = kQStages, A = kQAhead;
     using LD = KVLoad<D, NW, JK>;
     static_assert(NS == 4 && A == 2, "the unrolled walk below is written for 4 stages, 2 ahead");
@@ -403,30 +423,30 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
         signal(done_c, lane);
         ++j;
     };
-    Job jc = first_job<BS>(ulist, nU);
+    Job jc = first_job<BS, true>(ul);
     Job ji = jc;
     ld.issue(ji.j0, ji.ok, s0);
-    ji = next_job_q<BS>(ji, ulist, nU, t_last);
+    ji = next_job_q<BS>(ji, ul, t_last);
     ld.issue(ji.j0, ji.ok, s1);
-    ji = next_job_q<BS>(ji, ulist, nU, t_last);
+    ji = next_job_q<BS>(ji, ul, t_last);
     own_landed();
     signal(&landed[0], lane);
     while (jc.ok) {
         step(jc, ji, s0, s2, &landed[0], &landed[1], &done[0], &done[2]);
-        jc = next_job_q<BS>(jc, ulist, nU, t_last);
-        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        jc = next_job_q<BS, true>(jc, ul, t_last);
+        ji = next_job_q<BS>(ji, ul, t_last);
         if (!jc.ok) break;
         step(jc, ji, s1, s3, &landed[1], &landed[2], &done[1], &done[3]);
-        jc = next_job_q<BS>(jc, ulist, nU, t_last);
-        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        jc = next_job_q<BS, true>(jc, ul, t_last);
+        ji = next_job_q<BS>(ji, ul, t_last);
         if (!jc.ok) break;
         step(jc, ji, s2, s0, &landed[2], &landed[3], &done[2], &done[0]);
-        jc = next_job_q<BS>(jc, ulist, nU, t_last);
-        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        jc = next_job_q<BS, true>(jc, ul, t_last);
+        ji = next_job_q<BS>(ji, ul, t_last);
         if (!jc.ok) break;
         step(jc, ji, s3, s1, &landed[3], &landed[0], &done[3], &done[1]);
-        jc = next_job_q<BS>(jc, ulist, nU, t_last);
-        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        jc = next_job_q<BS, true>(jc, ul, t_last);
+        ji = next_job_q<BS>(ji, ul, t_last);
     }
     // Loads of job slots past the end finish before the wave leaves.
     wait_vm<0>();
@@ -442,8 +462,7 @@ __device__ __forceinline__ void q_ring(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
 // loads of jobs j + 2 and j + 3 in flight.
 template <int D, int BS, int NW, class Compute>
 __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>& ld,
-                                            const uint16_t* ulist, int nU, int t_last,
-                                            Compute&& compute) {
+                                            const UnionList& ul, int t_last, Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK;
     using LD = KVLoad<D, NW, JK>;
     static_assert(kQStages == 4, "the unrolled walk below is written for 4 stages");
@@ -456,10 +475,10 @@ __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>
             if (full) wait_vm_barrier<2 * LD::kPerWave>(); else wait_vm_barrier<0>();
         }
     };
-    Job jc = first_job<BS>(ulist, nU);
-    Job j1 = next_job_q<BS>(jc, ulist, nU, t_last);
-    Job j2 = next_job_q<BS>(j1, ulist, nU, t_last);
-    Job j3 = next_job_q<BS>(j2, ulist, nU, t_last);
+    Job jc = first_job<BS, true>(ul);
+    Job j1 = next_job_q<BS, true>(jc, ul, t_last);
+    Job j2 = next_job_q<BS, true>(j1, ul, t_last);
+    Job j3 = next_job_q<BS, true>(j2, ul, t_last);
     ld.issue(jc.j0, jc.ok, s0);
     ld.issue(j1.j0, j1.ok, s1);
     ld.issue(j2.j0, j2.ok, s2);
@@ -475,7 +494,7 @@ __device__ __forceinline__ void q_ring_sync(const KVLoad<D, NW, JobKeys<BS>::JK>
         jc = j1;
         j1 = j2;
         j2 = j3;
-        j3 = next_job_q<BS>(j3, ulist, nU, t_last);
+        j3 = next_job_q<BS, true>(j3, ul, t_last);
     };
     while (jc.ok) {
         step(s0, s3);
@@ -511,7 +530,7 @@ struct alignas(16) DsBuf {
 // the wait in 3 leaves in flight with the ring's job j + A.
 template <int D, int BS, int NW, int RT, class IssueDs, class Compute>
 __device__ __forceinline__ void q_ring_ds(const KVLoad<D, NW, JobKeys<BS>::JK, true>& ld,
-                                          const uint16_t* ulist, int nU, int t_last, int lane,
+                                          const UnionList& ul, int t_last, int lane,
                                           IssueDs&& issue_ds, Compute&& compute) {
     constexpr int JK = JobKeys<BS>::JK, NS = kQStages, A = kQAhead, NDMA = JK / 32;
     using LD = KVLoad<D, NW, JK, true>;
@@ -552,9 +571,9 @@ __device__ __forceinline__ void q_ring_ds(const KVLoad<D, NW, JobKeys<BS>::JK, t
         signal(done_c, lane);
         ++j;
     };
-    Job jc = first_job<BS>(ulist, nU);
-    Job jn = next_job_q<BS>(jc, ulist, nU, t_last);
-    Job ji = next_job_q<BS>(jn, ulist, nU, t_last);
+    Job jc = first_job<BS>(ul);
+    Job jn = next_job_q<BS>(jc, ul, t_last);
+    Job ji = next_job_q<BS>(jn, ul, t_last);
     issue_ds(jc, d0);
     ld.issue(jc.j0, jc.ok, s0);
     ld.issue(jn.j0, jn.ok, s1);
@@ -563,7 +582,7 @@ __device__ __forceinline__ void q_ring_ds(const KVLoad<D, NW, JobKeys<BS>::JK, t
     auto advance = [&]() {
         jc = jn;
         jn = ji;
-        ji = next_job_q<BS>(ji, ulist, nU, t_last);
+        ji = next_job_q<BS>(ji, ul, t_last);
     };
     while (jc.ok) {
         step(jc, jn, ji, s0, s2, d0, d1, &landed[0], &landed[1], &done[0], &done[2]);
@@ -732,7 +751,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
-        const uint64_t bm = uniform64(umask[cur.u]);
+        const uint64_t bm = cur.bm;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             if ((bm & tmask[i]) == 0ull) continue;
@@ -780,7 +799,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
         static_assert(RT == 2, "two tiles per wave");
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
-        const uint64_t bm = uniform64(umask[cur.u]);
+        const uint64_t bm = cur.bm;
         // Neither tile's tokens list the block (or both tiles are idle: past
         // the workgroup's tokens when G < 4): nothing to compute.  Loads and
         // barriers happen outside, so leaving early is safe.
@@ -824,9 +843,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_q_kernel(Problem p, QGeo qg,
     };
 
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, ulist, nU, t_last, compute_pair);
+        q_ring_sync<D, BS, NW>(ld, UnionList{ulist, umask, nU}, t_last, compute_pair);
     } else {
-        q_ring<D, BS, NW>(ld, ulist, nU, t_last, lane, compute);
+        q_ring<D, BS, NW>(ld, UnionList{ulist, umask, nU}, t_last, lane, compute);
     }
 
 #pragma unroll
@@ -959,7 +978,7 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     auto compute = [&](const Job& cur, const KVStage<D, JK>& sg) {
         const uint8_t* ks = reinterpret_cast<const uint8_t*>(sg.k);
         const uint8_t* vs = reinterpret_cast<const uint8_t*>(sg.v);
-        const uint64_t bm = umask[cur.u];
+        const uint64_t bm = cur.bm;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             if (!__builtin_amdgcn_readfirstlane((int)((bm & tmask[i]) != 0ull))) continue;
@@ -996,9 +1015,9 @@ __global__ __launch_bounds__(NW * 64) void dq_q_kernel(
     };
 
     if constexpr (SYNC) {
-        q_ring_sync<D, BS, NW>(ld, ulist, nU, t_last, compute);
+        q_ring_sync<D, BS, NW>(ld, UnionList{ulist, umask, nU}, t_last, compute);
     } else {
-        q_ring<D, BS, NW>(ld, ulist, nU, t_last, lane, compute);
+        q_ring<D, BS, NW>(ld, UnionList{ulist, umask, nU}, t_last, lane, compute);
     }
 
 #pragma unroll
@@ -1207,7 +1226,7 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
         }
     };
 
-    q_ring_ds<D, BS, NW, RT>(ld, ulist, nU, t_last, lane, issue_ds, compute);
+    q_ring_ds<D, BS, NW, RT>(ld, UnionList{ulist, umask, nU}, t_last, lane, issue_ds, compute);
 
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
