@@ -174,9 +174,10 @@ def run_workload(name, args, dev, cpu_leg: bool):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
     stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms, window=args.window)
-    serial = args.serial or args.sink
-    names = (("fwd", "prepare", "dkdv", "dkdv_reduce", "dq") + (("dsink",) if args.sink else ())
-             if serial else ("fwd", "prepare_lists", "prepare_delta", "dkdv", "dkdv_reduce", "dq"))
+    serial = args.serial
+    names = (("fwd", "prepare", "dkdv", "dkdv_reduce", "dq") if serial else
+             ("fwd", "prepare_lists", "prepare_delta", "dkdv", "dkdv_reduce", "dq")) + \
+        (("dsink",) if args.sink else ())
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     sink = None
@@ -198,7 +199,7 @@ def run_workload(name, args, dev, cpu_leg: bool):
             stages.prepare_lists()
             ev(2)
         ev(0)
-        nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse,
+        nsa.nsa_sel_fwd(q, k, v, idx, w.block_size, w.scale, cu, ms, out=o, lse=lse, sink=sink,
                         window=args.window)
         ev(3)
         stages.prepare_delta(o, dO)
@@ -213,6 +214,9 @@ def run_workload(name, args, dev, cpu_leg: bool):
             ev(7)
         stages.dq_stage(dO, lse)
         ev(8)
+        if sink is not None:
+            stages.dsink_stage(lse, sink, out=dsink)
+        ev(10)
         main.wait_stream(side)
         ev(9)
 
@@ -245,7 +249,7 @@ def run_workload(name, args, dev, cpu_leg: bool):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    n_ev = len(names) + 1 if serial else 10
+    n_ev = len(names) + 1 if serial else 11
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -259,7 +263,8 @@ def run_workload(name, args, dev, cpu_leg: bool):
     # beside the main stream's, so the stage times overlap)
     pairs = ({n: (j, j + 1) for j, n in enumerate(names)} if serial else
              {"fwd": (0, 3), "prepare_lists": (1, 2), "prepare_delta": (3, 4), "dkdv": (4, 5),
-              "dkdv_reduce": (6, 7), "dq": (5, 8)})
+              "dkdv_reduce": (6, 7), "dq": (5, 8), "dsink": (8, 10)})
+    pairs = {n: ab for n, ab in pairs.items() if n in names}
     for evs in events:
         for n, (a, b) in pairs.items():
             stage_ms[n] += evs[a].elapsed_time(evs[b])
