@@ -5,13 +5,16 @@
 // heads of 16/G tokens (G < 16) or 16 heads of one token (G >= 16) -- the heads
 // of a GQA group share one block list and are stacked as the MFMA rows.  Each
 // wave holds RT tiles.  The workgroup walks the union of its tokens' listed
-// blocks in ascending order, 32 keys at a time ("jobs"); every K/V slice is
-// copied from HBM once per workgroup, straight into a three-stage LDS ring by
-// buffer loads that write LDS (two jobs ahead, no register staging), and read
-// by the waves whose tiles list that block.  Per tile:
+// blocks in ascending order, one job at a time (a 64-key block, half of a
+// 128-key one, or a 32-key block); every K/V slice is copied from HBM once
+// per workgroup, straight into a four-stage LDS ring by buffer loads that
+// write LDS (two jobs ahead, no register staging), and read by the waves
+// whose tiles list that block.  Per tile:
 //   forward  S^T = K Q^T, mask, online softmax (base 2, lazy rescale),
 //            O^T += V^T P^T  (V read transposed from LDS: ds_read_b64_tr_b16)
 //   dQ       S^T = K Q^T, dP^T = V dO^T, dS = P (dP - Delta), dQ^T += K^T dS^T
+//   dQ from the dS the dK/dV kernel hands off: dQ^T += K^T dS^T (K alone in
+//            the ring, dS tiles staged per wave)
 // Every output row has one owner: no atomics.
 //
 // Method: page 1 of the reference text (NSA selection gradcheck gate) defines
