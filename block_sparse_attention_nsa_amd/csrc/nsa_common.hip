@@ -35,8 +35,28 @@ __device__ __forceinline__ void delta_row_offsets(const Problem& p, int64_t r0, 
     od = (int64_t)b * p.ldo.sb + (int32_t)(h * p.ldo.sh + t * p.ldo.st);
 }
 
-// bf16 rows: D/8 lanes per row, 16-byte loads, fp32 products and sums; one
-// 256-thread block covers rows [blk * 256 / (D/8), ...) in lse order.
+// bf16 rows: D/8 lanes per row, 16-byte loads, fp32 products and sums.
+// A lane's eight products, summed in element order:
+__device__ __forceinline__ float delta_dot8(uint4 a, uint4 b) {
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc += bf16_to_f32(av[i] & 0xffff) * bf16_to_f32(bv[i] & 0xffff);
+        acc += bf16_to_f32(av[i] >> 16) * bf16_to_f32(bv[i] >> 16);
+    }
+    return acc;
+}
+// ... then over the row's TPR lanes by a butterfly.
+template <int TPR>
+__device__ __forceinline__ float delta_lanes_sum(float acc) {
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+    return acc;
+}
+
+// One 256-thread block covers rows [blk * 256 / (D/8), ...) in lse order.
 template <int D>
 __device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t* __restrict__ o,
                                                 const uint16_t* __restrict__ dO,
@@ -49,29 +69,47 @@ __device__ __forceinline__ void delta_rows_bf16(const Problem& p, const uint16_t
     if (r < nrows) {
         int64_t oo, od;
         delta_row_offsets(p, blk * RPB, r, oo, od);
-        uint4 a = ldg16(o + oo + part * 8);
-        uint4 b = ldg16(dO + od + part * 8);
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w};
-        const uint32_t bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc += bf16_to_f32(av[i] & 0xffff) * bf16_to_f32(bv[i] & 0xffff);
-            acc += bf16_to_f32(av[i] >> 16) * bf16_to_f32(bv[i] >> 16);
-        }
+        acc = delta_dot8(ldg16(o + oo + part * 8), ldg16(dO + od + part * 8));
     }
-#pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+    acc = delta_lanes_sum<TPR>(acc);
     if (r < nrows && part == 0) delta[r] = acc;
 }
 
 template <int D>
 constexpr int delta_rows_per_block() { return 256 / (D / 8); }
 
-template <int D>
+// The stand-alone Delta launch: NR groups of 256 / (D/8) rows per block, each
+// thread issuing the loads of all its NR rows before the first product, so
+// that a quarter as many, longer-lived blocks keep four times the bytes in
+// flight.  Each row's arithmetic is the one above (same lanes, same order),
+// so Delta is bitwise the same as from count_delta_kernel.
+template <int D, int NR>
 __global__ __launch_bounds__(256) void delta_bf16_kernel(Problem p, const uint16_t* __restrict__ o,
                                                          const uint16_t* __restrict__ dO,
                                                          float* __restrict__ delta, int64_t nrows) {
-    delta_rows_bf16<D>(p, o, dO, delta, nrows, blockIdx.x);
+    constexpr int TPR = D / 8;
+    constexpr int RPB = 256 / TPR;
+    const int64_t r0 = (int64_t)blockIdx.x * (RPB * NR);
+    const int part = threadIdx.x % TPR;
+    uint4 a[NR], b[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int64_t r = r0 + i * RPB + threadIdx.x / TPR;
+        a[i] = make_uint4(0, 0, 0, 0);
+        b[i] = a[i];
+        if (r < nrows) {
+            int64_t oo, od;
+            delta_row_offsets(p, r0, r, oo, od);
+            a[i] = ldg16(o + oo + part * 8);
+            b[i] = ldg16(dO + od + part * 8);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int64_t r = r0 + i * RPB + threadIdx.x / TPR;
+        const float acc = delta_lanes_sum<TPR>(r < nrows ? delta_dot8(a[i], b[i]) : 0.f);
+        if (r < nrows && part == 0) delta[r] = acc;
+    }
 }
 
 __global__ __launch_bounds__(256) void delta_f32_kernel(Problem p, const float* __restrict__ o,
@@ -86,25 +124,29 @@ __global__ __launch_bounds__(256) void delta_f32_kernel(Problem p, const float* 
     delta[r] = acc;
 }
 
+// Row groups per block of the stand-alone bf16 Delta launch.
+constexpr int kDeltaGroups = 4;
+
 hipError_t launch_delta(const HostProblem& hp, const void* o, const void* dO, float* delta,
                         hipStream_t st) {
     const Problem& p = hp.dev;
     int64_t nrows = hp.rows;
     if (nrows == 0) return hipSuccess;
     if (hp.dtype == 1) {
-        int rpb = 256 / (p.D / 8);
+        constexpr int NR = kDeltaGroups;
+        const int rpb = 256 / (p.D / 8) * NR;
         dim3 grid((unsigned)((nrows + rpb - 1) / rpb));
         switch (p.D) {
             case 32:
-                hipLaunchKernelGGL(delta_bf16_kernel<32>, grid, dim3(256), 0, st, p,
+                hipLaunchKernelGGL((delta_bf16_kernel<32, NR>), grid, dim3(256), 0, st, p,
                                    (const uint16_t*)o, (const uint16_t*)dO, delta, nrows);
                 break;
             case 64:
-                hipLaunchKernelGGL(delta_bf16_kernel<64>, grid, dim3(256), 0, st, p,
+                hipLaunchKernelGGL((delta_bf16_kernel<64, NR>), grid, dim3(256), 0, st, p,
                                    (const uint16_t*)o, (const uint16_t*)dO, delta, nrows);
                 break;
             case 128:
-                hipLaunchKernelGGL(delta_bf16_kernel<128>, grid, dim3(256), 0, st, p,
+                hipLaunchKernelGGL((delta_bf16_kernel<128, NR>), grid, dim3(256), 0, st, p,
                                    (const uint16_t*)o, (const uint16_t*)dO, delta, nrows);
                 break;
             default:
