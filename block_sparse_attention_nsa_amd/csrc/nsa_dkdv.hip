@@ -269,6 +269,12 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                         sc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
                         dp[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
+                // S, and dP.  Per-block items issue the dP products inside p_ds below,
+                // between P's exponentials (P needs S alone, so the wave's own
+                // softmax fills the matrix pipe's shadow: dK/dV 1-3 % faster on
+                // sparse lists); paired items keep the two sets together (the
+                // split measured 2-3 % slower there).
+                constexpr bool kLateDp = !PAIRED;
 #pragma unroll
                 for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
@@ -276,9 +282,9 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
                         for (int kt = 0; kt < 2; ++kt) {
                             sc[rt][kt] = mfma(qa[kk][rt], kf[kt][kk], sc[rt][kt]);
-                            dp[rt][kt] = mfma(da[kk][rt], vf[kt][kk], dp[rt][kt]);
+                            if constexpr (!kLateDp) dp[rt][kt] = mfma(da[kk][rt], vf[kt][kk], dp[rt][kt]);
                         }
-                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!kLateDp) __builtin_amdgcn_sched_barrier(0);
 
                 // P and dS for rows 16rt + 4g + i, keys kbase + 16kt + r; the
                 // exponential is taken for every entry and masked by a select.
@@ -296,6 +302,15 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                 }
                 float pv[2][2][4], dsv[2][2][4];
                 auto p_ds = [&](auto masked) __attribute__((always_inline)) {
+                    if constexpr (kLateDp) {
+#pragma unroll
+                        for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+                            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                                for (int kt = 0; kt < 2; ++kt)
+                                    dp[rt][kt] = mfma(da[kk][rt], vf[kt][kk], dp[rt][kt]);
+                    }
 #pragma unroll
                     for (int rt = 0; rt < 2; ++rt) {
                         const float nl[4] = {-ll[rt].x * kLog2e, -ll[rt].y * kLog2e, -ll[rt].z * kLog2e,
@@ -315,8 +330,26 @@ void dkdv_kernel(Problem p, const uint16_t* __restrict__ q, const uint16_t* __re
                                     P = vis ? e : 0.f;
                                 }
                                 pv[kt][rt][i4] = P;
-                                dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
+                                if constexpr (!kLateDp) dsv[kt][rt][i4] = P * (dp[rt][kt][i4] - de[i4]);
                             }
+                        }
+                    }
+                    if constexpr (kLateDp) {
+                        // One dP product, then three of P's instructions.
+#pragma unroll
+                        for (int x = 0; x < 4 * KD; ++x) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);  // VALU, transcendental
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int rt = 0; rt < 2; ++rt) {
+                            const float de[4] = {dd[rt].x, dd[rt].y, dd[rt].z, dd[rt].w};
+#pragma unroll
+                            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                                for (int i4 = 0; i4 < 4; ++i4)
+                                    dsv[kt][rt][i4] = pv[kt][rt][i4] * (dp[rt][kt][i4] - de[i4]);
                         }
                     }
                 };
