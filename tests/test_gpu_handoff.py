@@ -3,7 +3,8 @@
 window, lists that cannot cover whole causal prefixes): dq = scale dS K
 from the stored dS (page 1's gradients; the dQ of the plain masked softmax
 attention).  Every output element against the float64 oracle at page 1's
-bf16 gate, on tile shapes of 4, 2 and 1 tokens of 16 rows, ragged tails,
+bf16 gate, on tile shapes of 4, 2 and 1 tokens of 16 rows (the last at
+head dims 32, 64 and 128 and block sizes 32, 64 and 128), ragged tails,
 lists with -1 padding, duplicates, out-of-range and future blocks and empty
 rows (the dS of a block is taken from its first listing in the row), and
 packed sequences with an empty one.  Each case also checks that the library
@@ -31,6 +32,8 @@ def _handoff_on(w):
     dict(name="ho-G8-D64-bs32", B=1, Hq=16, Hkv=2, T=530, D=64, S=6, bs=32),
     dict(name="ho-G16-D128-bs128", B=1, Hq=16, Hkv=1, T=900, D=128, S=3, bs=128),
     dict(name="ho-G32-D32-bs64", B=1, Hq=64, Hkv=2, T=420, D=32, S=4, bs=64),
+    dict(name="ho-G16-D64-bs64", B=2, Hq=16, Hkv=1, T=611, D=64, S=5, bs=64),
+    dict(name="ho-G16-D128-bs32", B=1, Hq=16, Hkv=1, T=389, D=128, S=7, bs=32),
     dict(name="ho-G4-D64-S>NB", B=1, Hq=8, Hkv=2, T=300, D=64, S=9, bs=32),
 ])
 def test_handoff_irregular_lists(case):
