@@ -271,11 +271,12 @@ def run_workload(name, args, dev, cpu_leg: bool):
         last = len(names) if serial else 9
         return acc, sorted(evs[0].elapsed_time(evs[last]) for evs in events)
 
-    # W warm-up steps; the last few carry every stage's events to find the
-    # dominant kernel.  Each timing event holds its stream back a little
-    # (a few us), so the timed region records only that kernel's two events
-    # (all three candidates' when there is no warm-up).
-    n_pre = min(3, args.warmup)
+    # W warm-up steps; with W >= 3 the last three carry every stage's events
+    # to find the dominant kernel.  Each timing event holds its stream back a
+    # little (a few us), so the timed region records only that kernel's two
+    # events (all three candidates' with fewer warm-up steps, whose first
+    # calls are too cold to rank the kernels).
+    n_pre = 3 if args.warmup >= 3 else 0
     for _ in range(args.warmup - n_pre):
         step()
     cands = ("fwd", "dq", "dkdv")
