@@ -183,7 +183,8 @@ def run_workload(name, args, dev, cpu_leg: bool):
     ms = w.max_seqlen if w.packed else None
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.T) if not w.packed else (w.Hq, w.T), dtype=torch.float32, device=dev)
-    stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms, window=args.window)
+    stages = nsa.BwdStages(q, k, v, idx, w.block_size, w.scale, cu, ms, window=args.window,
+                           sched_policy=args.sched)
     serial = args.serial
     names = (("fwd", "prepare", "dkdv", "dkdv_reduce", "dq") if serial else
              ("fwd", "prepare_lists", "prepare_delta", "dkdv", "dkdv_reduce", "dq")) + \
@@ -363,6 +364,8 @@ def run_workload(name, args, dev, cpu_leg: bool):
         config["window"] = args.window
     if args.sink:
         config["sink"] = "per-head logits ~ N(0, 1)"
+    if args.sched:
+        config["sched_policy"] = args.sched
     out = {
         "metric": "fwd+bwd useful TFLOP/s (bf16, D128) + % of MI355X bf16 MFMA peak",
         "value": round(value, 3),
@@ -411,6 +414,10 @@ def main():
                     help="sliding window of this many keys (0: none); a variant, not the metric's workload")
     ap.add_argument("--sink", action="store_true",
                     help="per-head attention-sink logits (forward with sink, dsink stage timed too)")
+    ap.add_argument("--sched", type=int, default=0, choices=(0, 1),
+                    help="scheduling policy of the hand-off dQ (nsa_sel_problem.sched_policy): "
+                         "0 one workgroup per item, longest first; 1 a persistent grid taking "
+                         "the items from a counter")
     ap.add_argument("--serial", action="store_true",
                     help="run every stage on one stream (default: the inversion beside the "
                          "forward and the dK/dV reduce beside dQ, on a second stream)")

@@ -187,11 +187,13 @@ def build_git() -> str:
 
 
 def nsa_sel_bwd(q, k, v, o, lse, dO, block_idx, block_size, scale=None, cu_seqlens=None,
-                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None, sink=None, window=0):
+                max_seqlen=None, workspace=None, dq=None, dk=None, dv=None, sink=None, window=0,
+                sched_policy=0):
     """dq, dk, dv = backward (nsa_sel_bwd); with sink logits (lse from the
     sink forward) also dsink, from nsa_sel_bwd_dsink on the same workspace:
-    dq, dk, dv, dsink."""
+    dq, dk, dv, dsink.  sched_policy: nsa_sel_problem.sched_policy."""
     p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
+    p.sched_policy = int(sched_policy)
     _check_tensors(q, k, v, block_idx, cu_seqlens, p)
     for name, t in (("o", o), ("dO", dO)):
         if t.shape != q.shape or t.dtype != q.dtype:
@@ -230,8 +232,9 @@ class BwdStages:
     over, so it comes last).  Buffers are allocated once here."""
 
     def __init__(self, q, k, v, block_idx, block_size, scale=None, cu_seqlens=None,
-                 max_seqlen=None, window=0):
+                 max_seqlen=None, window=0, sched_policy=0):
         self.p = make_problem(q, k, block_idx, block_size, scale, cu_seqlens, max_seqlen, window)
+        self.p.sched_policy = int(sched_policy)
         _check_tensors(q, k, v, block_idx, cu_seqlens, self.p)
         self.q, self.k, self.v, self.idx, self.cu = q, k, v, block_idx, cu_seqlens
         self.ws = torch.empty(max(bwd_workspace_bytes(self.p), 1), dtype=torch.uint8,

@@ -64,6 +64,7 @@ class Problem(ctypes.Structure):
         ("stride_dk", ctypes.c_int64 * 3),
         ("stride_dv", ctypes.c_int64 * 3),
         ("Tk", ctypes.c_int32),
+        ("sched_policy", ctypes.c_int32),
     ]
 
 

@@ -53,6 +53,9 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
     int Tmax = p->T, Z = p->B;
     // Keys per (z, hkv): dense problems may have more keys than queries.
     if (p->Tk < 0) return fail(NSA_ERR_INVALID_ARG, "Tk=%d must be >= 0 (0: T)", p->Tk);
+    if (p->sched_policy != 0 && p->sched_policy != 1)
+        return fail(NSA_ERR_INVALID_ARG, "sched_policy=%d is not 0 (static) or 1 (persistent)",
+                    p->sched_policy);
     if (packed && p->Tk != 0 && p->Tk != p->T)
         return fail(NSA_ERR_INVALID_ARG, "packed inputs need Tk = 0 or T (got %d)", p->Tk);
     const int Tk = p->Tk == 0 ? p->T : p->Tk;
@@ -169,6 +172,7 @@ nsa_status make_problem(const nsa_sel_problem* p, nsa::HostProblem& hp) {
                     p->block_size >= 32 && p->S <= 64 && (int64_t)p->S * p->block_size < Kmax &&
                     (int64_t)Tmax * Smin * p->block_size * G * 2 < (1ll << 31);
     if (hp.ds_handoff && nsa::dq_ds_lds_bytes(hp) > 163840) hp.ds_handoff = false;
+    hp.sched = p->sched_policy;
     if (nsa::invert_lds_bytes(hp) > 163840)
         return fail(NSA_ERR_UNSUPPORTED, "the block inversion needs %zu bytes of LDS for %lld blocks (max 163840)",
                     nsa::invert_lds_bytes(hp), (long long)NBmax);
@@ -195,7 +199,7 @@ nsa::BwdWorkspace carve(const nsa::HostProblem& hp, void* base) {
     w.item_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
     w.pslot_pre = (int*)take(sizeof(int) * ZH * (NB + 1));
     w.zh_base = (int*)take(sizeof(int) * (2 * (ZH + 1) + 3 * ZH + 1));
-    w.ticket = (int*)take(sizeof(int));
+    w.ticket = (int*)take(3 * sizeof(int));
     w.iota = (int*)take(hp.pair_possible ? sizeof(int) * hp.dev.Tmax : 0);
     // (16-key blocks use the 32-key tile's slot layout)
     w.partials = (float*)take(sizeof(float) * hp.pslots * 2 * std::max(32, hp.dev.bs) * hp.dev.D);

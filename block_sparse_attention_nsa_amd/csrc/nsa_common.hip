@@ -226,8 +226,9 @@ __device__ __forceinline__ void stage_rows(const Problem& p, const Seq& s, const
 __device__ __forceinline__ void count_chunk(const Problem& p, int CT, int C, const int* __restrict__ idx,
                                             int* __restrict__ chunk_pos, int c, int zh,
                                             int* __restrict__ ticket) {
-    // The scan that follows counts its finished workgroups from zero.
-    if (c == 0 && zh == 0 && threadIdx.x == 0) *ticket = 0;
+    // The scan that follows counts its finished workgroups from zero, and the
+    // persistent hand-off dQ its items and leavers.
+    if (c == 0 && zh == 0 && threadIdx.x < 3) ticket[threadIdx.x] = 0;
     extern __shared__ int sm[];
     int* hist = sm;                                          // [NBmax]
     const int NBH = (p.NBmax + 1) / 2;                       // ints per 16-bit array

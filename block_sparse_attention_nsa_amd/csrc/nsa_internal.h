@@ -2,6 +2,7 @@
 // kernel files: the backward workspace layout and the kernel launchers.
 #pragma once
 
+#include <algorithm>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -32,6 +33,10 @@ struct HostProblem {
     // that cannot cover whole causal prefixes: S * block_size < longest
     // sequence).  The backward then runs dK/dV before dQ.
     bool ds_handoff;
+    // Scheduling policy of the hand-off dQ (nsa_sel_problem.sched_policy):
+    // 0 one workgroup per item in a static longest-first order, 1 a
+    // persistent grid taking the same order from a device counter.
+    int sched;
     // The caller's strides of q, k, v, o, dO, dq, dk, dv when the problem is
     // strided (the device copies hold 32-bit head / token strides).
     int64_t given[8][3];
@@ -48,7 +53,9 @@ struct BwdWorkspace {
     int* zh_base;        // [2][ZH + 1]: global prefixes of items and partial slots,
                          // then [2][ZH]: per-(z, hkv) totals of both, [ZH]: per-(z,
                          // hkv) whole-prefix flags, [1]: all of them set
-    int* ticket;         // [1]: scan workgroups done (the last one plans)
+    int* ticket;         // [3]: scan workgroups done (the last one plans), then the
+                         // persistent hand-off dQ's item counter and leaver count
+                         // (all three zeroed by the inversion's count kernel)
     int* iota;           // [Tmax] (pair_possible): iota[t] = t, the lists of a
                          // whole-prefix selection
     float* partials;     // [pslots][bs][D][2]

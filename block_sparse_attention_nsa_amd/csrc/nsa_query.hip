@@ -138,14 +138,14 @@ struct WgCoord {
 // s_z) pairs precede level lw and #{z : s_z <= lw} lie on it; 64 candidate
 // levels are tested per pass, one per lane.  Returns false when b is past
 // the last pair.
-__device__ bool packed_pair(const Problem& p, const QGeo& qg, int& zh, int& w) {
+__device__ bool packed_pair(const Problem& p, const QGeo& qg, int b, int& zh, int& w) {
     const int lane = threadIdx.x & 63, L = qg.wg_per_zh;
     int s_z = L;
     if (lane < p.Z) {
         const int len = min(max(p.cu[lane + 1] - p.cu[lane], 0), p.Tmax);
         s_z = L - (len + qg.TW - 1) / qg.TW;
     }
-    const int hkv = (int)blockIdx.x % p.Hkv, n = (int)blockIdx.x / p.Hkv;
+    const int hkv = b % p.Hkv, n = b / p.Hkv;
     for (int c = 0; c < L; c += 64) {
         const int lw = c + lane;
         int before = 0, on = 0;
@@ -177,21 +177,23 @@ __device__ bool packed_pair(const Problem& p, const QGeo& qg, int& zh, int& w) {
 // work; then, and for packed inputs, workgroups are dealt round-robin over
 // the XCDs, latest token first (packed: as above, or, with more than 64
 // sequences, every (window, group) in turn, empty ones included).  K/V then
-// come from HBM or the memory-side cache more often.
-__device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
+// come from HBM or the memory-side cache more often.  b: the workgroup's
+// place in that order (its block index, or the item a persistent workgroup
+// took), of nb in all.
+__device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg, int b, int nb) {
     WgCoord c;
     int zh, w;
     const int ZH = p.Z * p.Hkv;
     if (p.packed && p.Z <= 64) {
-        if (!packed_pair(p, qg, zh, w)) {
+        if (!packed_pair(p, qg, b, zh, w)) {
             zh = 0;
             w = -1;  // past the last pair: T0 lies past every sequence
         }
     } else if (p.packed || ZH % 8 != 0) {
-        zh = (int)blockIdx.x % ZH;
-        w = (int)blockIdx.x / ZH;
+        zh = b % ZH;
+        w = b / ZH;
     } else {
-        const int L = xcd_remap(blockIdx.x, gridDim.x);
+        const int L = xcd_remap(b, nb);
         zh = L / qg.wg_per_zh;
         w = L % qg.wg_per_zh;
     }
@@ -199,6 +201,9 @@ __device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
     c.hkv = zh % p.Hkv;
     c.T0 = (qg.wg_per_zh - 1 - w) * qg.TW;
     return c;
+}
+__device__ __forceinline__ WgCoord wg_coord(const Problem& p, const QGeo& qg) {
+    return wg_coord(p, qg, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Union of the blocks listed by tokens T0 .. T0+n_tok-1: umask[u] holds the
@@ -1063,13 +1068,15 @@ __device__ __forceinline__ uint32_t ds_tile_byte(int key, int col4) {
     return (uint32_t)((((key >> 1) * 4 + col4) * 16) + (key & 1) * 8);
 }
 
+// The dQ of one (window, group) work item b of nb (its place in the launch
+// order of wg_coord).
 template <int D, int BS, int RT, int NW, int TPT>
-__global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
-                                                        const uint16_t* __restrict__ k,
-                                                        const int* __restrict__ idx,
-                                                        const int* __restrict__ posmap,
-                                                        const uint16_t* __restrict__ ds,
-                                                        uint16_t* __restrict__ dq) {
+__device__ __forceinline__ void dq_ds_item(const Problem& p, const QGeo& qg,
+                                           const uint16_t* __restrict__ k,
+                                           const int* __restrict__ idx,
+                                           const int* __restrict__ posmap,
+                                           const uint16_t* __restrict__ ds,
+                                           uint16_t* __restrict__ dq, int b, int nb) {
     using L = RowTile<D>;
     constexpr int ND = D / 16, JK = JobKeys<BS>::JK, NKS = JK / 32, NDMA = JK / 32;
     static_assert(BS >= 32 && JobKeys<BS>::KT == JK, "whole 32-key steps of one block");
@@ -1083,7 +1090,7 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
 
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6),
               g = lane >> 4, r = lane & 15;
-    const WgCoord wc = wg_coord(p, qg);
+    const WgCoord wc = wg_coord(p, qg, b, nb);
     const Seq s = seq_of(p, wc.z);
     if (wc.T0 >= s.len) return;
     const int n_tok = min(qg.TW, s.len - wc.T0);
@@ -1284,6 +1291,53 @@ __global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
     }
 }
 
+// One workgroup per work item, in the launch order of wg_coord (latest
+// token windows first); the hardware dispatcher deals them out greedily.
+template <int D, int BS, int RT, int NW, int TPT>
+__global__ __launch_bounds__(NW * 64) void dq_ds_kernel(Problem p, QGeo qg,
+                                                        const uint16_t* __restrict__ k,
+                                                        const int* __restrict__ idx,
+                                                        const int* __restrict__ posmap,
+                                                        const uint16_t* __restrict__ ds,
+                                                        uint16_t* __restrict__ dq) {
+    dq_ds_item<D, BS, RT, NW, TPT>(p, qg, k, idx, posmap, ds, dq, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// Persistent form (scheduling policy 1): a grid of at most one workgroup per
+// CU, each taking the next item of the same longest-first order from the
+// counter sched[0] until none is left; every item is still one workgroup's
+// alone, so the result is the same bit for bit.  The prepare stage zeroes
+// sched[0..1]; the last workgroup to leave zeroes them again, so that a dQ
+// stage run twice after one prepare also starts from zero.  Every
+// workgroup leaves once the counter has passed n_items.
+template <int D, int BS, int RT, int NW, int TPT>
+__global__ __launch_bounds__(NW * 64) void dq_ds_persistent(Problem p, QGeo qg,
+                                                            const uint16_t* __restrict__ k,
+                                                            const int* __restrict__ idx,
+                                                            const int* __restrict__ posmap,
+                                                            const uint16_t* __restrict__ ds,
+                                                            uint16_t* __restrict__ dq,
+                                                            int* __restrict__ sched, int n_items) {
+    __shared__ int item_s;
+    for (;;) {
+        if (threadIdx.x == 0) item_s = atomicAdd(&sched[0], 1);
+        __syncthreads();
+        const int item = item_s;
+        __syncthreads();
+        if (item >= n_items) break;
+        dq_ds_item<D, BS, RT, NW, TPT>(p, qg, k, idx, posmap, ds, dq, item, n_items);
+        // The next item rebuilds the union and reuses the ring's LDS.
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(&sched[1], 1) == (int)gridDim.x - 1) {
+            atomicExch(&sched[0], 0);
+            atomicExch(&sched[1], 0);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -1423,22 +1477,38 @@ size_t dq_ds_lds_bytes(const HostProblem& hp) {
 hipError_t launch_dq_handoff(const HostProblem& hp, const void* k, const int* block_idx,
                              const BwdWorkspace& ws, void* dq, hipStream_t st) {
     const QGeo qg = q_geo(hp, kRT_Q, kNW_Q);
-    const unsigned grid = (unsigned)((int64_t)hp.ZH * qg.wg_per_zh);
-    if (grid == 0) return hipSuccess;
+    const int64_t n_items = (int64_t)hp.ZH * qg.wg_per_zh;
+    if (n_items == 0) return hipSuccess;
     const size_t lds = query_dynamic_lds(hp);
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kNW_Q * 64), lds, st, hp.dev, qg,
-                           (const uint16_t*)k, block_idx, (const int*)ws.posmap,
-                           (const uint16_t*)ws.ds, (uint16_t*)dq);
+    unsigned pgrid = 0;  // persistent grid: one workgroup per CU (LDS allows no more)
+    if (hp.sched == 1) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        pgrid = (unsigned)std::min<int64_t>(n_items, std::max(cus, 1));
+    }
+    auto go = [&](auto kernel, auto persistent) {
+        if (pgrid)
+            hipLaunchKernelGGL(persistent, dim3(pgrid), dim3(kNW_Q * 64), lds, st, hp.dev, qg,
+                               (const uint16_t*)k, block_idx, (const int*)ws.posmap,
+                               (const uint16_t*)ws.ds, (uint16_t*)dq, ws.ticket + 1, (int)n_items);
+        else
+            hipLaunchKernelGGL(kernel, dim3((unsigned)n_items), dim3(kNW_Q * 64), lds, st, hp.dev, qg,
+                               (const uint16_t*)k, block_idx, (const int*)ws.posmap,
+                               (const uint16_t*)ws.ds, (uint16_t*)dq);
     };
     const int D = hp.dev.D, BS = hp.dev.bs, G = hp.dev.G;
     const int tpt = G % 16 == 0 ? 1 : G == 8 ? 2 : G == 4 ? 4 : 0;
-#define NSA_DQ_DS(D_, BS_)                                                          \
-    else if (D == D_ && BS == BS_) {                                                \
-        if (tpt == 1) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 1>);                   \
-        else if (tpt == 2) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 2>);              \
-        else if (tpt == 4) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 4>);              \
-        else return hipErrorInvalidValue;                                           \
+#define NSA_DQ_DS(D_, BS_)                                                                      \
+    else if (D == D_ && BS == BS_) {                                                            \
+        if (tpt == 1) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 1>,                                \
+                         dq_ds_persistent<D_, BS_, kRT_Q, kNW_Q, 1>);                           \
+        else if (tpt == 2) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 2>,                           \
+                              dq_ds_persistent<D_, BS_, kRT_Q, kNW_Q, 2>);                      \
+        else if (tpt == 4) go(dq_ds_kernel<D_, BS_, kRT_Q, kNW_Q, 4>,                           \
+                              dq_ds_persistent<D_, BS_, kRT_Q, kNW_Q, 4>);                      \
+        else return hipErrorInvalidValue;                                                       \
     }
     if (false) {}
     NSA_DQ_DS(32, 32) NSA_DQ_DS(32, 64) NSA_DQ_DS(32, 128)

@@ -123,6 +123,18 @@ typedef struct nsa_sel_problem {
      * [B, Hkv, Tk, D] (default strides from Tk).  Packed problems need 0 or
      * T (queries and keys share the cumulative lengths). */
     int32_t Tk;
+    /* Work scheduling of the dQ stage when it takes the dS that dK/dV hands
+     * over (nsa_sel_bwd_ds_handoff() != 0; ignored otherwise).  Page 3 of the
+     * reference text lists a scheduling policy among its backward's
+     * parameters (natural order, with longest-processing-time first named
+     * as a pending tweak for packed inputs).  0: one workgroup per (token
+     * window, KV head) item, launched longest first (the latest token
+     * windows, which list the most blocks), dealt out by the hardware
+     * dispatcher.  1: a persistent grid of one workgroup per compute unit
+     * that takes the items in that same order from a counter in the
+     * workspace.  Each item is one workgroup's alone either way, so results
+     * are bitwise the same.  Other values: NSA_ERR_INVALID_ARG. */
+    int32_t sched_policy;
 } nsa_sel_problem;
 
 typedef struct hipStream_t_opaque* nsa_stream_t; /* a hipStream_t; NULL = null stream */

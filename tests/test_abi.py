@@ -77,6 +77,8 @@ def _fwd(p, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cu=None, o=FAKE, lse=FAKE):
     (dict(block_size=0), _lib.NSA_ERR_INVALID_ARG, "block_size"),
     (dict(T=-1), _lib.NSA_ERR_INVALID_ARG, "T="),
     (dict(scale=float("nan")), _lib.NSA_ERR_INVALID_ARG, "scale"),
+    (dict(sched_policy=2), _lib.NSA_ERR_INVALID_ARG, "sched_policy"),
+    (dict(sched_policy=-1), _lib.NSA_ERR_INVALID_ARG, "sched_policy"),
     (dict(dtype=1, D=48), _lib.NSA_ERR_UNSUPPORTED, "D in"),
     (dict(dtype=1, D=64, block_size=8), _lib.NSA_ERR_UNSUPPORTED, "block_size in"),
     (dict(D=24), _lib.NSA_ERR_UNSUPPORTED, "D in"),

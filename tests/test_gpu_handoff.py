@@ -11,6 +11,7 @@ packed sequences with an empty one.  Each case also checks that the library
 reports the hand-off for it."""
 import numpy as np
 import pytest
+import torch
 
 import block_sparse_attention_nsa_amd as nsa
 import workloads
@@ -71,3 +72,48 @@ def test_handoff_bitwise_repeatable():
     for x, y, n in zip(a, b, ("dq", "dk", "dv")):
         assert bool((x == y).all()), n
     say("[ho-repeat] dq, dk, dv bitwise equal over two calls")
+
+
+def _persistent_case(name):
+    if name == "ho-persist-G8":
+        return workloads.make_thd([3000, 0, 1500, 2049], 16, 2, 128, 6, 64, "bf16",
+                                  "own_first_random", seed=87, name=name)
+    return workloads.make_workload(name)
+
+
+@pytest.mark.parametrize("name", ["select_T8192", "packed_8seq", "ho-persist-G8"])
+def test_persistent_schedule_is_bitwise_the_same(name):
+    """sched_policy 1 (a persistent grid of one workgroup per CU taking the
+    hand-off dQ's items from a workspace counter, longest first) gives the
+    same dq, dk, dv bit for bit as the default launch, on problems with more
+    items than CUs (tiles of 1, 4 and 2 tokens); two backward calls on one
+    workspace, and the dQ stage run twice after one prepare, check that the
+    counter starts from zero each time."""
+    w = _persistent_case(name)
+    assert _handoff_on(w)
+    d = to_dev(w)
+    cu = d["cu"]
+    ms = w.max_seqlen if w.packed else None
+    o, lse = nsa.nsa_sel_fwd(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms)
+    ref = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"], w.block_size,
+                          w.scale, cu, ms)
+    ws = torch.empty(nsa.bwd_workspace_bytes(nsa.make_problem(d["q"], d["k"], d["idx"],
+                                                               w.block_size, w.scale, cu, ms)),
+                     dtype=torch.uint8, device="cuda")
+    for it in range(2):
+        got = nsa.nsa_sel_bwd(d["q"], d["k"], d["v"], o, lse, d["dO"], d["idx"], w.block_size,
+                              w.scale, cu, ms, workspace=ws, sched_policy=1)
+        for a, b, n in zip(ref, got, ("dq", "dk", "dv")):
+            assert torch.equal(a, b), f"call {it}: {n}"
+    st = nsa.BwdStages(d["q"], d["k"], d["v"], d["idx"], w.block_size, w.scale, cu, ms,
+                       sched_policy=1)
+    st.prepare(o, d["dO"])
+    st.dkdv_blocks(d["dO"], lse)
+    st.dkdv_reduce()
+    for it in range(2):
+        st.dq.zero_()  # an item the walk skipped would stay zero
+        dq = st.dq_stage(d["dO"], lse)
+        assert torch.equal(dq, ref[0]), f"dQ stage run {it}"
+    torch.cuda.synchronize()
+    say(f"[{name}] persistent hand-off dQ: bitwise equal to the default launch "
+        f"(two calls, and the dQ stage twice after one prepare)")
