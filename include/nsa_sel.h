@@ -125,9 +125,10 @@ typedef struct nsa_sel_problem {
     int32_t Tk;
     /* Work scheduling of the dQ stage when it takes the dS that dK/dV hands
      * over (nsa_sel_bwd_ds_handoff() != 0; ignored otherwise).  Page 3 of the
-     * reference text lists a scheduling policy among its backward's
-     * parameters (natural order, with longest-processing-time first named
-     * as a pending tweak for packed inputs).  0: one workgroup per (token
+     * reference text (the pull request porting the SM80 SDPA backward; the
+     * review comment on bwd_params_for_flavor) passes a scheduling policy to
+     * its backward: natural order, with longest-processing-time first named
+     * as a pending tweak for packed inputs.  0: one workgroup per (token
      * window, KV head) item, launched longest first (the latest token
      * windows, which list the most blocks), dealt out by the hardware
      * dispatcher.  1: a persistent grid of one workgroup per compute unit
